@@ -1,0 +1,254 @@
+/*
+ * q4g128_oracle.c -- plain, slow, fp64 CPU oracle for the group-wise
+ * asymmetric int4 weight-streaming product y = x . dequant(W).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or constant
+ * with the HIP library.
+ *
+ * What it computes follows the Token Rush README (github.com/zyhector/
+ * token-rush):
+ *   - the weight format paragraph ("group-wise asymmetric int4"): every 128
+ *     consecutive weights share one bf16 scale and one bf16 minimum, 4.25
+ *     bits per weight;
+ *   - the constraints list ("4.25 bits per weight ... 128-group scale and
+ *     minimum");
+ *   - the bandwidth paragraph: a decode step is a product of the activation
+ *     with every streamed weight matrix;
+ *   - the steps table, rows 13-14 and 28: an M-row verify step is the same
+ *     product with M activation rows.
+ * and the bw24 article (wpnews.pro), exactness paragraph: verify and decode
+ * must agree exactly, and summation order is part of the contract.
+ *
+ * Readings taken where the pages leave a step open (all listed in the design
+ * notes): a weight is w = q*s + m (q = 0 maps to the minimum); the 128-weight
+ * group runs along the contraction axis k within one output column n; codes
+ * are packed as W[n][k/8] uint32 with nibble (k mod 8) of that word holding
+ * code k, low nibble first; scale and minimum are stored [n][k/128].
+ *
+ * Arithmetic: every bf16 is decoded exactly from its bit fields; w is formed
+ * in fp64 and checked to be exact (a 4-bit code times an 8-bit significand
+ * plus an 8-bit significand); y[m][n] = sum over k ascending of x[m][k]*w in
+ * fp64; a[m][n] = sum of |x[m][k]*w| is the tolerance scale.  Each (m, n) is
+ * summed by one thread, so results do not depend on the thread count.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC (no fast-math).  Compiling with
+ * -DORACLE_PLANT=<n> plants one deliberate mistake; the test suite uses that
+ * to show that its pins catch each kind of mistake.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#ifndef ORACLE_PLANT
+#define ORACLE_PLANT 0
+#endif
+
+enum { ORC_OK = 0, ORC_EINVAL = 1, ORC_EINEXACT = 2, ORC_ENONFINITE = 3 };
+
+/* bf16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.  Decoded
+ * from the fields, not by reinterpreting memory. */
+static int bf16_decode(uint16_t b, double *out)
+{
+    int sign = (b >> 15) & 1;
+    int e = (b >> 7) & 0xFF;
+    int f = b & 0x7F;
+    double v;
+    if (e == 0xFF)
+        return ORC_ENONFINITE;
+    if (e == 0)
+        v = ldexp((double)f, -126 - 7);           /* subnormal: f/128 * 2^-126 */
+    else
+        v = ldexp((double)(128 + f), e - 127 - 7); /* (1 + f/128) * 2^(e-127) */
+    *out = sign ? -v : v;
+    return ORC_OK;
+}
+
+/* Code k of output column n. */
+static int code_at(const uint32_t *W, long K, long n, long k)
+{
+    uint32_t word = W[n * (K / 8) + k / 8];
+#if ORACLE_PLANT == 3
+    return (int)((word >> (4 * (7 - k % 8))) & 0xFu); /* planted: high nibble first */
+#else
+    return (int)((word >> (4 * (k % 8))) & 0xFu);
+#endif
+}
+
+/* Index of the (n, group-of-k) entry in a [N][K/128] scale or minimum array. */
+static long group_index(long K, long N, long n, long k)
+{
+    long G = K / 128;
+#if ORACLE_PLANT == 4
+    (void)N;
+    return n * G + (k / 64) % G;      /* planted: groups of 64 */
+#elif ORACLE_PLANT == 5
+    (void)G;
+    return (k / 128) * N + n;         /* planted: scale array read transposed */
+#else
+    (void)N;
+    return n * G + k / 128;
+#endif
+}
+
+/* Knuth's two-sum: err is the exact rounding error of s = a + b. */
+static double two_sum_err(double a, double b, double s)
+{
+    double bb = s - a;
+    return (a - (s - bb)) + (b - bb);
+}
+
+/* Exact fp64 weight w = q*s + m of column n, position k. */
+static int weight_f64(const uint32_t *W, const uint16_t *S, const uint16_t *Mn,
+                      long K, long N, long n, long k, double *w)
+{
+    double s, m, qs, v;
+    int q = code_at(W, K, n, k);
+    long gi = group_index(K, N, n, k);
+    if (bf16_decode(S[gi], &s) || bf16_decode(Mn[gi], &m))
+        return ORC_ENONFINITE;
+    qs = (double)q * s;               /* <= 12 significant bits: exact */
+#if ORACLE_PLANT == 1
+    m = 0.0;                          /* planted: minimum dropped */
+#elif ORACLE_PLANT == 2
+    m = -m;                           /* planted: minimum subtracted */
+#endif
+    v = qs + m;
+    if (two_sum_err(qs, m, v) != 0.0)
+        return ORC_EINEXACT;
+    *w = v;
+    return ORC_OK;
+}
+
+static int shape_ok(long M, long K, long N)
+{
+    return M >= 1 && K >= 128 && K % 128 == 0 && N >= 1;
+}
+
+int q4o_abi_version(void) { return 1; }
+
+int q4o_plant(void) { return ORACLE_PLANT; }
+
+/* Codes as bytes, [N][K]. */
+int q4o_codes(const uint32_t *W, long K, long N, uint8_t *q)
+{
+    if (!shape_ok(1, K, N) || !W || !q)
+        return ORC_EINVAL;
+    for (long n = 0; n < N; ++n)
+        for (long k = 0; k < K; ++k)
+            q[n * K + k] = (uint8_t)code_at(W, K, n, k);
+    return ORC_OK;
+}
+
+/* Decoded weights, fp64, [N][K] (w_nk; the product uses its transpose). */
+int q4o_dequant_f64(const uint32_t *W, const uint16_t *S, const uint16_t *Mn,
+                    long K, long N, double *w)
+{
+    if (!shape_ok(1, K, N) || !W || !S || !Mn || !w)
+        return ORC_EINVAL;
+    for (long n = 0; n < N; ++n)
+        for (long k = 0; k < K; ++k) {
+            int rc = weight_f64(W, S, Mn, K, N, n, k, &w[n * K + k]);
+            if (rc)
+                return rc;
+        }
+    return ORC_OK;
+}
+
+/* Decoded weights rounded once to fp32 (round to nearest, ties to even),
+ * [N][K].  A one-rounding fp32 dequant must equal this bit for bit. */
+int q4o_dequant_f32(const uint32_t *W, const uint16_t *S, const uint16_t *Mn,
+                    long K, long N, float *w32)
+{
+    if (!shape_ok(1, K, N) || !W || !S || !Mn || !w32)
+        return ORC_EINVAL;
+    for (long n = 0; n < N; ++n)
+        for (long k = 0; k < K; ++k) {
+            double w;
+            int rc = weight_f64(W, S, Mn, K, N, n, k, &w);
+            if (rc)
+                return rc;
+            w32[n * K + k] = (float)w;
+        }
+    return ORC_OK;
+}
+
+/* y[m][c] and a[m][c] for the listed output columns cols[c] (all columns
+ * when cols is NULL, then ncols must equal N).  x is bf16 [M][K]. */
+int q4o_gemm_cols(const uint16_t *x, long M, long K, const uint32_t *W,
+                  const uint16_t *S, const uint16_t *Mn, long N,
+                  const long *cols, long ncols, double *y, double *a,
+                  int nthreads)
+{
+    int status = ORC_OK;
+    if (!shape_ok(M, K, N) || !x || !W || !S || !Mn || !y || !a || ncols < 0)
+        return ORC_EINVAL;
+    if (!cols && ncols != N)
+        return ORC_EINVAL;
+    for (long c = 0; cols && c < ncols; ++c)
+        if (cols[c] < 0 || cols[c] >= N)
+            return ORC_EINVAL;
+#ifdef _OPENMP
+    if (nthreads < 1)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+#else
+    (void)nthreads;
+#endif
+    for (long c = 0; c < ncols; ++c) {
+        long n = cols ? cols[c] : c;
+        for (long m = 0; m < M; ++m) {
+            double acc = 0.0, mag = 0.0;
+#if ORACLE_PLANT == 6
+            long kend = K - 1;        /* planted: last k dropped */
+#else
+            long kend = K;
+#endif
+            long xrow = m;
+#if ORACLE_PLANT == 7
+            xrow = 0;                 /* planted: every output row reads x row 0 */
+#endif
+            for (long k = 0; k < kend; ++k) {
+                double w, xv, p;
+                int rc = weight_f64(W, S, Mn, K, N, n, k, &w);
+                if (!rc)
+                    rc = bf16_decode(x[xrow * K + k], &xv);
+                if (rc) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+                    status = rc;
+                    break;
+                }
+                p = xv * w;
+                acc += p;
+                mag += fabs(p);
+            }
+            y[m * ncols + c] = acc;
+            a[m * ncols + c] = mag;
+        }
+    }
+    return status;
+}
+
+/* Whole product: y, a are [M][N]. */
+int q4o_gemm(const uint16_t *x, long M, long K, const uint32_t *W,
+             const uint16_t *S, const uint16_t *Mn, long N, double *y,
+             double *a, int nthreads)
+{
+    return q4o_gemm_cols(x, M, K, W, S, Mn, N, NULL, N, y, a, nthreads);
+}
+
+/* Threads the OpenMP runtime would use by default (for reporting). */
+int q4o_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

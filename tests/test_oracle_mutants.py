@@ -1,0 +1,31 @@
+"""Each planted mistake in the oracle (a dropped or sign-flipped minimum, the
+wrong nibble order, the wrong group size, a transposed scale read, a dropped
+term of the sum, a wrong activation row) must trip at least one pin.  The
+mutants are separate builds of the same C source; CPU only."""
+import os
+import shutil
+
+import pytest
+
+import oracle
+import oracle_pins
+from oracle.build import build_oracle
+
+PLANTS = {1: "minimum dropped", 2: "minimum subtracted", 3: "high nibble first",
+          4: "groups of 64", 5: "scale read transposed", 6: "last k dropped",
+          7: "every row reads x row 0"}
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+@pytest.mark.parametrize("plant", sorted(PLANTS), ids=lambda p: PLANTS[p].replace(" ", "_"))
+def test_planted_mistake_is_caught(tmp_path, plant):
+    lib = build_oracle(out=os.path.join(str(tmp_path), f"mutant{plant}.so"), plant=plant)
+    mutant = oracle.Oracle(lib)
+    assert mutant.plant == plant
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, oracle.OracleError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches planted mistake {plant}: {PLANTS[plant]}"
