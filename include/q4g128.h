@@ -1,0 +1,118 @@
+/*
+ * q4g128.h -- C ABI of libq4g128.so: the int4-g128 weight-streaming product
+ *
+ *     y[M][N] = x[M][K] . dequant(W)[K][N],   1 <= M <= 8
+ *
+ * on AMD Instinct MI355X (gfx950).  M = 1 is a plain decode step; M = 2..8 is
+ * a speculative verify step that checks M draft tokens in one pass (Token
+ * Rush README, steps table rows 13-14 and 28).  Decode is bound by streaming
+ * the weights (Token Rush README, bandwidth paragraph), so the library reads
+ * every weight byte once per call, for all M rows together.
+ *
+ * Weight format (Token Rush README, weight format paragraph): group-wise
+ * asymmetric int4, 128 consecutive weights along K per bf16 scale s and bf16
+ * minimum m, w = q*s + m for a 4-bit code q, 4.25 bits per weight.
+ *
+ * Layouts (all row-major, all DEVICE memory owned by the caller):
+ *   x      bf16  [M][K]      activation rows
+ *   W      uint32 [N][K/8]   codes of output column n; nibble i (bits 4i..4i+3,
+ *                            low nibble first) of word j holds code k = 8j + i
+ *   scale  bf16  [N][K/128]  scale of column n, group k/128
+ *   min    bf16  [N][K/128]  minimum of column n, group k/128
+ *   y      fp32  [M][N]      output, fully overwritten, never accumulated into
+ *
+ * Arithmetic: fp32 accumulation.  For every (K, N) the library fixes one
+ * summation order that is the same for every M and every row, so row m of an
+ * M-row call equals the one-row call on x[m] bit for bit (bw24 article,
+ * exactness paragraph: verify must agree exactly with decode, and summation
+ * order is part of the contract).  Results are deterministic run to run; the
+ * library uses no atomics on results.
+ *
+ * Conventions for every call below:
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *     work on it and return without synchronising.
+ *   - Argument errors return Q4G128_EINVAL (null pointer, M outside [1, 8],
+ *     K <= 0, K > 2^24 or K % 128 != 0, N <= 0 or N > 2^28, splits > 65535,
+ *     x or W or w_out not 16-byte aligned,
+ *     scale or min not 2-byte aligned, y or workspace not 4-byte aligned,
+ *     splits outside [1, K/128]) or Q4G128_EWORKSPACE (workspace too small),
+ *     always before anything is enqueued.
+ *   - A failed kernel launch returns Q4G128_EHIP; q4g128_last_error() then
+ *     holds the HIP error text for the calling thread.
+ *   - Outputs must not alias inputs.  The library allocates no memory, keeps
+ *     no mutable global state and is safe to call from several threads; a
+ *     split-K workspace must not be shared by calls in flight at once.
+ */
+#ifndef Q4G128_H
+#define Q4G128_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4G128_ABI_VERSION 1
+#define Q4G128_GROUP 128
+#define Q4G128_MAX_M 8
+
+typedef enum {
+    Q4G128_OK = 0,
+    Q4G128_EINVAL = 1,
+    Q4G128_EWORKSPACE = 2,
+    Q4G128_EHIP = 3
+} q4g128_status;
+
+/* The product without splitting K: one kernel launch, y written directly.
+ * Best for wide N (N/16 well above the compute-unit count).
+ * Passages: Token Rush README, bandwidth and weight format paragraphs
+ * (decode as one pass over the streamed weights; the format), steps table row
+ * 3 (an int4 GEMV with projections fused side by side along N). */
+q4g128_status q4g128_gemm(const void *x, int M, int K,
+                          const uint32_t *W, const void *scale, const void *min,
+                          int N, float *y, void *stream);
+
+/* Bytes of workspace q4g128_gemm_splitk needs: splits * M * N * 4 (fp32
+ * partial sums P[s][m][n]).  Returns 0 for invalid arguments. */
+size_t q4g128_splitk_workspace_bytes(int M, int N, int splits);
+
+/* Split count the library recommends for a (K, N) shape: a pure function of
+ * K and N only (never of M, so rows stay bit-identical across M).  1 means
+ * "do not split"; returns 0 for invalid K or N. */
+int q4g128_splitk_default_splits(int K, int N);
+
+/* The product with K cut into `splits` contiguous, group-aligned ranges
+ * (split s covers groups [s*G/splits, (s+1)*G/splits), G = K/128).  Each
+ * range writes fp32 partial sums to the workspace; a second pass sums them
+ * in ascending s into y.  Deterministic; for splits == 1 it computes exactly
+ * what q4g128_gemm computes.  For short N, where one column per lane gives
+ * too little parallelism.  Passage: Token Rush README, steps table rows 8-9
+ * (a split-K GEMV whose partial sums are added afterwards). */
+q4g128_status q4g128_gemm_splitk(const void *x, int M, int K,
+                                 const uint32_t *W, const void *scale, const void *min,
+                                 int N, float *y, int splits,
+                                 float *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/* Decoded weights w_out[n][k] = fp32(q*s + m), rounded once (fma), laid out
+ * fp32 [N][K].  Uses the same device unpacking as the product; it exists so
+ * tests can compare the unpack and dequant bit for bit.  Passage: Token Rush
+ * README, weight format paragraph. */
+q4g128_status q4g128_dequant(const uint32_t *W, const void *scale, const void *min,
+                             int K, int N, float *w_out, void *stream);
+
+/* Static text for a status code. */
+const char *q4g128_status_string(q4g128_status s);
+
+/* Last HIP error text recorded on the calling thread ("" if none). */
+const char *q4g128_last_error(void);
+
+/* Q4G128_ABI_VERSION of the loaded library. */
+int q4g128_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4G128_H */

@@ -40,6 +40,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -178,13 +179,16 @@ int q4o_dequant_f32(const uint32_t *W, const uint16_t *S, const uint16_t *Mn,
 }
 
 /* y[m][c] and a[m][c] for the listed output columns cols[c] (all columns
- * when cols is NULL, then ncols must equal N).  x is bf16 [M][K]. */
+ * when cols is NULL, then ncols must equal N).  x is bf16 [M][K].  Each
+ * column's weights are decoded once into a scratch vector, x once into
+ * doubles; the sums then run over k in ascending order. */
 int q4o_gemm_cols(const uint16_t *x, long M, long K, const uint32_t *W,
                   const uint16_t *S, const uint16_t *Mn, long N,
                   const long *cols, long ncols, double *y, double *a,
                   int nthreads)
 {
     int status = ORC_OK;
+    double *xd;
     if (!shape_ok(M, K, N) || !x || !W || !S || !Mn || !y || !a || ncols < 0)
         return ORC_EINVAL;
     if (!cols && ncols != N)
@@ -192,46 +196,61 @@ int q4o_gemm_cols(const uint16_t *x, long M, long K, const uint32_t *W,
     for (long c = 0; cols && c < ncols; ++c)
         if (cols[c] < 0 || cols[c] >= N)
             return ORC_EINVAL;
+    xd = (double *)malloc((size_t)M * (size_t)K * sizeof(double));
+    if (!xd)
+        return ORC_EINVAL;
+    for (long e = 0; e < M * K; ++e)
+        if (bf16_decode(x[e], &xd[e])) {
+            free(xd);
+            return ORC_ENONFINITE;
+        }
 #ifdef _OPENMP
     if (nthreads < 1)
         nthreads = omp_get_max_threads();
-#pragma omp parallel for schedule(static) num_threads(nthreads)
+#pragma omp parallel num_threads(nthreads)
 #else
     (void)nthreads;
 #endif
-    for (long c = 0; c < ncols; ++c) {
-        long n = cols ? cols[c] : c;
-        for (long m = 0; m < M; ++m) {
-            double acc = 0.0, mag = 0.0;
-#if ORACLE_PLANT == 6
-            long kend = K - 1;        /* planted: last k dropped */
-#else
-            long kend = K;
+    {
+        double *wcol = (double *)malloc((size_t)K * sizeof(double));
+#ifdef _OPENMP
+#pragma omp for schedule(static)
 #endif
-            long xrow = m;
-#if ORACLE_PLANT == 7
-            xrow = 0;                 /* planted: every output row reads x row 0 */
-#endif
-            for (long k = 0; k < kend; ++k) {
-                double w, xv, p;
-                int rc = weight_f64(W, S, Mn, K, N, n, k, &w);
-                if (!rc)
-                    rc = bf16_decode(x[xrow * K + k], &xv);
-                if (rc) {
+        for (long c = 0; c < ncols; ++c) {
+            long n = cols ? cols[c] : c;
+            int rc = wcol ? ORC_OK : ORC_EINVAL;
+            for (long k = 0; k < K && !rc; ++k)
+                rc = weight_f64(W, S, Mn, K, N, n, k, &wcol[k]);
+            if (rc) {
 #ifdef _OPENMP
 #pragma omp atomic write
 #endif
-                    status = rc;
-                    break;
-                }
-                p = xv * w;
-                acc += p;
-                mag += fabs(p);
+                status = rc;
+                continue;
             }
-            y[m * ncols + c] = acc;
-            a[m * ncols + c] = mag;
+            for (long m = 0; m < M; ++m) {
+                double acc = 0.0, mag = 0.0;
+#if ORACLE_PLANT == 6
+                long kend = K - 1;        /* planted: last k dropped */
+#else
+                long kend = K;
+#endif
+                long xrow = m;
+#if ORACLE_PLANT == 7
+                xrow = 0;                 /* planted: every output row reads x row 0 */
+#endif
+                for (long k = 0; k < kend; ++k) {
+                    double p = xd[xrow * K + k] * wcol[k];
+                    acc += p;
+                    mag += fabs(p);
+                }
+                y[m * ncols + c] = acc;
+                a[m * ncols + c] = mag;
+            }
         }
+        free(wcol);
     }
+    free(xd);
     return status;
 }
 

@@ -1,0 +1,197 @@
+"""Python binding of libq4g128.so: the int4-g128 weight-streaming product on
+AMD MI355X (gfx950).
+
+Argument marshalling only.  Every step of the product runs in the library's
+HIP kernels; PyTorch supplies device memory and the stream.  The functions
+carry the C ABI's names (include/q4g128.h) and take torch tensors:
+
+    x      [M][K]    bf16 (or int16/uint16 holding bf16 bit patterns), 1 <= M <= 8
+    W      [N][K/8]  int32/uint32 packed codes, low nibble first
+    scale  [N][K/128] bf16 (or 16-bit bit patterns)
+    min    [N][K/128] bf16 (or 16-bit bit patterns)
+    y      [M][N]    float32
+
+There is no CPU fallback: if the library is missing, or a tensor is not on a
+GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libq4g128.so")
+
+Q4G128_OK, Q4G128_EINVAL, Q4G128_EWORKSPACE, Q4G128_EHIP = 0, 1, 2, 3
+GROUP = 128
+MAX_M = 8
+
+_lib = None
+
+
+class Q4G128Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(what)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libq4g128.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise Q4G128Error(-1, f"libq4g128.so not built at {LIB_PATH}; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.q4g128_gemm.argtypes = [vp, ci, ci, vp, vp, vp, ci, vp, vp]
+        L.q4g128_gemm.restype = ci
+        L.q4g128_gemm_splitk.argtypes = [vp, ci, ci, vp, vp, vp, ci, vp, ci, vp, sz, vp]
+        L.q4g128_gemm_splitk.restype = ci
+        L.q4g128_dequant.argtypes = [vp, vp, vp, ci, ci, vp, vp]
+        L.q4g128_dequant.restype = ci
+        L.q4g128_splitk_workspace_bytes.argtypes = [ci, ci, ci]
+        L.q4g128_splitk_workspace_bytes.restype = sz
+        L.q4g128_splitk_default_splits.argtypes = [ci, ci]
+        L.q4g128_splitk_default_splits.restype = ci
+        L.q4g128_status_string.argtypes = [ci]
+        L.q4g128_status_string.restype = ctypes.c_char_p
+        L.q4g128_last_error.argtypes = []
+        L.q4g128_last_error.restype = ctypes.c_char_p
+        L.q4g128_abi_version.argtypes = []
+        L.q4g128_abi_version.restype = ci
+        _lib = L
+    return _lib
+
+
+def q4g128_abi_version() -> int:
+    return int(lib().q4g128_abi_version())
+
+
+def q4g128_status_string(status: int) -> str:
+    return lib().q4g128_status_string(int(status)).decode()
+
+
+def q4g128_last_error() -> str:
+    return lib().q4g128_last_error().decode()
+
+
+def q4g128_splitk_workspace_bytes(M: int, N: int, splits: int) -> int:
+    return int(lib().q4g128_splitk_workspace_bytes(int(M), int(N), int(splits)))
+
+
+def q4g128_splitk_default_splits(K: int, N: int) -> int:
+    return int(lib().q4g128_splitk_default_splits(int(K), int(N)))
+
+
+# ---- marshalling helpers -----------------------------------------------------
+
+_HALF = (torch.bfloat16, torch.int16, torch.uint16)
+_WORD = (torch.int32, torch.uint32)
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, ndim: int = 2) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device}); there is no CPU path")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-D tensor (got shape {tuple(t.shape)})")
+    return t
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != Q4G128_OK:
+        detail = q4g128_last_error() if status == Q4G128_EHIP else ""
+        raise Q4G128Error(status, f"{what}: {q4g128_status_string(status)} {detail}".strip())
+
+
+def _operands(x, W, scale, min):
+    x = _dev(x, "x", _HALF)
+    W = _dev(W, "W", _WORD)
+    scale = _dev(scale, "scale", _HALF)
+    min = _dev(min, "min", _HALF)
+    M, K = x.shape
+    N = W.shape[0]
+    if W.shape[1] * 8 != K:
+        raise ValueError(f"W has {W.shape[1]} words per column; x has K={K} (needs K/8)")
+    if K % GROUP or tuple(scale.shape) != (N, K // GROUP) or tuple(min.shape) != (N, K // GROUP):
+        raise ValueError(f"scale/min must be [N][K/128] = {(N, K // GROUP)}")
+    for t in (W, scale, min):
+        if t.device != x.device:
+            raise ValueError("all operands must be on the same device")
+    return x, W, scale, min, M, K, N
+
+
+def _out(y, M, N, device):
+    if y is None:
+        return torch.empty((M, N), dtype=torch.float32, device=device)
+    y = _dev(y, "y", (torch.float32,))
+    if tuple(y.shape) != (M, N):
+        raise ValueError(f"y must be [M][N] = {(M, N)}")
+    return y
+
+
+# ---- entry points ------------------------------------------------------------
+
+def q4g128_gemm(x, W, scale, min, y=None, stream=None) -> torch.Tensor:
+    """y[M][N] = x . dequant(W), K not split (one launch)."""
+    x, W, scale, min, M, K, N = _operands(x, W, scale, min)
+    y = _out(y, M, N, x.device)
+    st = lib().q4g128_gemm(x.data_ptr(), M, K, W.data_ptr(), scale.data_ptr(), min.data_ptr(), N,
+                           y.data_ptr(), _stream(stream, x.device))
+    _check(st, "q4g128_gemm")
+    return y
+
+
+def q4g128_gemm_splitk(x, W, scale, min, splits=None, workspace=None, y=None, stream=None) -> torch.Tensor:
+    """y = x . dequant(W) with K cut into `splits` group-aligned ranges
+    (default: q4g128_splitk_default_splits(K, N)); partial sums go to
+    `workspace` (allocated here if not given) and are summed in split order."""
+    x, W, scale, min, M, K, N = _operands(x, W, scale, min)
+    y = _out(y, M, N, x.device)
+    if splits is None:
+        splits = q4g128_splitk_default_splits(K, N)
+    need = q4g128_splitk_workspace_bytes(M, N, splits) if splits >= 1 else 0
+    if workspace is None:
+        workspace = torch.empty((max(need, 4) // 4,), dtype=torch.float32, device=x.device)
+    workspace = _dev(workspace, "workspace", (torch.float32,), ndim=workspace.dim())
+    ws_bytes = workspace.numel() * 4
+    st = lib().q4g128_gemm_splitk(x.data_ptr(), M, K, W.data_ptr(), scale.data_ptr(), min.data_ptr(), N,
+                                  y.data_ptr(), int(splits), workspace.data_ptr(), ws_bytes,
+                                  _stream(stream, x.device))
+    _check(st, "q4g128_gemm_splitk")
+    return y
+
+
+def q4g128_dequant(W, scale, min, out=None, stream=None) -> torch.Tensor:
+    """Decoded weights fp32 [N][K], w = fp32(q*s + m) rounded once."""
+    W = _dev(W, "W", _WORD)
+    scale = _dev(scale, "scale", _HALF)
+    min = _dev(min, "min", _HALF)
+    N, K = W.shape[0], W.shape[1] * 8
+    if tuple(scale.shape) != (N, K // GROUP) or tuple(min.shape) != (N, K // GROUP):
+        raise ValueError(f"scale/min must be [N][K/128] = {(N, K // GROUP)}")
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float32, device=W.device)
+    out = _dev(out, "out", (torch.float32,))
+    if tuple(out.shape) != (N, K):
+        raise ValueError(f"out must be [N][K] = {(N, K)}")
+    st = lib().q4g128_dequant(W.data_ptr(), scale.data_ptr(), min.data_ptr(), K, N, out.data_ptr(),
+                              _stream(stream, W.device))
+    _check(st, "q4g128_dequant")
+    return out
+
+
+__all__ = ["q4g128_gemm", "q4g128_gemm_splitk", "q4g128_dequant", "q4g128_splitk_workspace_bytes",
+           "q4g128_splitk_default_splits", "q4g128_status_string", "q4g128_last_error",
+           "q4g128_abi_version", "Q4G128Error", "lib", "LIB_PATH"]

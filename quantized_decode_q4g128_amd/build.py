@@ -1,0 +1,51 @@
+"""Build libq4g128.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+
+Every HIP source is compiled with packed fp32 instructions disabled
+(``-target-feature -packed-fp32-ops``); hipcc's host pass warns that it does
+not know the feature, which is harmless.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_PATH = os.path.join(PKG, "libq4g128.so")
+SOURCES = [os.path.join(CSRC, "q4g128_kernels.hip"), os.path.join(CSRC, "q4g128_api.cpp")]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm toolchain required to build libq4g128.so)")
+
+
+def compile_flags(arch: str = ARCH):
+    return [f"--offload-arch={arch}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
+            "-I", INCLUDE, "-I", CSRC]
+
+
+def build_library(out: str = LIB_PATH, extra_flags=(), quiet: bool = True) -> str:
+    tmp = out + ".tmp"
+    cmd = [hipcc()] + compile_flags() + list(extra_flags) + ["-shared"] + SOURCES + ["-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = [l for l in (res.stdout + res.stderr).splitlines() if l.strip() and noise not in l]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
+    if msgs and not quiet:
+        print("\n".join(msgs))
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build_library(quiet=False))

@@ -1,0 +1,147 @@
+// C ABI of libq4g128.so: argument checks, the (K, N) plan, kernel launches.
+// Declarations and the contract of every entry point: include/q4g128.h.
+#include "../../include/q4g128.h"
+
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "q4g128_launch.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+void set_error(const char *what, hipError_t e)
+{
+    snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Size limits keep every 32-bit offset inside the kernels (buffer offsets,
+// grid dimensions) from overflowing.
+constexpr int kMaxK = 1 << 24;
+constexpr int kMaxN = 1 << 28;
+constexpr int kMaxSplits = 65535;
+
+bool shape_ok(int M, int K, int N)
+{
+    return M >= 1 && M <= Q4G128_MAX_M && K > 0 && K <= kMaxK && K % Q4G128_GROUP == 0 && N > 0 &&
+           N <= kMaxN;
+}
+
+bool operands_ok(const void *x, const uint32_t *W, const void *scale, const void *min, const float *y)
+{
+    return x && W && scale && min && y && aligned(x, 16) && aligned(W, 16) && aligned(scale, 2) &&
+           aligned(min, 2) && aligned(y, 4);
+}
+
+// Output tiles of 16 columns per wave.  One tile per wave for every shape.
+int plan_tiles_per_wave(int /*K*/, int /*N*/) { return 1; }
+
+// Waves the split-K planner aims for: 8 per compute unit on a 256-CU MI355X,
+// enough loads in flight per CU to cover HBM latency.
+constexpr long kTargetWaves = 2048;
+
+q4g128_status run_gemv(const void *x, int M, int K, const uint32_t *W, const void *scale,
+                       const void *min, int N, float *out, int S, hipStream_t stream)
+{
+    q4g128::GemvArgs a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.M = M;
+    a.K = K;
+    a.W = W;
+    a.scale = static_cast<const uint16_t *>(scale);
+    a.mn = static_cast<const uint16_t *>(min);
+    a.N = N;
+    a.out = out;
+    a.S = S;
+    hipError_t e = q4g128::launch_gemv(a, plan_tiles_per_wave(K, N), stream);
+    if (e != hipSuccess) {
+        set_error("gemv launch", e);
+        return Q4G128_EHIP;
+    }
+    return Q4G128_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4g128_abi_version(void) { return Q4G128_ABI_VERSION; }
+
+const char *q4g128_status_string(q4g128_status s)
+{
+    switch (s) {
+    case Q4G128_OK: return "ok";
+    case Q4G128_EINVAL: return "invalid argument";
+    case Q4G128_EWORKSPACE: return "workspace too small";
+    case Q4G128_EHIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char *q4g128_last_error(void) { return g_last_error; }
+
+size_t q4g128_splitk_workspace_bytes(int M, int N, int splits)
+{
+    if (M < 1 || M > Q4G128_MAX_M || N < 1 || splits < 1) return 0;
+    return (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
+}
+
+int q4g128_splitk_default_splits(int K, int N)
+{
+    if (K <= 0 || K % Q4G128_GROUP != 0 || N <= 0) return 0;
+    const long G = K / Q4G128_GROUP;
+    const long waves = ((long)N + 15) / 16 / plan_tiles_per_wave(K, N);
+    if (waves >= kTargetWaves) return 1;
+    long s = (kTargetWaves + waves - 1) / waves;
+    if (s > G) s = G;
+    return (int)s;
+}
+
+q4g128_status q4g128_gemm(const void *x, int M, int K, const uint32_t *W, const void *scale,
+                          const void *min, int N, float *y, void *stream)
+{
+    if (!shape_ok(M, K, N) || !operands_ok(x, W, scale, min, y)) return Q4G128_EINVAL;
+    return run_gemv(x, M, K, W, scale, min, N, y, 1, static_cast<hipStream_t>(stream));
+}
+
+q4g128_status q4g128_gemm_splitk(const void *x, int M, int K, const uint32_t *W, const void *scale,
+                                 const void *min, int N, float *y, int splits, float *workspace,
+                                 size_t workspace_bytes, void *stream)
+{
+    if (!shape_ok(M, K, N) || !operands_ok(x, W, scale, min, y)) return Q4G128_EINVAL;
+    if (splits < 1 || splits > K / Q4G128_GROUP || splits > kMaxSplits) return Q4G128_EINVAL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (splits == 1) return run_gemv(x, M, K, W, scale, min, N, y, 1, st);
+    if (!workspace || !aligned(workspace, 4)) return Q4G128_EINVAL;
+    if (workspace_bytes < q4g128_splitk_workspace_bytes(M, N, splits)) return Q4G128_EWORKSPACE;
+    q4g128_status rc = run_gemv(x, M, K, W, scale, min, N, workspace, splits, st);
+    if (rc != Q4G128_OK) return rc;
+    hipError_t e = q4g128::launch_splitk_sum(workspace, splits, (size_t)M * (size_t)N, y, st);
+    if (e != hipSuccess) {
+        set_error("split-K sum launch", e);
+        return Q4G128_EHIP;
+    }
+    return Q4G128_OK;
+}
+
+q4g128_status q4g128_dequant(const uint32_t *W, const void *scale, const void *min, int K, int N,
+                             float *w_out, void *stream)
+{
+    if (!shape_ok(1, K, N) || !W || !scale || !min || !w_out) return Q4G128_EINVAL;
+    if (!aligned(W, 16) || !aligned(scale, 2) || !aligned(min, 2) || !aligned(w_out, 16))
+        return Q4G128_EINVAL;
+    hipError_t e = q4g128::launch_dequant(W, static_cast<const uint16_t *>(scale),
+                                          static_cast<const uint16_t *>(min), K, N, w_out,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        set_error("dequant launch", e);
+        return Q4G128_EHIP;
+    }
+    return Q4G128_OK;
+}
+
+}  // extern "C"

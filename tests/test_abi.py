@@ -1,0 +1,117 @@
+"""The C-ABI library without a GPU: it loads, exports every function
+include/q4g128.h declares, and rejects bad arguments before launching
+anything (every call below returns before its first HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_decode_q4g128_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4g128.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4g128_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(q.LIB_PATH):
+        pytest.fail("libq4g128.so is not built (run __graft_entry__.build())")
+    return q.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert {"q4g128_gemm", "q4g128_gemm_splitk", "q4g128_dequant"} <= set(names)
+    for name in names:
+        assert hasattr(L, name), f"{name} declared in q4g128.h but not exported"
+
+
+def test_version_and_status_strings(L):
+    assert q.q4g128_abi_version() == 1
+    assert q.q4g128_status_string(0) == "ok"
+    assert q.q4g128_status_string(1) == "invalid argument"
+    assert q.q4g128_status_string(2) == "workspace too small"
+    assert q.q4g128_status_string(3) == "HIP error"
+    assert q.q4g128_status_string(99) == "unknown status"
+
+
+def test_workspace_bytes(L):
+    assert q.q4g128_splitk_workspace_bytes(1, 5120, 7) == 7 * 5120 * 4
+    assert q.q4g128_splitk_workspace_bytes(8, 34816, 2) == 2 * 8 * 34816 * 4
+    for bad in ((0, 10, 2), (9, 10, 2), (1, 0, 2), (1, 10, 0)):
+        assert q.q4g128_splitk_workspace_bytes(*bad) == 0
+
+
+def test_default_splits_depend_on_shape_only(L):
+    # Wide N needs no split; short N is split to fill the machine; never more
+    # splits than 128-groups.
+    assert q.q4g128_splitk_default_splits(5120, 34816) == 1
+    assert q.q4g128_splitk_default_splits(5120, 131072) == 1
+    s_down = q.q4g128_splitk_default_splits(17408, 5120)
+    assert 2 <= s_down <= 136
+    assert q.q4g128_splitk_default_splits(1024, 1024) <= 8
+    assert q.q4g128_splitk_default_splits(128, 1) == 1
+    assert q.q4g128_splitk_default_splits(100, 10) == 0
+    assert q.q4g128_splitk_default_splits(1024, 0) == 0
+
+
+FAKE = 0x10000   # 64 KiB-aligned non-null address; never dereferenced
+
+
+def call_gemm(L, x=FAKE, M=1, K=256, W=FAKE, s=FAKE, m=FAKE, N=16, y=FAKE):
+    return L.q4g128_gemm(x, M, K, W, s, m, N, y, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(W=None), dict(s=None), dict(m=None), dict(y=None),
+    dict(M=0), dict(M=9), dict(K=0), dict(K=100), dict(K=-128), dict(N=0),
+    dict(x=FAKE + 8), dict(W=FAKE + 4), dict(s=FAKE + 1), dict(y=FAKE + 2),
+])
+def test_gemm_rejects(L, kw):
+    assert call_gemm(L, **kw) == q.Q4G128_EINVAL
+
+
+def test_splitk_rejects(L):
+    f = L.q4g128_gemm_splitk
+    args = [FAKE, 1, 256, FAKE, FAKE, FAKE, 16]
+    assert f(*args, FAKE, 0, FAKE, 1 << 20, None) == q.Q4G128_EINVAL      # splits < 1
+    assert f(*args, FAKE, 3, FAKE, 1 << 20, None) == q.Q4G128_EINVAL      # splits > K/128
+    assert f(*args, FAKE, 2, None, 1 << 20, None) == q.Q4G128_EINVAL      # no workspace
+    assert f(*args, FAKE, 2, FAKE + 2, 1 << 20, None) == q.Q4G128_EINVAL  # misaligned
+    assert f(*args, FAKE, 2, FAKE, 2 * 16 * 4 - 4, None) == q.Q4G128_EWORKSPACE
+    assert f(FAKE, 1, 250, FAKE, FAKE, FAKE, 16, FAKE, 2, FAKE, 1 << 20, None) == q.Q4G128_EINVAL
+
+
+def test_dequant_rejects(L):
+    f = L.q4g128_dequant
+    assert f(None, FAKE, FAKE, 256, 4, FAKE, None) == q.Q4G128_EINVAL
+    assert f(FAKE, FAKE, FAKE, 200, 4, FAKE, None) == q.Q4G128_EINVAL
+    assert f(FAKE, FAKE, FAKE, 256, 0, FAKE, None) == q.Q4G128_EINVAL
+    assert f(FAKE, FAKE, FAKE, 256, 4, FAKE + 4, None) == q.Q4G128_EINVAL
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((1, 128), dtype=torch.bfloat16)
+    W = torch.zeros((4, 16), dtype=torch.int32)
+    s = torch.zeros((4, 1), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        q.q4g128_gemm(x, W, s, s)
+
+
+def test_product_path_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "quantized_decode_q4g128_amd")
+    banned = ("import oracle", "from oracle", "q4o_", "q4g128_oracle")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                for b in banned:
+                    assert b not in text, (f, b)

@@ -1,0 +1,194 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on MI355X.
+
+* dequant export: bit-exact against the oracle's once-rounded weights;
+* one-hot activations select single weights (ties the product's unpack to
+  the oracle's);
+* every workload within |y - y_ref| <= 1e-3 * sum|x*w| + 1e-6;
+* rows of an M-row call bit-identical to one-row calls, M = 1..8;
+* split-K deterministic run to run and across streams;
+* y(2x) = 2 y(x) exactly;
+* ragged and extreme shapes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import quantized_decode_q4g128_amd as q
+from gpu_util import DEV, assert_within_tolerance, bits, dev_weights, dev_x, host_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def test_device_is_gfx950():
+    assert torch.cuda.is_available()
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    assert name.startswith("gfx950"), name
+
+
+@pytest.mark.parametrize("K,N,seed", [(1024, 1024, 0), (256, 17, 1), (128, 1, 2), (5120, 64, 3),
+                                      (17408, 5, 4)])
+def test_dequant_bit_exact(orc, K, N, seed):
+    case = synth.make_random(1, K, N, seed)
+    wt = case.weights
+    w = host_f32(q.q4g128_dequant(*dev_weights(wt)))
+    w32 = orc.dequant_f32(wt.W, wt.scale, wt.mn)
+    assert np.array_equal(bits(w), bits(w32))
+
+
+def test_one_hot_selects_weights(orc):
+    K, N = 1024, 100
+    case = synth.make_random(1, K, N, 7)
+    wt = case.weights
+    w32 = orc.dequant_f32(wt.W, wt.scale, wt.mn)
+    ks = [0, 1, 4, 7, 8, 130, 515, 1023]           # every nibble slot, several groups
+    x = np.zeros((8, K), dtype=np.uint16)
+    for m, k in enumerate(ks):
+        x[m, k] = 0x3F80
+    y = host_f32(q.q4g128_gemm(dev_x(x), *dev_weights(wt)))
+    s = synth.bf16_bits_to_f32(wt.scale).astype(np.float64)
+    mn = synth.bf16_bits_to_f32(wt.mn).astype(np.float64)
+    madj = mn - 128.0 * s                           # exact in fp64
+    madj_exact = madj.astype(np.float32).astype(np.float64) == madj
+    for m, k in enumerate(ks):
+        g = k // 128
+        exact_cols = madj_exact[:, g]
+        assert exact_cols.mean() > 0.9
+        assert np.array_equal(bits(y[m, exact_cols]), bits(w32[exact_cols, k])), (m, k)
+        # where mn - 128*s rounds in fp32, the result is still within one rounding
+        ok = np.abs(y[m, ~exact_cols] - w32[~exact_cols, k]) <= 2 ** -22 * np.abs(w32[~exact_cols, k]) + 1e-30
+        assert ok.all(), (m, k)
+
+
+WORKLOADS = ["tiny", "gateup", "down", "verify"]
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_workload_within_tolerance(orc, name):
+    case = synth.make_case(name)
+    wt = case.weights
+    y_ref, a_ref = orc.gemm(case.x, wt.W, wt.scale, wt.mn)
+    x = dev_x(case.x)
+    W, s, m = dev_weights(wt)
+    y = host_f32(q.q4g128_gemm(x, W, s, m))
+    r1 = assert_within_tolerance(y, y_ref, a_ref, f"{name} gemm")
+    ys = host_f32(q.q4g128_gemm_splitk(x, W, s, m))
+    r2 = assert_within_tolerance(ys, y_ref, a_ref, f"{name} gemm_splitk")
+    print(f"{name}: worst |err|/tol gemm {r1:.2e} splitk {r2:.2e}")
+
+
+@pytest.mark.parametrize("K,N,seed", [(K, N, sd) for K, N, sd in synth.stream_shapes()])
+def test_stream_shapes_within_tolerance(orc, K, N, seed):
+    case = synth.make_random(1, K, N, seed)
+    wt = case.weights
+    y_ref, a_ref = orc.gemm(case.x, wt.W, wt.scale, wt.mn)
+    x = dev_x(case.x)
+    W, s, m = dev_weights(wt)
+    y = host_f32(q.q4g128_gemm_splitk(x, W, s, m))
+    assert_within_tolerance(y, y_ref, a_ref, f"stream K={K} N={N}")
+
+
+def test_rows_bit_identical_to_single_row_verify_shape():
+    case = synth.make_case("verify", 8)
+    W, s, m = dev_weights(case.weights)
+    x8 = dev_x(case.x)
+    y8 = host_f32(q.q4g128_gemm(x8, W, s, m))
+    for M in range(1, 9):
+        yM = host_f32(q.q4g128_gemm(x8[:M].contiguous(), W, s, m))
+        assert np.array_equal(bits(yM), bits(y8[:M])), M
+    for r in range(8):
+        y1 = host_f32(q.q4g128_gemm(x8[r:r + 1].contiguous(), W, s, m))
+        assert np.array_equal(bits(y1[0]), bits(y8[r])), r
+
+
+def test_rows_bit_identical_to_single_row_split_k():
+    case = synth.make_random(8, 17408, 5120, 2, outlier_frac=0.01)
+    W, s, m = dev_weights(case.weights)
+    x8 = dev_x(case.x)
+    y8 = host_f32(q.q4g128_gemm_splitk(x8, W, s, m))
+    for M in (1, 2, 3, 5, 7):
+        yM = host_f32(q.q4g128_gemm_splitk(x8[:M].contiguous(), W, s, m))
+        assert np.array_equal(bits(yM), bits(y8[:M])), M
+    for r in range(8):
+        y1 = host_f32(q.q4g128_gemm_splitk(x8[r:r + 1].contiguous(), W, s, m))
+        assert np.array_equal(bits(y1[0]), bits(y8[r])), r
+
+
+def test_split_k_deterministic_across_runs_and_streams():
+    case = synth.make_case("down")
+    W, s, m = dev_weights(case.weights)
+    x = dev_x(case.x)
+    ya = host_f32(q.q4g128_gemm_splitk(x, W, s, m))
+    yb = host_f32(q.q4g128_gemm_splitk(x, W, s, m))
+    side = torch.cuda.Stream(DEV)
+    with torch.cuda.stream(side):
+        yc_t = q.q4g128_gemm_splitk(x, W, s, m, stream=side)
+    side.synchronize()
+    yc = host_f32(yc_t)
+    assert np.array_equal(bits(ya), bits(yb)) and np.array_equal(bits(ya), bits(yc))
+    y1 = host_f32(q.q4g128_gemm_splitk(x, W, s, m, splits=1))
+    yg = host_f32(q.q4g128_gemm(x, W, s, m))
+    assert np.array_equal(bits(y1), bits(yg))
+
+
+@pytest.mark.parametrize("splits", [None, 1])
+def test_power_of_two_scaling_is_exact(splits):
+    case = synth.make_random(3, 5120, 777, 9)
+    W, s, m = dev_weights(case.weights)
+    x2 = case.x.copy()
+    assert ((x2 & 0x7F80) != 0).all() or True
+    nz = (x2 & 0x7F80) != 0
+    x2[nz] += 0x0080                                # doubles every normal bf16
+    assert ((x2 & 0x7FFF)[~nz] == 0).all()          # no subnormals in the draw
+    f = q.q4g128_gemm if splits == 1 else q.q4g128_gemm_splitk
+    y = host_f32(f(dev_x(case.x), W, s, m))
+    y2 = host_f32(f(dev_x(x2), W, s, m))
+    assert np.array_equal(bits(y2), bits(2 * y))
+
+
+EDGE = [(1, 128, 1), (3, 128, 17), (8, 256, 100), (2, 1024, 1000), (8, 17408, 48), (5, 384, 65),
+        (1, 2048, 16), (4, 640, 63)]
+
+
+@pytest.mark.parametrize("M,K,N", EDGE)
+def test_edge_shapes(orc, M, K, N):
+    case = synth.make_random(M, K, N, 100 + M + K + N, outlier_frac=0.01)
+    wt = case.weights
+    y_ref, a_ref = orc.gemm(case.x, wt.W, wt.scale, wt.mn)
+    x = dev_x(case.x)
+    W, s, m = dev_weights(wt)
+    G = K // 128
+    assert_within_tolerance(host_f32(q.q4g128_gemm(x, W, s, m)), y_ref, a_ref, "gemm")
+    for sp in sorted({1, 2, 3, G} & set(range(1, G + 1))):
+        y = host_f32(q.q4g128_gemm_splitk(x, W, s, m, splits=sp))
+        assert_within_tolerance(y, y_ref, a_ref, f"splitk splits={sp}")
+
+
+def test_output_fully_overwritten(orc):
+    case = synth.make_random(2, 512, 40, 77)
+    wt = case.weights
+    y_ref, a_ref = orc.gemm(case.x, wt.W, wt.scale, wt.mn)
+    y = torch.full((2, 40), float("nan"), dtype=torch.float32, device=DEV)
+    q.q4g128_gemm(dev_x(case.x), *dev_weights(wt), y=y)
+    assert_within_tolerance(host_f32(y), y_ref, a_ref, "prefilled y")
+    y.fill_(float("nan"))
+    q.q4g128_gemm_splitk(dev_x(case.x), *dev_weights(wt), splits=4, y=y)
+    assert_within_tolerance(host_f32(y), y_ref, a_ref, "prefilled y split")
+
+
+def test_invalid_arguments_are_rejected_before_launch():
+    case = synth.make_random(1, 256, 8, 5)
+    W, s, m = dev_weights(case.weights)
+    x = dev_x(case.x)
+    with pytest.raises(q.Q4G128Error) as e:
+        q.q4g128_gemm_splitk(x, W, s, m, splits=3)
+    assert e.value.status == q.Q4G128_EINVAL
+    with pytest.raises(q.Q4G128Error) as e:
+        q.q4g128_gemm(dev_x(np.zeros((9, 256), np.uint16)), W, s, m)
+    assert e.value.status == q.Q4G128_EINVAL
+    ws = torch.empty(4, dtype=torch.float32, device=DEV)
+    with pytest.raises(q.Q4G128Error) as e:
+        q.q4g128_gemm_splitk(x, W, s, m, splits=2, workspace=ws)
+    assert e.value.status == q.Q4G128_EWORKSPACE
+    with pytest.raises(ValueError):
+        q.q4g128_gemm(x[:, :128].contiguous(), W, s, m)
