@@ -35,7 +35,8 @@
  *     K <= 0, K > 2^24 or K % 128 != 0, N <= 0 or N > 2^28, splits > 65535,
  *     x or W or w_out not 16-byte aligned,
  *     scale or min not 2-byte aligned, y or workspace not 4-byte aligned,
- *     splits outside [1, K/128]) or Q4G128_EWORKSPACE (workspace too small),
+ *     splits outside [1, ceil(K/1024)]) or Q4G128_EWORKSPACE (workspace too
+ *     small),
  *     always before anything is enqueued.
  *   - A failed kernel launch returns Q4G128_EHIP; q4g128_last_error() then
  *     holds the HIP error text for the calling thread.
@@ -82,8 +83,9 @@ size_t q4g128_splitk_workspace_bytes(int M, int N, int splits);
  * "do not split"; returns 0 for invalid K or N. */
 int q4g128_splitk_default_splits(int K, int N);
 
-/* The product with K cut into `splits` contiguous, group-aligned ranges
- * (split s covers groups [s*G/splits, (s+1)*G/splits), G = K/128).  Each
+/* The product with K cut into `splits` contiguous ranges of whole blocks of
+ * 8 groups (1024 k): with nb = ceil(K/1024) blocks, split s covers blocks
+ * [s*nb/splits, (s+1)*nb/splits), so 1 <= splits <= nb.  Each
  * range writes fp32 partial sums to the workspace; a second pass sums them
  * in ascending s into y.  Deterministic; for splits == 1 it computes exactly
  * what q4g128_gemm computes.  For short N, where one column per lane gives

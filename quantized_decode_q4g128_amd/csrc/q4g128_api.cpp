@@ -37,6 +37,9 @@ bool operands_ok(const void *x, const uint32_t *W, const void *scale, const void
            aligned(min, 2) && aligned(y, 4);
 }
 
+// K splits align to blocks of kRing = 8 groups (1024 k).
+int max_splits(int K) { return (K / Q4G128_GROUP + q4g128::kRing - 1) / q4g128::kRing; }
+
 // Output tiles of 16 columns per wave.  One tile per wave for every shape.
 int plan_tiles_per_wave(int /*K*/, int /*N*/) { return 1; }
 
@@ -92,12 +95,17 @@ size_t q4g128_splitk_workspace_bytes(int M, int N, int splits)
 
 int q4g128_splitk_default_splits(int K, int N)
 {
-    if (K <= 0 || K % Q4G128_GROUP != 0 || N <= 0) return 0;
-    const long G = K / Q4G128_GROUP;
-    const long waves = ((long)N + 15) / 16 / plan_tiles_per_wave(K, N);
+    if (K <= 0 || K % Q4G128_GROUP != 0 || N <= 0 || K > kMaxK || N > kMaxN) return 0;
+    const long nb = max_splits(K);
+    const long tpw = plan_tiles_per_wave(K, N);
+    const long waves = ((long)N + 16 * tpw - 1) / (16 * tpw);
     if (waves >= kTargetWaves) return 1;
+    // Enough waves to fill the machine, then the fewest splits that keep the
+    // widest split as short as the most even division allows.
     long s = (kTargetWaves + waves - 1) / waves;
-    if (s > G) s = G;
+    if (s > nb) s = nb;
+    const long widest = (nb + s - 1) / s;
+    while (s > 1 && (nb + s - 2) / (s - 1) == widest) --s;
     return (int)s;
 }
 
@@ -113,7 +121,7 @@ q4g128_status q4g128_gemm_splitk(const void *x, int M, int K, const uint32_t *W,
                                  size_t workspace_bytes, void *stream)
 {
     if (!shape_ok(M, K, N) || !operands_ok(x, W, scale, min, y)) return Q4G128_EINVAL;
-    if (splits < 1 || splits > K / Q4G128_GROUP || splits > kMaxSplits) return Q4G128_EINVAL;
+    if (splits < 1 || splits > max_splits(K) || splits > kMaxSplits) return Q4G128_EINVAL;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (splits == 1) return run_gemv(x, M, K, W, scale, min, N, y, 1, st);
     if (!workspace || !aligned(workspace, 4)) return Q4G128_EINVAL;

@@ -9,204 +9,310 @@
 // Per 128-group the sum is factored as
 //   sum_k x*(q*s + mn) = s * sum_k x*(128 + q) + (mn - 128*s) * sum_k x
 // The codes enter a bf16 MFMA as the exact bf16 values 128 + q (a mask and an
-// OR per pair, no conversion); the x rows are the A operand, padded with zero
-// rows to 16; the row sums sum_k x come from a second MFMA against an all-ones
-// B operand.  Every output element is its own dot product inside the MFMA,
-// and the schedule of instructions depends on (K, N) only, so row m of an
-// M-row call is bit-identical to the one-row call (bw24 article, exactness
-// paragraph).
+// OR per pair, no conversion); the x rows are the A operand (A rows >= M
+// repeat a real row and are never stored); the group row sums sum_k x are
+// formed once per workgroup while x is staged (dot2 with ones, then a fixed
+// 16-lane tree).  Every output element is its own dot product inside the
+// MFMA, and the schedule of instructions depends on (K, N) only, so row m of
+// an M-row call is bit-identical to the one-row call (bw24 article,
+// exactness paragraph).
 //
 // Work layout: a workgroup of 4 waves owns 64*TPW output columns and one
 // contiguous range of 128-groups (the K split).  Each wave owns TPW tiles of
 // 16 columns; lane (i = l%16, h = l/16) streams column i's 16-byte code piece
 // h of every group (words 16g+4h .. 16g+4h+3), so the four lanes of a column
-// read its 64 contiguous bytes per group.  x for kChunk groups at a time sits
-// in LDS (double buffered), reordered into the pair order of the codes.
+// read its 64 contiguous bytes per group.  The workgroup stages x for up to
+// CG groups at a time in LDS (all of its K range unless M*K is large),
+// reordered into the pair order of the codes; lanes whose A row is >= M read
+// a real row, and their D rows are never stored.  The main loop has no
+// branches that depend on data: groups past the end of a range are processed
+// with scale and minimum forced to zero.
 #include "q4g128_device.h"
 #include "q4g128_launch.h"
 
 namespace q4g128 {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kChunk = 8;                      // groups per LDS x chunk; also prefetch depth
-constexpr int kRowStride = kChunk * 128 + 8;   // bf16 per LDS row: 16-byte pad vs bank conflicts
-constexpr int kPiecesPerRow = kChunk * 16;     // 16-byte x pieces per row per chunk
-constexpr int kStagePerThread = (kMaxM * kPiecesPerRow + kThreads - 1) / kThreads;
-
-static_assert(kPiecesPerRow == 128, "piece index math below assumes 128 pieces per row");
-
 // All outstanding LDS operations of this wave complete, then a workgroup
-// barrier.  Outstanding global loads (the code prefetch) are left in flight.
+// barrier.  Outstanding global loads (the code prefetch) stay in flight.
 __device__ __forceinline__ void lds_barrier()
 {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int TPW>
+// bf16 number j (0..7, a compile-time constant) of eight packed in a u32x4.
+__device__ __forceinline__ float bf16_at(const u32x4 &v, int j)
+{
+    const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
+    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+// x in LDS: row r of the staged range holds its 16-byte blocks (8 bf16 in
+// pair order) with block index b stored at b ^ (r & 7).  Lanes of one row
+// block read 8 different rows at the same block index; the XOR spreads them
+// over 8 different 16-byte bank groups, without padding rows.
+__device__ __forceinline__ int swz(int blk, int row) { return blk ^ (row & 7); }
+
+// One wave's share: TPW tiles of 16 columns, the groups [gs, ge) of one K
+// split.  x for the groups [cs, ce) being processed is in LDS (see swz),
+// followed by the x row sums of those groups, Xs[g - cs][row] (fp32).
+//
+// Loads: the codes of a group come from a ring of RING slots (slot = group
+// index mod RING, refilled RING groups ahead).  With VSM the scales and
+// minimums of 8 groups arrive in one 16-byte load per array; blocks of 8
+// groups alternate between two register sets (the loop body covers two
+// blocks, so the roles are static).  Without VSM, each group's scale and
+// minimum ride in the code ring, and a range may end inside a block: the
+// groups past its end are processed with scale and minimum zero (exact zeros)
+// on a copy of its last group's x.
+template <int TPW, bool VSM, int RING>
+struct Tile {
+    int i, h, M, K, G, gs, ge;
+    size_t K8;
+    __amdgpu_buffer_rsrc_t rw, rs, rm;
+    uint32_t vw[TPW], vs[TPW];
+    u32x4 cb[RING][TPW];
+    uint32_t sb[RING][TPW], mb[RING][TPW];       // !VSM
+    u32x4 sm[2][2][TPW];                          // VSM: [block set][scale, min][tile]
+    float acc[TPW][4];
+
+    __device__ __forceinline__ void fetch(int q, int g)
+    {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            cb[q][u] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw[u], 64 * g, 0);
+            if (!VSM) {
+                sb[q][u] = __builtin_amdgcn_raw_buffer_load_b16(rs, vs[u], 2 * g, 0);
+                mb[q][u] = __builtin_amdgcn_raw_buffer_load_b16(rm, vs[u], 2 * g, 0);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void fetch_sm(int set, int g8)
+    {
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            sm[set][0][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, vs[u], 2 * g8, 0);
+            sm[set][1][u] = __builtin_amdgcn_raw_buffer_load_b128(rm, vs[u], 2 * g8, 0);
+        }
+    }
+
+    // Fill the ring with the first RING groups of [cs, ce) (clamped to ce - 1)
+    // and, with VSM, the first block's scales and minimums.
+    __device__ __forceinline__ void prime(int cs, int ce)
+    {
+#pragma unroll
+        for (int q = 0; q < RING; ++q) fetch(q, min(cs + q, ce - 1));
+        if (VSM) fetch_sm(0, cs);
+    }
+
+    // Group g (LDS group index lg) from ring slot q; `set`/`j` locate its
+    // scale and minimum (VSM).
+    __device__ __forceinline__ void group(const uint16_t *rbase, const int (&aoff)[4], const float *xrow,
+                                          int ce, int q, int g, int lg, int set, int j, UnpackConsts uc)
+    {
+        const uint16_t *gp = rbase + lg * 128;
+        u32x4 a[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u32x4 *>(gp + aoff[t]);
+        const f32x4 xsum = *reinterpret_cast<const f32x4 *>(xrow + lg * 8);
+        // Consume the ring slot before its refill is issued, so the refill
+        // lands in the same registers.
+        u32x4 bq[TPW][4];
+        float s[TPW], m[TPW];
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            bq[u][0] = unpack_biased(cb[q][u].x, uc);
+            bq[u][1] = unpack_biased(cb[q][u].y, uc);
+            bq[u][2] = unpack_biased(cb[q][u].z, uc);
+            bq[u][3] = unpack_biased(cb[q][u].w, uc);
+            s[u] = VSM ? bf16_at(sm[set][0][u], j) : bf16_lo(sb[q][u]);
+            m[u] = VSM ? bf16_at(sm[set][1][u], j) : bf16_lo(mb[q][u]);
+        }
+        fetch(q, min(g + RING, ce - 1));
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) d = mfma_16x16x32(a[t], bq[u][t], d);
+            float sc = s[u];
+            float m_adj = fmaf(-kBias, s[u], m[u]);      // mn - 128*s, one rounding
+            if (!VSM && g >= ce) {                        // wave-uniform padding group
+                sc = 0.0f;
+                m_adj = 0.0f;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                acc[u][r] = fmaf(sc, d[r], acc[u][r]);
+                acc[u][r] = fmaf(m_adj, xsum[r], acc[u][r]);
+            }
+        }
+    }
+
+    // Groups [cs, ce), cs a multiple of 8 past gs; with VSM ce - cs is a
+    // multiple of 8 too.  The ring is refilled up to ce - 1.
+    __device__ __forceinline__ void run(const uint16_t *xs, int cs, int ce)
+    {
+        const UnpackConsts uc = unpack_consts();
+        const int ng = ce - cs;
+        const int arow = min(i, M - 1);          // rows >= M read a real row; never stored
+        const uint16_t *rbase = xs + arow * ng * 128;
+        const float *xrow = reinterpret_cast<const float *>(xs + M * ng * 128) + 4 * (h & 1);
+        int aoff[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) aoff[t] = swz(4 * h + t, arow) * 8;
+        const int last8 = cs + (ng - 1) / 8 * 8;         // first group of the last block
+        for (int g16 = cs; g16 < ce; g16 += 16) {
+            if (VSM) fetch_sm(1, min(g16 + 8, last8));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int g = g16 + j;
+                const int lg = VSM ? g - cs : min(g - cs, ng - 1);
+                group(rbase, aoff, xrow, ce, j % RING, g, lg, 0, j, uc);
+            }
+            if (g16 + 8 < ce) {                  // wave-uniform: odd block count
+                if (VSM) fetch_sm(0, min(g16 + 16, last8));
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int g = g16 + 8 + j;
+                    const int lg = VSM ? g - cs : min(g - cs, ng - 1);
+                    group(rbase, aoff, xrow, ce, (8 + j) % RING, g, lg, 1, j, uc);
+                }
+            }
+        }
+    }
+};
+
+// Sum of a float over each row of 16 lanes, by a fixed tree; lane 15 of the
+// row ends with the total.
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, false));
+    return v;
+}
+
+// Stage x[0..M)[cs*128 .. ce*128) into LDS (swizzled, pair order) and the
+// row sums Xs[g - cs][row] of each 128-group.  Piece p is 16 bytes: row
+// p / pr, block p % pr, pr = 16 * (ce - cs); the 16 pieces of one (row,
+// group) sit in one 16-lane row of a wave, whose lanes add their pieces'
+// sums by a fixed tree.  At most kStageMax pieces per thread.
+__device__ __forceinline__ void stage_x(uint16_t *xs, const uint16_t *__restrict__ x, int M, int K, int cs,
+                                        int ce)
+{
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    const int tid = threadIdx.x;
+    const int ng = ce - cs;
+    const int pr = ng * 16;
+    const int pieces = M * pr;
+    float *Xs = reinterpret_cast<float *>(xs + M * ng * 128);
+    u32x4 st[kStageMax];
+#pragma unroll
+    for (int j = 0; j < kStageMax; ++j) {
+        if (kThreads * j < pieces) {            // workgroup-uniform
+            const int p = min(tid + kThreads * j, pieces - 1);
+            const int row = p / pr, blk = p - row * pr;
+            st[j] = *reinterpret_cast<const u32x4 *>(x + (size_t)row * K + (size_t)cs * 128 + blk * 8);
+        }
+    }
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, kOnePair);
+#pragma unroll
+    for (int j = 0; j < kStageMax; ++j) {
+        if (kThreads * j < pieces) {
+            const int pu = tid + kThreads * j;
+            const int p = min(pu, pieces - 1);
+            const int row = p / pr, blk = p - row * pr;
+            *reinterpret_cast<u32x4 *>(&xs[(row * pr + swz(blk, row)) * 8]) = pair_order(st[j]);
+            // Each element goes through a scalar before the bit cast: this
+            // compiler bit-casts a vector element expression as element 0.
+            const uint32_t w0 = st[j].x, w1 = st[j].y, w2 = st[j].z, w3 = st[j].w;
+            float part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, 0.0f, false);
+            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, part, false);
+            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, part, false);
+            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, part, false);
+            const float tot = row16_sum(part);
+            if ((tid & 15) == 15 && pu < pieces) Xs[(blk >> 4) * 8 + row] = tot;
+        }
+    }
+}
+
+// CHUNKED = false: the workgroup's whole K range fits in LDS; x is staged
+// once.  CHUNKED = true: the range is processed CG groups at a time (CG a
+// multiple of 16), each chunk staged, primed and drained on its own.  Both
+// accumulate the same groups in the same order with the same instructions, so
+// they give identical bits.
+// A chunk of 16 groups of x for 8 rows must fit the staging registers.
+static_assert(kStageMax * kThreads >= 8 * 16 * 16, "x staging cannot hold one 16-group chunk at M = 8");
+
+template <int TPW, bool CHUNKED, bool VSM, int RING>
 __global__ __launch_bounds__(kThreads) void gemv_q4g128(
     const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ mn, int N,
-    float *__restrict__ out, int S)
+    float *__restrict__ out, int S, int CG)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][kMaxM * kRowStride];
-    __shared__ __attribute__((aligned(16))) uint16_t xzero[kChunk * 128];   // A rows >= M read here
+    extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int i = lane & 15;    // column within a tile; A row
-    const int h = lane >> 4;    // 16-byte code piece within a group; D row block
-    const int G = K >> 7;
-    const size_t K8 = (size_t)(K >> 3);
+    Tile<TPW, VSM, RING> T;
+    T.i = lane & 15;    // column within a tile; A row
+    T.h = lane >> 4;    // 16-byte code piece within a group; D row block
+    T.M = M;
+    T.K = K;
+    T.G = K >> 7;
+    T.K8 = (size_t)(K >> 3);
+    const int G = T.G;
+
+    // K split: split s covers 8-group blocks [s*nb/S, (s+1)*nb/S).
+    const int nb = (G + kRing - 1) / kRing;
     const int split = blockIdx.y;
-    const int gs = (int)(((long)split * G) / S);
-    const int ge = (int)(((long)(split + 1) * G) / S);
-    const int ng = ge - gs;
-    const int nchunks = (ng + kChunk - 1) / kChunk;
+    T.gs = (split * nb / S) * kRing;
+    T.ge = min(((split + 1) * nb / S) * kRing, G);
 
+    // Columns: waves past N alias the last column and store nothing.
     const int col0 = (blockIdx.x * kWaves + wave) * TPW * 16;
-    const bool wave_live = col0 < N;   // wave-uniform
-
-    // Wave-local buffer descriptors: codes, scales and minimums of this wave's
-    // 16*TPW columns; the group offset of every load is a scalar (soffset),
-    // the column offset a per-lane constant (voffset).
-    const int ncols = __builtin_amdgcn_readfirstlane(max(0, min(16 * TPW, N - col0)));
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + (size_t)col0 * K8, (uint32_t)((size_t)ncols * K8 * 4));
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(scale + (size_t)col0 * G, (uint32_t)(ncols * G * 2));
-    const __amdgpu_buffer_rsrc_t rm = make_rsrc(mn + (size_t)col0 * G, (uint32_t)(ncols * G * 2));
-    uint32_t vw[TPW], vs[TPW];
+    const int cbase = __builtin_amdgcn_readfirstlane(min(col0, N - 1));
+    const int ncols = __builtin_amdgcn_readfirstlane(max(1, min(16 * TPW, N - cbase)));
+    T.rw = make_rsrc(W + (size_t)cbase * T.K8, (uint32_t)((size_t)ncols * T.K8 * 4));
+    T.rs = make_rsrc(scale + (size_t)cbase * G, (uint32_t)(ncols * G * 2));
+    T.rm = make_rsrc(mn + (size_t)cbase * G, (uint32_t)(ncols * G * 2));
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-        const int c = min(16 * u + i, ncols - 1);   // ragged tail: read a real column, store nothing
-        vw[u] = (uint32_t)((size_t)c * K8 * 4 + 16 * h);
-        vs[u] = (uint32_t)(c * G * 2);
+        const int c = min(16 * u + T.i, ncols - 1);   // ragged tail: read a real column
+        T.vw[u] = (uint32_t)((size_t)c * T.K8 * 4 + 16 * T.h);
+        T.vs[u] = (uint32_t)(c * G * 2);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) T.acc[u][r] = 0.0f;
     }
 
-    // Code / scale / minimum prefetch ring: slot q holds group gs + c*kChunk + q.
-    // Loads past the end of the range re-read its last group (clamped), so the
-    // ring is refilled unconditionally.
-    u32x4 cb[kChunk][TPW];
-    uint32_t sb[kChunk][TPW], mb[kChunk][TPW];
-    auto fetch = [&](int q, int g) {
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            cb[q][u] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw[u], 64 * g, 0);
-            sb[q][u] = __builtin_amdgcn_raw_buffer_load_b16(rs, vs[u], 2 * g, 0);
-            mb[q][u] = __builtin_amdgcn_raw_buffer_load_b16(rm, vs[u], 2 * g, 0);
-        }
-    };
-    if (wave_live) {
-#pragma unroll
-        for (int q = 0; q < kChunk; ++q) fetch(q, min(gs + q, ge - 1));
-    }
-
-    // x staging: piece p = (row p/128, 16-byte block p%128 of the chunk).
-    const int pieces = M * kPiecesPerRow;
-    u32x4 st[kStagePerThread];
-    auto load_chunk = [&](int c) {
-#pragma unroll
-        for (int j = 0; j < kStagePerThread; ++j) {
-            const int p = tid + kThreads * j;
-            const int g = gs + c * kChunk + ((p & 127) >> 4);
-            if (p < pieces && g < ge)
-                st[j] = *reinterpret_cast<const u32x4 *>(x + (size_t)(p >> 7) * K + (size_t)g * 128 +
-                                                         (p & 15) * 8);
-        }
-    };
-    auto store_chunk = [&](int c, int buf) {
-#pragma unroll
-        for (int j = 0; j < kStagePerThread; ++j) {
-            const int p = tid + kThreads * j;
-            const int g = gs + c * kChunk + ((p & 127) >> 4);
-            if (p < pieces && g < ge)
-                *reinterpret_cast<u32x4 *>(&xs[buf][(p >> 7) * kRowStride + (p & 127) * 8]) =
-                    pair_order(st[j]);
-        }
-    };
-
-    static_assert(kChunk * 128 * 2 == kThreads * 8, "one 8-byte zero store per thread");
-    reinterpret_cast<uint2 *>(xzero)[tid] = make_uint2(0u, 0u);
-    load_chunk(0);
-    store_chunk(0, 0);
-    lds_barrier();
-
-    float acc[TPW][4];
-#pragma unroll
-    for (int u = 0; u < TPW; ++u)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[u][r] = 0.0f;
-
-    const u32x4 ones = {kOnePair, kOnePair, kOnePair, kOnePair};
-    const UnpackConsts uc = unpack_consts();
-
-    // One 128-group: A fragments from LDS, row sums, then per tile the code
-    // MFMAs and the scale/minimum epilogue.  `q` is the ring slot.
-    auto do_group = [&](const uint16_t *abase, int q, int g) {
-        u32x4 a[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u32x4 *>(abase + q * 128 + 8 * t);
-        f32x4 xsum = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) xsum = mfma_16x16x32(a[t], ones, xsum);
-        u32x4 cw[TPW];
-        uint32_t sv[TPW], mv[TPW];
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            cw[u] = cb[q][u];
-            sv[u] = sb[q][u];
-            mv[u] = mb[q][u];
-        }
-        fetch(q, min(g + kChunk, ge - 1));
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
-            d = mfma_16x16x32(a[0], unpack_biased(cw[u].x, uc), d);
-            d = mfma_16x16x32(a[1], unpack_biased(cw[u].y, uc), d);
-            d = mfma_16x16x32(a[2], unpack_biased(cw[u].z, uc), d);
-            d = mfma_16x16x32(a[3], unpack_biased(cw[u].w, uc), d);
-            const float s = bf16_lo(sv[u]);
-            const float m = bf16_lo(mv[u]);
-            const float m_adj = fmaf(-kBias, s, m);   // mn - 128*s, one rounding
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                acc[u][r] = fmaf(s, d[r], acc[u][r]);
-                acc[u][r] = fmaf(m_adj, xsum[r], acc[u][r]);
-            }
-        }
-    };
-
-    const bool row_live = i < M;
-    for (int c = 0; c < nchunks; ++c) {
-        const bool more = c + 1 < nchunks;
-        if (more) load_chunk(c + 1);
-        if (wave_live) {
-            const uint16_t *abase =
-                row_live ? &xs[c & 1][i * kRowStride + 32 * h] : &xzero[32 * h];
-            const int g0 = gs + c * kChunk;
-            if (g0 + kChunk <= ge) {
-#pragma unroll
-                for (int q = 0; q < kChunk; ++q) do_group(abase, q, g0 + q);
-            } else {
-#pragma unroll
-                for (int q = 0; q < kChunk; ++q)
-                    if (g0 + q < ge) do_group(abase, q, g0 + q);
-            }
-        }
-        if (more) store_chunk(c + 1, (c + 1) & 1);
+    if (!CHUNKED) {
+        T.prime(T.gs, T.ge);
+        stage_x(xs, x, M, K, T.gs, T.ge);
         lds_barrier();
+        T.run(xs, T.gs, T.ge);
+    } else {
+        for (int cs = T.gs; cs < T.ge; cs += CG) {
+            const int ce = min(cs + CG, T.ge);
+            T.prime(cs, ce);
+            stage_x(xs, x, M, K, cs, ce);
+            lds_barrier();
+            T.run(xs, cs, ce);
+            __builtin_amdgcn_s_waitcnt(0);      // chunk drained: ring and LDS reads done
+            lds_barrier();
+        }
     }
 
-    if (!wave_live) return;
     float *o = out + (size_t)split * (size_t)M * (size_t)N;
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-        const int n = col0 + 16 * u + i;
+        const int n = col0 + 16 * u + T.i;
         if (n < N) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = 4 * h + r;
-                if (row < M) o[(size_t)row * N + n] = acc[u][r];
+                const int row = 4 * T.h + r;
+                if (row < M) o[(size_t)row * N + n] = T.acc[u][r];
             }
         }
     }
@@ -257,22 +363,40 @@ __global__ __launch_bounds__(256) void dequant_q4g128(const uint32_t *__restrict
 
 int columns_per_block(int tpw) { return kWaves * 16 * tpw; }
 
+int chunk_groups(int M)
+{
+    int cg = kStageMax * kThreads / 16 / M;         // pieces per thread <= kStageMax
+    cg = cg / 16 * 16;
+    return cg < 16 ? 16 : cg;
+}
+
+template <int TPW, bool CHUNKED, bool VSM>
+static void launch_one(const GemvArgs &a, dim3 grid, int cg, hipStream_t stream)
+{
+    const size_t lds = (size_t)a.M * (size_t)cg * 128 * 2 + (size_t)cg * 8 * 4;
+    hipLaunchKernelGGL((gemv_q4g128<TPW, CHUNKED, VSM, kRingDepth>), grid, dim3(kThreads, 1, 1), lds, stream,
+                       a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.S, cg);
+}
+
 hipError_t launch_gemv(const GemvArgs &a, int tpw, hipStream_t stream)
 {
     const int cpb = columns_per_block(tpw);
+    // The widest split spans ceil(nb/S) blocks of 8 groups.
+    const int nb = (a.K / 128 + kRing - 1) / kRing;
+    const int span = (nb + a.S - 1) / a.S * kRing;
+    const int cg = chunk_groups(a.M);
+    const bool chunked = span > cg;
+    // 16-byte scale/minimum loads need K/128 a multiple of 8 and aligned bases.
+    const bool vsm = (a.K / 128) % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scale) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(a.mn) & 15) == 0;
     dim3 grid((unsigned)((a.N + cpb - 1) / cpb), (unsigned)a.S, 1);
-    dim3 block(kThreads, 1, 1);
-    switch (tpw) {
-    case 1:
-        hipLaunchKernelGGL(gemv_q4g128<1>, grid, block, 0, stream, a.x, a.M, a.K, a.W, a.scale, a.mn,
-                           a.N, a.out, a.S);
-        break;
-    case 2:
-        hipLaunchKernelGGL(gemv_q4g128<2>, grid, block, 0, stream, a.x, a.M, a.K, a.W, a.scale, a.mn,
-                           a.N, a.out, a.S);
-        break;
-    default:
-        return hipErrorInvalidValue;
+    if (tpw != 1) return hipErrorInvalidValue;
+    if (vsm) {
+        if (chunked) launch_one<1, true, true>(a, grid, cg, stream);
+        else launch_one<1, false, true>(a, grid, span, stream);
+    } else {
+        if (chunked) launch_one<1, true, false>(a, grid, cg, stream);
+        else launch_one<1, false, false>(a, grid, span, stream);
     }
     return hipGetLastError();
 }

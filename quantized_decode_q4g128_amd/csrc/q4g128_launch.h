@@ -8,7 +8,22 @@
 
 namespace q4g128 {
 
+#ifndef Q4G128_WAVES
+#define Q4G128_WAVES 4
+#endif
+#ifndef Q4G128_RING
+#define Q4G128_RING 8
+#endif
+#ifndef Q4G128_STAGE
+#define Q4G128_STAGE 10
+#endif
+
 constexpr int kMaxM = 8;
+constexpr int kWaves = Q4G128_WAVES;       // waves per workgroup (share one LDS copy of x)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRing = 8;                   // K splits align to blocks of 8 groups (1024 k)
+constexpr int kRingDepth = Q4G128_RING;    // groups of codes in flight per wave (8 or 16)
+constexpr int kStageMax = Q4G128_STAGE;    // 16-byte x pieces staged per thread per chunk
 
 struct GemvArgs {
     const uint16_t *x;       // bf16 [M][K]
@@ -18,8 +33,12 @@ struct GemvArgs {
     const uint16_t *mn;      // bf16 [N][K/128]
     int N;
     float *out;              // S == 1: y [M][N]; S > 1: partials [S][M][N]
-    int S;                   // K splits (group-aligned), 1..K/128
+    int S;                   // K splits, 1..ceil(K/1024): split s covers 8-group
+                             // blocks [s*nb/S, (s+1)*nb/S), nb = ceil(K/1024)
 };
+
+// x chunk (in 128-groups, a multiple of kRing) staged in LDS for M rows.
+int chunk_groups(int M);
 
 // Output columns one workgroup covers for a given tiles-per-wave setting.
 int columns_per_block(int tpw);

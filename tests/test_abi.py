@@ -55,8 +55,8 @@ def test_default_splits_depend_on_shape_only(L):
     assert q.q4g128_splitk_default_splits(5120, 34816) == 1
     assert q.q4g128_splitk_default_splits(5120, 131072) == 1
     s_down = q.q4g128_splitk_default_splits(17408, 5120)
-    assert 2 <= s_down <= 136
-    assert q.q4g128_splitk_default_splits(1024, 1024) <= 8
+    assert 2 <= s_down <= 17                  # at most one split per 1024 k
+    assert q.q4g128_splitk_default_splits(1024, 1024) == 1
     assert q.q4g128_splitk_default_splits(128, 1) == 1
     assert q.q4g128_splitk_default_splits(100, 10) == 0
     assert q.q4g128_splitk_default_splits(1024, 0) == 0
@@ -82,10 +82,11 @@ def test_splitk_rejects(L):
     f = L.q4g128_gemm_splitk
     args = [FAKE, 1, 256, FAKE, FAKE, FAKE, 16]
     assert f(*args, FAKE, 0, FAKE, 1 << 20, None) == q.Q4G128_EINVAL      # splits < 1
-    assert f(*args, FAKE, 3, FAKE, 1 << 20, None) == q.Q4G128_EINVAL      # splits > K/128
-    assert f(*args, FAKE, 2, None, 1 << 20, None) == q.Q4G128_EINVAL      # no workspace
-    assert f(*args, FAKE, 2, FAKE + 2, 1 << 20, None) == q.Q4G128_EINVAL  # misaligned
-    assert f(*args, FAKE, 2, FAKE, 2 * 16 * 4 - 4, None) == q.Q4G128_EWORKSPACE
+    assert f(*args, FAKE, 2, FAKE, 1 << 20, None) == q.Q4G128_EINVAL      # splits > ceil(K/1024)
+    big = [FAKE, 1, 2048, FAKE, FAKE, FAKE, 16]
+    assert f(*big, FAKE, 2, None, 1 << 20, None) == q.Q4G128_EINVAL       # no workspace
+    assert f(*big, FAKE, 2, FAKE + 2, 1 << 20, None) == q.Q4G128_EINVAL   # misaligned
+    assert f(*big, FAKE, 2, FAKE, 2 * 16 * 4 - 4, None) == q.Q4G128_EWORKSPACE
     assert f(FAKE, 1, 250, FAKE, FAKE, FAKE, 16, FAKE, 2, FAKE, 1 << 20, None) == q.Q4G128_EINVAL
 
 
