@@ -97,6 +97,34 @@ q4g128_status q4g128_gemm_splitk(const void *x, int M, int K,
                                  float *workspace, size_t workspace_bytes,
                                  void *stream);
 
+/* Bytes of workspace q4g128_gemm_streamk needs for a (K, N) shape: 2 MiB of
+ * partial-sum slots plus 4 * ceil(N/16) bytes of counters, rounded up to
+ * 256.  Independent of M.  Returns 0 if the shape is not supported (K not a
+ * positive multiple of 1024, N outside [1, 2^28]). */
+size_t q4g128_streamk_workspace_bytes(int K, int N);
+
+/* The product with the work spread evenly over the compute units (stream-K):
+ * one workgroup per compute unit, each wave an equal contiguous share of the
+ * (16-column tile, 1024-k block) units.  A tile split between waves is
+ * summed in parts; the last wave to finish it adds the parts in a fixed
+ * order (determined by K, N and the device's compute-unit count), so results
+ * are deterministic and rows are bit-identical across M, but they differ in
+ * rounding from q4g128_gemm.  Passages: Token Rush README, bandwidth
+ * paragraph (decode is bound by streaming the weights: every CU must stream
+ * its share at full rate) and steps table rows 8-9 (partial sums over K).
+ *
+ * Requirements beyond the common ones: K % 1024 == 0; scale and min 16-byte
+ * aligned; workspace 256-byte aligned, at least
+ * q4g128_streamk_workspace_bytes(K, N) bytes, ZERO-FILLED before its first
+ * use.  Every call leaves the counters it used at zero again, so a workspace
+ * can be reused call after call, but not by two calls in flight at once.
+ * Returns Q4G128_EINVAL for an unsupported shape (large K is cut into slices
+ * internally; shapes whose slices cannot hold 8 rows of x are rejected). */
+q4g128_status q4g128_gemm_streamk(const void *x, int M, int K,
+                                  const uint32_t *W, const void *scale, const void *min,
+                                  int N, float *y, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
 /* Decoded weights w_out[n][k] = fp32(q*s + m), rounded once (fma), laid out
  * fp32 [N][K].  Uses the same device unpacking as the product; it exists so
  * tests can compare the unpack and dequant bit for bit.  Passage: Token Rush

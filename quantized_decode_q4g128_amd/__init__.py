@@ -49,6 +49,10 @@ def lib() -> ctypes.CDLL:
         L.q4g128_gemm.restype = ci
         L.q4g128_gemm_splitk.argtypes = [vp, ci, ci, vp, vp, vp, ci, vp, ci, vp, sz, vp]
         L.q4g128_gemm_splitk.restype = ci
+        L.q4g128_gemm_streamk.argtypes = [vp, ci, ci, vp, vp, vp, ci, vp, vp, sz, vp]
+        L.q4g128_gemm_streamk.restype = ci
+        L.q4g128_streamk_workspace_bytes.argtypes = [ci, ci]
+        L.q4g128_streamk_workspace_bytes.restype = sz
         L.q4g128_dequant.argtypes = [vp, vp, vp, ci, ci, vp, vp]
         L.q4g128_dequant.restype = ci
         L.q4g128_splitk_workspace_bytes.argtypes = [ci, ci, ci]
@@ -173,6 +177,36 @@ def q4g128_gemm_splitk(x, W, scale, min, splits=None, workspace=None, y=None, st
     return y
 
 
+def q4g128_streamk_workspace_bytes(K: int, N: int) -> int:
+    return int(lib().q4g128_streamk_workspace_bytes(int(K), int(N)))
+
+
+def q4g128_streamk_workspace(K: int, N: int, device) -> torch.Tensor:
+    """A zero-filled workspace for q4g128_gemm_streamk on (K, N); reusable by
+    successive calls (each call leaves it zero-filled), one call at a time."""
+    nbytes = q4g128_streamk_workspace_bytes(K, N)
+    if nbytes == 0:
+        raise ValueError(f"stream-K does not support K={K}, N={N} (K must be a multiple of 1024)")
+    return torch.zeros((nbytes // 4,), dtype=torch.int32, device=device)
+
+
+def q4g128_gemm_streamk(x, W, scale, min, workspace=None, y=None, stream=None) -> torch.Tensor:
+    """y = x . dequant(W) with the work spread evenly over the compute units.
+    `workspace` must come from q4g128_streamk_workspace (zero-filled) and must
+    not be in use by another call in flight; one is allocated if not given."""
+    x, W, scale, min, M, K, N = _operands(x, W, scale, min)
+    y = _out(y, M, N, x.device)
+    if workspace is None:
+        workspace = q4g128_streamk_workspace(K, N, x.device)
+    if workspace.device != x.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the operands' device")
+    st = lib().q4g128_gemm_streamk(x.data_ptr(), M, K, W.data_ptr(), scale.data_ptr(), min.data_ptr(), N,
+                                   y.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   _stream(stream, x.device))
+    _check(st, "q4g128_gemm_streamk")
+    return y
+
+
 def q4g128_dequant(W, scale, min, out=None, stream=None) -> torch.Tensor:
     """Decoded weights fp32 [N][K], w = fp32(q*s + m) rounded once."""
     W = _dev(W, "W", _WORD)
@@ -192,6 +226,7 @@ def q4g128_dequant(W, scale, min, out=None, stream=None) -> torch.Tensor:
     return out
 
 
-__all__ = ["q4g128_gemm", "q4g128_gemm_splitk", "q4g128_dequant", "q4g128_splitk_workspace_bytes",
+__all__ = ["q4g128_gemm", "q4g128_gemm_splitk", "q4g128_gemm_streamk", "q4g128_streamk_workspace",
+           "q4g128_streamk_workspace_bytes", "q4g128_dequant", "q4g128_splitk_workspace_bytes",
            "q4g128_splitk_default_splits", "q4g128_status_string", "q4g128_last_error",
            "q4g128_abi_version", "Q4G128Error", "lib", "LIB_PATH"]

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libq4g128.so")
-SOURCES = [os.path.join(CSRC, "q4g128_kernels.hip"), os.path.join(CSRC, "q4g128_api.cpp")]
+SOURCES = [os.path.join(CSRC, "q4g128_kernels.hip"), os.path.join(CSRC, "q4g128_streamk.hip"),
+           os.path.join(CSRC, "q4g128_api.cpp")]
 ARCH = "gfx950"
 
 

@@ -68,6 +68,24 @@ q4g128_status run_gemv(const void *x, int M, int K, const uint32_t *W, const voi
     return Q4G128_OK;
 }
 
+// Stream-K workspace: partial-sum slots first, then one counter per tile.
+constexpr size_t kSkPartBytes = (size_t)2 * q4g128::kSkMaxWaves * 128 * sizeof(float);
+
+size_t streamk_ws_bytes(int N)
+{
+    const size_t tiles = ((size_t)N + 15) / 16;
+    return (kSkPartBytes + tiles * 4 + 255) / 256 * 256;
+}
+
+// Compute units of the calling thread's current device, or -1.
+int device_cus()
+{
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    return ncu;
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,6 +149,47 @@ q4g128_status q4g128_gemm_splitk(const void *x, int M, int K, const uint32_t *W,
     hipError_t e = q4g128::launch_splitk_sum(workspace, splits, (size_t)M * (size_t)N, y, st);
     if (e != hipSuccess) {
         set_error("split-K sum launch", e);
+        return Q4G128_EHIP;
+    }
+    return Q4G128_OK;
+}
+
+size_t q4g128_streamk_workspace_bytes(int K, int N)
+{
+    if (K <= 0 || K % 1024 != 0 || K > kMaxK || N < 1 || N > kMaxN) return 0;
+    return streamk_ws_bytes(N);
+}
+
+q4g128_status q4g128_gemm_streamk(const void *x, int M, int K, const uint32_t *W, const void *scale,
+                                  const void *min, int N, float *y, void *workspace, size_t workspace_bytes,
+                                  void *stream)
+{
+    if (!shape_ok(M, K, N) || !operands_ok(x, W, scale, min, y)) return Q4G128_EINVAL;
+    if (K % 1024 != 0 || !aligned(scale, 16) || !aligned(min, 16)) return Q4G128_EINVAL;
+    if (!workspace || !aligned(workspace, 256)) return Q4G128_EINVAL;
+    if (workspace_bytes < streamk_ws_bytes(N)) return Q4G128_EWORKSPACE;
+    const int ncu = device_cus();
+    if (ncu < 0) {
+        set_error("device query", hipGetLastError());
+        return Q4G128_EHIP;
+    }
+    q4g128::SkShape plan;
+    if (!q4g128::streamk_plan(K, N, ncu, &plan)) return Q4G128_EINVAL;
+    q4g128::GemvArgs a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.M = M;
+    a.K = K;
+    a.W = W;
+    a.scale = static_cast<const uint16_t *>(scale);
+    a.mn = static_cast<const uint16_t *>(min);
+    a.N = N;
+    a.out = y;
+    a.S = 1;
+    float *parts = static_cast<float *>(workspace);
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + kSkPartBytes);
+    hipError_t e = q4g128::launch_gemv_streamk(a, plan, parts, cnt, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        set_error("stream-K launch", e);
         return Q4G128_EHIP;
     }
     return Q4G128_OK;

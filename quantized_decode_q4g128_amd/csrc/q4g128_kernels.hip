@@ -29,28 +29,9 @@
 // with scale and minimum forced to zero.
 #include "q4g128_device.h"
 #include "q4g128_launch.h"
+#include "q4g128_stage.h"
 
 namespace q4g128 {
-
-// All outstanding LDS operations of this wave complete, then a workgroup
-// barrier.  Outstanding global loads (the code prefetch) stay in flight.
-__device__ __forceinline__ void lds_barrier()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// bf16 number j (0..7, a compile-time constant) of eight packed in a u32x4.
-__device__ __forceinline__ float bf16_at(const u32x4 &v, int j)
-{
-    const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
-    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
-}
-
-// x in LDS: row r of the staged range holds its 16-byte blocks (8 bf16 in
-// pair order) with block index b stored at b ^ (r & 7).  Lanes of one row
-// block read 8 different rows at the same block index; the XOR spreads them
-// over 8 different 16-byte bank groups, without padding rows.
-__device__ __forceinline__ int swz(int blk, int row) { return blk ^ (row & 7); }
 
 // One wave's share: TPW tiles of 16 columns, the groups [gs, ge) of one K
 // split.  x for the groups [cs, ce) being processed is in LDS (see swz),
@@ -182,61 +163,6 @@ struct Tile {
     }
 };
 
-// Sum of a float over each row of 16 lanes, by a fixed tree; lane 15 of the
-// row ends with the total.
-__device__ __forceinline__ float row16_sum(float v)
-{
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, false));
-    return v;
-}
-
-// Stage x[0..M)[cs*128 .. ce*128) into LDS (swizzled, pair order) and the
-// row sums Xs[g - cs][row] of each 128-group.  Piece p is 16 bytes: row
-// p / pr, block p % pr, pr = 16 * (ce - cs); the 16 pieces of one (row,
-// group) sit in one 16-lane row of a wave, whose lanes add their pieces'
-// sums by a fixed tree.  At most kStageMax pieces per thread.
-__device__ __forceinline__ void stage_x(uint16_t *xs, const uint16_t *__restrict__ x, int M, int K, int cs,
-                                        int ce)
-{
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-    const int tid = threadIdx.x;
-    const int ng = ce - cs;
-    const int pr = ng * 16;
-    const int pieces = M * pr;
-    float *Xs = reinterpret_cast<float *>(xs + M * ng * 128);
-    u32x4 st[kStageMax];
-#pragma unroll
-    for (int j = 0; j < kStageMax; ++j) {
-        if (kThreads * j < pieces) {            // workgroup-uniform
-            const int p = min(tid + kThreads * j, pieces - 1);
-            const int row = p / pr, blk = p - row * pr;
-            st[j] = *reinterpret_cast<const u32x4 *>(x + (size_t)row * K + (size_t)cs * 128 + blk * 8);
-        }
-    }
-    const bf16x2 ones = __builtin_bit_cast(bf16x2, kOnePair);
-#pragma unroll
-    for (int j = 0; j < kStageMax; ++j) {
-        if (kThreads * j < pieces) {
-            const int pu = tid + kThreads * j;
-            const int p = min(pu, pieces - 1);
-            const int row = p / pr, blk = p - row * pr;
-            *reinterpret_cast<u32x4 *>(&xs[(row * pr + swz(blk, row)) * 8]) = pair_order(st[j]);
-            // Each element goes through a scalar before the bit cast: this
-            // compiler bit-casts a vector element expression as element 0.
-            const uint32_t w0 = st[j].x, w1 = st[j].y, w2 = st[j].z, w3 = st[j].w;
-            float part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, 0.0f, false);
-            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, part, false);
-            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, part, false);
-            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, part, false);
-            const float tot = row16_sum(part);
-            if ((tid & 15) == 15 && pu < pieces) Xs[(blk >> 4) * 8 + row] = tot;
-        }
-    }
-}
-
 // CHUNKED = false: the workgroup's whole K range fits in LDS; x is staged
 // once.  CHUNKED = true: the range is processed CG groups at a time (CG a
 // multiple of 16), each chunk staged, primed and drained on its own.  Both
@@ -289,14 +215,14 @@ __global__ __launch_bounds__(kThreads) void gemv_q4g128(
 
     if (!CHUNKED) {
         T.prime(T.gs, T.ge);
-        stage_x(xs, x, M, K, T.gs, T.ge);
+        stage_x<kThreads, kStageMax>(xs, x, M, K, T.gs, T.ge);
         lds_barrier();
         T.run(xs, T.gs, T.ge);
     } else {
         for (int cs = T.gs; cs < T.ge; cs += CG) {
             const int ce = min(cs + CG, T.ge);
             T.prime(cs, ce);
-            stage_x(xs, x, M, K, cs, ce);
+            stage_x<kThreads, kStageMax>(xs, x, M, K, cs, ce);
             lds_barrier();
             T.run(xs, cs, ce);
             __builtin_amdgcn_s_waitcnt(0);      // chunk drained: ring and LDS reads done

@@ -40,6 +40,31 @@ struct GemvArgs {
 // x chunk (in 128-groups, a multiple of kRing) staged in LDS for M rows.
 int chunk_groups(int M);
 
+// ---- work-balanced (stream-K) kernel ----------------------------------------
+constexpr int kSkWaves = 8;                 // waves per workgroup, one workgroup per CU
+constexpr int kSkThreads = 64 * kSkWaves;
+constexpr int kSkMaxBlocks = 9;             // blocks of 1024 k per K slice: 8 rows of x fit LDS
+constexpr int kSkStage = 8 * kSkMaxBlocks * 8 * 16 / kSkThreads;   // x pieces per thread
+constexpr int kSkMaxWaves = 256 * kSkWaves; // waves of the largest launch (256 CUs)
+
+// Partition of the units (tile of 16 columns, block of 8 groups): K is cut
+// into SK slices of whole blocks; each slice's units are split evenly over
+// Wsl waves.
+struct SkShape {
+    int T;      // tiles, ceil(N / 16)
+    int nb;     // blocks per column, K / 1024
+    int SK;     // K slices
+    int Wsl;    // waves per slice
+};
+
+// Plan for (K, N) on a device with `ncu` compute units; false if the shape
+// is not supported (K not a multiple of 1024, too many slices, offsets).
+bool streamk_plan(int K, int N, int ncu, SkShape *p);
+size_t streamk_lds_bytes(const SkShape &p, int M);
+// parts: 2 * kSkMaxWaves slots of 512 bytes; cnt: T zero-filled counters.
+hipError_t launch_gemv_streamk(const GemvArgs &a, const SkShape &p, float *parts, uint32_t *cnt,
+                               hipStream_t stream);
+
 // Output columns one workgroup covers for a given tiles-per-wave setting.
 int columns_per_block(int tpw);
 

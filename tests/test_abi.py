@@ -116,3 +116,23 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 for b in banned:
                     assert b not in text, (f, b)
+
+
+def test_streamk_workspace_bytes(L):
+    parts = 2 * 2048 * 128 * 4
+    assert q.q4g128_streamk_workspace_bytes(5120, 34816) == (parts + 4 * 2176 + 255) // 256 * 256
+    assert q.q4g128_streamk_workspace_bytes(1024, 1) == (parts + 4 + 255) // 256 * 256
+    assert q.q4g128_streamk_workspace_bytes(5120 + 128, 16) == 0      # K not a multiple of 1024
+    assert q.q4g128_streamk_workspace_bytes(1024, 0) == 0
+
+
+def test_streamk_rejects(L):
+    f = L.q4g128_gemm_streamk
+    ok = [FAKE, 1, 2048, FAKE, FAKE, FAKE, 16, FAKE]
+    need = q.q4g128_streamk_workspace_bytes(2048, 16)
+    assert f(FAKE, 1, 2048 + 128, FAKE, FAKE, FAKE, 16, FAKE, FAKE, need, None) == q.Q4G128_EINVAL
+    assert f(*ok, None, need, None) == q.Q4G128_EINVAL                   # no workspace
+    assert f(*ok, FAKE + 16, need, None) == q.Q4G128_EINVAL              # not 256-byte aligned
+    assert f(*ok, FAKE, need - 4, None) == q.Q4G128_EWORKSPACE
+    assert f(FAKE, 1, 2048, FAKE, FAKE + 2, FAKE, 16, FAKE, FAKE, need, None) == q.Q4G128_EINVAL   # scale not 16-aligned
+    assert f(FAKE, 9, 2048, FAKE, FAKE, FAKE, 16, FAKE, FAKE, need, None) == q.Q4G128_EINVAL
