@@ -16,10 +16,22 @@ the host as a baseline.  A result that fails parity against the oracle is not
 reported (value null).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+HBM traffic of the dominant kernel comes from two rocprofv3 counter runs
+(FETCH_SIZE, then WRITE_SIZE) of `--pmc-workload`, turned into a summary by
+`--pmc-summarize`; the summary is keyed by a hash of the kernel sources and
+ignored once they change:
+
+    rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run --output-format csv -- python3 bench.py --pmc-workload
+    rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run --output-format csv -- python3 bench.py --pmc-workload
+    python3 bench.py --pmc-summarize OUT/fetch OUT/write profiles/gemv_q4g128_gateup_pmc.txt
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -37,6 +49,10 @@ import synth  # noqa: E402
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 ROTATE_BYTES = 1.2e9            # > 4x the 256 MB last-level cache
 METRIC = "achieved HBM GB/s (% of MI355X peak) for int4-g128 GEMV at M=1 and M=7"
+KERNEL = "gemv_q4g128"          # the dominant (only) kernel of a decode step
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_q4g128_gateup_pmc.txt")
+COPY_BYTES = 256 << 20          # calibration copy for the traffic counters
+PMC_LAUNCHES = 24
 
 
 def parse():
@@ -47,18 +63,33 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="bounded CPU time budget for the oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--pmc-workload", action="store_true",
+                   help="run the counter workload (a known-size copy, then decode launches) and exit")
+    p.add_argument("--pmc-summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
+                   help="turn two rocprofv3 counter runs of --pmc-workload into a traffic summary")
     return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources and headers the kernels are built from."""
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "quantized_decode_q4g128_amd")
+    for path in sorted(glob.glob(os.path.join(pkg, "csrc", "*")) + [os.path.join(pkg, "build.py")]):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 class Rotation:
     """R device copies of one weight set plus one x; call i uses copy i % R."""
 
-    def __init__(self, case, torch, q):
+    def __init__(self, case, torch, q, copies=None):
         self.torch, self.q = torch, q
         wt = case.weights
         self.M, self.K, self.N = case.M, case.K, case.N
         self.bytes = synth.algorithmic_bytes(self.M, self.K, self.N)
-        self.R = max(2, math.ceil(ROTATE_BYTES / self.bytes))
+        self.R = copies or max(2, math.ceil(ROTATE_BYTES / self.bytes))
         dev = torch.device("cuda:0")
         W = torch.from_numpy(wt.W.view(np.int32)).to(dev)
         s = torch.from_numpy(wt.scale.view(np.int16)).to(dev)
@@ -102,22 +133,123 @@ def cpu_baseline(case, budget_s):
         reps += 1
     dt = (time.perf_counter() - t0) / reps
     B = synth.algorithmic_bytes(case.M, case.K, case.N)
-    return {"value": B / dt / 1e9, "unit": "GB/s", "cores": orc.max_threads(), "kind": "oracle",
+    return {"value": round(B / dt / 1e9, 4), "unit": "GB/s", "cores": orc.max_threads(), "kind": "oracle",
             "sample": f"{reps} full fp64 oracle calls on the same M={case.M} K={case.K} N={case.N} "
-                      f"input ({dt * 1e3:.1f} ms per call)"}, (y, a)
+                      f"input ({dt * 1e3:.1f} ms per call, {reps * dt:.1f} s in all)"}, (y, a)
 
+
+# ---- HBM traffic from counters ------------------------------------------------
+
+def pmc_workload():
+    """One elementwise copy of COPY_BYTES (the calibration: it reads and
+    writes exactly that many bytes), then PMC_LAUNCHES decode launches over
+    rotating weight copies."""
+    import torch
+    import quantized_decode_q4g128_amd as q
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1, out=dst)              # an elementwise kernel: reads and writes COPY_BYTES
+    torch.cuda.synchronize()
+    rot = Rotation(synth.make_case("gateup"), torch, q)
+    stream = torch.cuda.current_stream()
+    for i in range(PMC_LAUNCHES):
+        rot.call(i, stream)
+    torch.cuda.synchronize()
+    print(f"pmc workload: copy {COPY_BYTES} B, {PMC_LAUNCHES} launches of {KERNEL}", flush=True)
+
+
+def _counter_per_dispatch(d, name_filter):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            if name_filter(r["Kernel_Name"]):
+                per[int(r["Dispatch_Id"])] = per.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
+    return [per[k] for k in sorted(per)]
+
+
+def pmc_summarize(fetch_dir, write_dir, out):
+    is_kernel = lambda n: KERNEL in n and "streamk" not in n and "splitk" not in n
+    is_copy = lambda n: "MulFunctor" in n
+    lines = {}
+    for label, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        k = _counter_per_dispatch(d, is_kernel)
+        c = _counter_per_dispatch(d, is_copy)
+        if not k or not c:
+            raise SystemExit(f"{label}: missing dispatches (kernel {len(k)}, copy {len(c)})")
+        copy_kib = max(c)                   # the calibration copy
+        factor = (COPY_BYTES / 1024.0) / copy_kib
+        steady = k[len(k) // 4:]            # skip the first launches
+        lines[label] = (float(np.mean(steady)), copy_kib, factor, len(steady))
+    case = synth.make_case("gateup")
+    B = synth.algorithmic_bytes(case.M, case.K, case.N)
+    fetch_b = lines["FETCH_SIZE"][0] * 1024 * lines["FETCH_SIZE"][2]
+    write_b = lines["WRITE_SIZE"][0] * 1024 * lines["WRITE_SIZE"][2]
+    with open(out, "w") as f:
+        f.write(f"# HBM traffic of {KERNEL} on the decode gate/up projection (M=1 K=5120 N=34816)\n")
+        f.write("# commands (from the repository root; rocprofv3 run from /tmp with TMPDIR=/tmp):\n")
+        f.write("#   rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run --output-format csv -- "
+                "python3 bench.py --pmc-workload\n")
+        f.write("#   rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run --output-format csv -- "
+                "python3 bench.py --pmc-workload\n")
+        f.write("#   python3 bench.py --pmc-summarize OUT/fetch OUT/write " + os.path.relpath(out, ROOT) + "\n")
+        f.write("# calibration: one device copy of copy_bytes; factor = copy_bytes / counter reading\n")
+        f.write(f"kernel_source_hash: {kernel_source_hash()}\n")
+        f.write(f"copy_bytes: {COPY_BYTES}\n")
+        for label in ("FETCH_SIZE", "WRITE_SIZE"):
+            mean, copy_kib, factor, n = lines[label]
+            f.write(f"{label}_kernel_kib_per_dispatch: {mean:.1f}\n")
+            f.write(f"{label}_kernel_dispatches_averaged: {n}\n")
+            f.write(f"{label}_copy_kib: {copy_kib:.1f}\n")
+            f.write(f"{label}_factor: {factor:.4f}\n")
+        f.write(f"fetch_bytes_per_launch: {fetch_b:.0f}\n")
+        f.write(f"write_bytes_per_launch: {write_b:.0f}\n")
+        f.write(f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}\n")
+        f.write(f"algorithmic_bytes_per_launch: {B}\n")
+        f.write(f"traffic_over_algorithmic: {(fetch_b + write_b) / B:.4f}\n")
+    print(open(out).read())
+
+
+def traffic_from_summary():
+    """HBM bytes per launch from the committed counter summary, or None when
+    it is missing or was taken on other kernel sources."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    kv = {}
+    with open(PMC_SUMMARY) as f:
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+# ---- main --------------------------------------------------------------------
 
 def main():
     args = parse()
+    if args.pmc_summarize:
+        pmc_summarize(*args.pmc_summarize)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the product runs on one GPU's "
+              f"share of the weights and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
     import torch
     import quantized_decode_q4g128_amd as q
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.pmc_workload:
+        pmc_workload()
+        return
 
     dec_case = synth.make_case("gateup")
     ver_case = synth.make_case("verify", 7)
@@ -149,6 +281,7 @@ def main():
     gbps = dec.bytes * args.steps / (wall_d * 1e-3) / 1e9
     achieved = dec.bytes / t_dec / 1e9
     ver_gbps = ver.bytes / t_ver / 1e9
+    traffic = traffic_from_summary()
 
     line = {
         "metric": METRIC,
@@ -172,8 +305,10 @@ def main():
                       "bytes_per_call": ver.bytes,
                       "time_ratio_vs_M1": round(t_ver / t_dec, 4) if ok_ver and ok_dec else None},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
-                     "kernel": "gemv_q4g128<1>", "us_per_launch": round(t_dec * 1e6, 3)},
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": round(traffic) if traffic is not None else None,
+                     "kernel": KERNEL, "us_per_launch": round(t_dec * 1e6, 3),
+                     "algorithmic_bytes_per_launch": dec.bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

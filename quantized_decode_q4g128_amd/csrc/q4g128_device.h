@@ -60,6 +60,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Each lane takes the four words that lane src_lane holds in v (one LDS
+// crossbar permute per word; no LDS memory is used).
+__device__ __forceinline__ u32x4 lane_gather(const u32x4 &v, int src_lane)
+{
+    const int a = src_lane * 4;
+    u32x4 r;
+    r.x = (uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)v.x);
+    r.y = (uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)v.y);
+    r.z = (uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)v.z);
+    r.w = (uint32_t)__builtin_amdgcn_ds_bpermute(a, (int)v.w);
+    return r;
+}
+
 // bf16 held in the low / high half of a 32-bit register -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }

@@ -17,16 +17,20 @@
 // an M-row call is bit-identical to the one-row call (bw24 article,
 // exactness paragraph).
 //
-// Work layout: a workgroup of 4 waves owns 64*TPW output columns and one
-// contiguous range of 128-groups (the K split).  Each wave owns TPW tiles of
-// 16 columns; lane (i = l%16, h = l/16) streams column i's 16-byte code piece
-// h of every group (words 16g+4h .. 16g+4h+3), so the four lanes of a column
-// read its 64 contiguous bytes per group.  The workgroup stages x for up to
-// CG groups at a time in LDS (all of its K range unless M*K is large),
-// reordered into the pair order of the codes; lanes whose A row is >= M read
-// a real row, and their D rows are never stored.  The main loop has no
-// branches that depend on data: groups past the end of a range are processed
-// with scale and minimum forced to zero.
+// Work layout: a workgroup of WAVES waves (2 for M <= 2, 4 above) owns
+// 16*WAVES*TPW output columns and one contiguous range of 128-groups (the K
+// split).  Each wave owns TPW tiles of 16 columns.  Lane (i = l%16, h = l/16)
+// feeds column i's 16-byte code piece h of every group (words
+// 16g+4h .. 16g+4h+3) to the MFMA; the loads themselves are issued with each
+// run of four neighbouring lanes reading one column's 64 contiguous bytes, and
+// a lane permute moves every piece to its MFMA lane.  The workgroup stages x
+// for up to CG groups at a time in LDS (all of its K range unless M*K is
+// large), reordered into the pair order of the codes; lanes whose A row is
+// >= M read a real row, and their D rows are never stored.  The main loop
+// has no branches that depend on data: groups past the end of a range are
+// processed with scale and minimum forced to zero.  Which wave or workgroup
+// owns a column never changes the instructions that compute it, so the
+// choice of WAVES by M keeps rows bit-identical across M.
 #include "q4g128_device.h"
 #include "q4g128_launch.h"
 #include "q4g128_stage.h"
@@ -48,6 +52,7 @@ namespace q4g128 {
 template <int TPW, bool VSM, int RING>
 struct Tile {
     int i, h, M, K, G, gs, ge;
+    int src;                                      // lane holding this lane's code piece
     size_t K8;
     __amdgpu_buffer_rsrc_t rw, rs, rm;
     uint32_t vw[TPW], vs[TPW];
@@ -81,9 +86,11 @@ struct Tile {
     // and, with VSM, the first block's scales and minimums.
     __device__ __forceinline__ void prime(int cs, int ce)
     {
+        // Scales and minimums first: the loop's first wait for them then
+        // leaves the code loads in flight.
+        if (VSM) fetch_sm(0, cs);
 #pragma unroll
         for (int q = 0; q < RING; ++q) fetch(q, min(cs + q, ce - 1));
-        if (VSM) fetch_sm(0, cs);
     }
 
     // Group g (LDS group index lg) from ring slot q; `set`/`j` locate its
@@ -96,20 +103,43 @@ struct Tile {
 #pragma unroll
         for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u32x4 *>(gp + aoff[t]);
         const f32x4 xsum = *reinterpret_cast<const f32x4 *>(xrow + lg * 8);
-        // Consume the ring slot before its refill is issued, so the refill
-        // lands in the same registers.
-        u32x4 bq[TPW][4];
+        // Take the ring slot out (the gather reads it), then refill it at once
+        // so RING groups stay in flight; the scheduling barrier keeps the
+        // compiler from sinking the refill below the arithmetic.
+        u32x4 c[TPW];
         float s[TPW], m[TPW];
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
-            bq[u][0] = unpack_biased(cb[q][u].x, uc);
-            bq[u][1] = unpack_biased(cb[q][u].y, uc);
-            bq[u][2] = unpack_biased(cb[q][u].z, uc);
-            bq[u][3] = unpack_biased(cb[q][u].w, uc);
-            s[u] = VSM ? bf16_at(sm[set][0][u], j) : bf16_lo(sb[q][u]);
-            m[u] = VSM ? bf16_at(sm[set][1][u], j) : bf16_lo(mb[q][u]);
+#if Q4G128_QUAD
+            c[u] = lane_gather(cb[q][u], src);
+#else
+            c[u] = cb[q][u];
+#endif
+            if (!VSM) {                           // scale and minimum ride in the same slot
+                s[u] = bf16_lo(sb[q][u]);
+                m[u] = bf16_lo(mb[q][u]);
+            }
         }
         fetch(q, min(g + RING, ce - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 bq[TPW][4];
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            bq[u][0] = unpack_biased(c[u].x, uc);
+            bq[u][1] = unpack_biased(c[u].y, uc);
+            bq[u][2] = unpack_biased(c[u].z, uc);
+            bq[u][3] = unpack_biased(c[u].w, uc);
+#if Q4G128_QUAD
+            if (VSM && j == 0) {                  // first group of a block: gather its scales/minimums
+                sm[set][0][u] = lane_gather(sm[set][0][u], src);
+                sm[set][1][u] = lane_gather(sm[set][1][u], src);
+            }
+#endif
+            if (VSM) {
+                s[u] = bf16_at(sm[set][0][u], j);
+                m[u] = bf16_at(sm[set][1][u], j);
+            }
+        }
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -141,23 +171,37 @@ struct Tile {
         int aoff[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) aoff[t] = swz(4 * h + t, arow) * 8;
-        const int last8 = cs + (ng - 1) / 8 * 8;         // first group of the last block
-        for (int g16 = cs; g16 < ce; g16 += 16) {
-            if (VSM) fetch_sm(1, min(g16 + 8, last8));
+        const int nblk = (ng + 7) / 8;                   // blocks of 8 groups (last may be short, !VSM)
+        const int last8 = cs + (nblk - 1) * 8;           // first group of the last block
+        // Two blocks per iteration with no branch inside, so the scale/minimum
+        // prefetch of the second block stays ahead of the first block's work.
+        // Ring slot of group g: (g - cs) % RING, a constant per unrolled step.
+        int b = 0;
+        for (; b + 2 <= nblk; b += 2) {
+            const int g0 = cs + 8 * b;
+            if (VSM) fetch_sm(1, g0 + 8);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int g = g16 + j;
+                const int g = g0 + j;
+                group(rbase, aoff, xrow, ce, j % RING, g, g - cs, 0, j, uc);
+            }
+            if (VSM) fetch_sm(0, min(g0 + 16, last8));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int g = g0 + 8 + j;
+                const int lg = VSM ? g - cs : min(g - cs, ng - 1);
+                group(rbase, aoff, xrow, ce, (8 + j) % RING, g, lg, 1, j, uc);
+            }
+        }
+        if (b < nblk) {                                  // odd block count: the last block
+            const int g0 = cs + 8 * b;                   // 16 * (b / 2) groups past cs: slot j % RING
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int g = g0 + j;
                 const int lg = VSM ? g - cs : min(g - cs, ng - 1);
                 group(rbase, aoff, xrow, ce, j % RING, g, lg, 0, j, uc);
-            }
-            if (g16 + 8 < ce) {                  // wave-uniform: odd block count
-                if (VSM) fetch_sm(0, min(g16 + 16, last8));
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int g = g16 + 8 + j;
-                    const int lg = VSM ? g - cs : min(g - cs, ng - 1);
-                    group(rbase, aoff, xrow, ce, (8 + j) % RING, g, lg, 1, j, uc);
-                }
             }
         }
     }
@@ -169,10 +213,10 @@ struct Tile {
 // accumulate the same groups in the same order with the same instructions, so
 // they give identical bits.
 // A chunk of 16 groups of x for 8 rows must fit the staging registers.
-static_assert(kStageMax * kThreads >= 8 * 16 * 16, "x staging cannot hold one 16-group chunk at M = 8");
+static_assert(kStageMax * 64 * kWavesSmall >= 8 * 16 * 16, "x staging cannot hold one 16-group chunk at M = 8");
 
-template <int TPW, bool CHUNKED, bool VSM, int RING>
-__global__ __launch_bounds__(kThreads) void gemv_q4g128(
+template <int TPW, bool CHUNKED, bool VSM, int RING, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
     const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ mn, int N,
     float *__restrict__ out, int S, int CG)
@@ -198,31 +242,49 @@ __global__ __launch_bounds__(kThreads) void gemv_q4g128(
     T.ge = min(((split + 1) * nb / S) * kRing, G);
 
     // Columns: waves past N alias the last column and store nothing.
-    const int col0 = (blockIdx.x * kWaves + wave) * TPW * 16;
+    const int col0 = (blockIdx.x * WAVES + wave) * TPW * 16;
     const int cbase = __builtin_amdgcn_readfirstlane(min(col0, N - 1));
     const int ncols = __builtin_amdgcn_readfirstlane(max(1, min(16 * TPW, N - cbase)));
     T.rw = make_rsrc(W + (size_t)cbase * T.K8, (uint32_t)((size_t)ncols * T.K8 * 4));
     T.rs = make_rsrc(scale + (size_t)cbase * G, (uint32_t)(ncols * G * 2));
     T.rm = make_rsrc(mn + (size_t)cbase * G, (uint32_t)(ncols * G * 2));
+    // Code loads: lane 4a + b reads piece b of column a, so each run of four
+    // consecutive lanes covers 64 contiguous bytes (the memory pipeline only
+    // merges neighbouring lanes); the MFMA wants piece h of column i in lane
+    // i + 16h, which fetches it from lane 4i + h when it is consumed.
+#if Q4G128_QUAD
+    const int la = lane >> 2, lb = lane & 3;
+    T.src = 4 * T.i + T.h;
+#else
+    const int la = T.i, lb = T.h;
+    T.src = lane;
+#endif
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-        const int c = min(16 * u + T.i, ncols - 1);   // ragged tail: read a real column
-        T.vw[u] = (uint32_t)((size_t)c * T.K8 * 4 + 16 * T.h);
+        const int cl = min(16 * u + la, ncols - 1);   // ragged tail: read a real column
+        T.vw[u] = (uint32_t)((size_t)cl * T.K8 * 4 + 16 * lb);
+        // 16-byte scale/minimum loads (VSM) follow the same quad order and are
+        // gathered once per block; 2-byte ones are read by the lane using them.
+        const int c = min(16 * u + ((VSM && Q4G128_QUAD) ? la : T.i), ncols - 1);
         T.vs[u] = (uint32_t)(c * G * 2);
 #pragma unroll
         for (int r = 0; r < 4; ++r) T.acc[u][r] = 0.0f;
     }
 
     if (!CHUNKED) {
+        XStage<64 * WAVES, kStageMax> xst;
+        xst.load(x, M, K, T.gs, T.ge);
         T.prime(T.gs, T.ge);
-        stage_x<kThreads, kStageMax>(xs, x, M, K, T.gs, T.ge);
+        xst.store(xs, M, T.gs, T.ge);
         lds_barrier();
         T.run(xs, T.gs, T.ge);
     } else {
         for (int cs = T.gs; cs < T.ge; cs += CG) {
             const int ce = min(cs + CG, T.ge);
+            XStage<64 * WAVES, kStageMax> xst;
+            xst.load(x, M, K, cs, ce);
             T.prime(cs, ce);
-            stage_x<kThreads, kStageMax>(xs, x, M, K, cs, ce);
+            xst.store(xs, M, cs, ce);
             lds_barrier();
             T.run(xs, cs, ce);
             __builtin_amdgcn_s_waitcnt(0);      // chunk drained: ring and LDS reads done
@@ -287,26 +349,42 @@ __global__ __launch_bounds__(256) void dequant_q4g128(const uint32_t *__restrict
 
 // ---- launchers ---------------------------------------------------------------
 
-int columns_per_block(int tpw) { return kWaves * 16 * tpw; }
+int waves_for(int M) { return M <= kSmallM ? kWavesSmall : kWavesLarge; }
+
+int columns_per_block(int tpw, int M) { return waves_for(M) * 16 * tpw; }
 
 int chunk_groups(int M)
 {
-    int cg = kStageMax * kThreads / 16 / M;         // pieces per thread <= kStageMax
+    int cg = kStageMax * 64 * waves_for(M) / 16 / M;   // pieces per thread <= kStageMax
     cg = cg / 16 * 16;
     return cg < 16 ? 16 : cg;
 }
 
-template <int TPW, bool CHUNKED, bool VSM>
+template <int TPW, bool CHUNKED, bool VSM, int WAVES>
 static void launch_one(const GemvArgs &a, dim3 grid, int cg, hipStream_t stream)
 {
     const size_t lds = (size_t)a.M * (size_t)cg * 128 * 2 + (size_t)cg * 8 * 4;
-    hipLaunchKernelGGL((gemv_q4g128<TPW, CHUNKED, VSM, kRingDepth>), grid, dim3(kThreads, 1, 1), lds, stream,
-                       a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.S, cg);
+    hipLaunchKernelGGL((gemv_q4g128<TPW, CHUNKED, VSM, kRingDepth, WAVES>), grid, dim3(64 * WAVES, 1, 1), lds,
+                       stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.S, cg);
+}
+
+template <int WAVES>
+static void launch_waves(const GemvArgs &a, dim3 grid, bool chunked, bool vsm, int cg, int span, hipStream_t stream)
+{
+    if (vsm) {
+        if (chunked) launch_one<1, true, true, WAVES>(a, grid, cg, stream);
+        else launch_one<1, false, true, WAVES>(a, grid, span, stream);
+    } else {
+        if (chunked) launch_one<1, true, false, WAVES>(a, grid, cg, stream);
+        else launch_one<1, false, false, WAVES>(a, grid, span, stream);
+    }
 }
 
 hipError_t launch_gemv(const GemvArgs &a, int tpw, hipStream_t stream)
 {
-    const int cpb = columns_per_block(tpw);
+    if (tpw != 1) return hipErrorInvalidValue;
+    const int waves = waves_for(a.M);
+    const int cpb = columns_per_block(tpw, a.M);
     // The widest split spans ceil(nb/S) blocks of 8 groups.
     const int nb = (a.K / 128 + kRing - 1) / kRing;
     const int span = (nb + a.S - 1) / a.S * kRing;
@@ -316,14 +394,8 @@ hipError_t launch_gemv(const GemvArgs &a, int tpw, hipStream_t stream)
     const bool vsm = (a.K / 128) % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scale) & 15) == 0 &&
                      (reinterpret_cast<uintptr_t>(a.mn) & 15) == 0;
     dim3 grid((unsigned)((a.N + cpb - 1) / cpb), (unsigned)a.S, 1);
-    if (tpw != 1) return hipErrorInvalidValue;
-    if (vsm) {
-        if (chunked) launch_one<1, true, true>(a, grid, cg, stream);
-        else launch_one<1, false, true>(a, grid, span, stream);
-    } else {
-        if (chunked) launch_one<1, true, false>(a, grid, cg, stream);
-        else launch_one<1, false, false>(a, grid, span, stream);
-    }
+    if (waves == kWavesSmall) launch_waves<kWavesSmall>(a, grid, chunked, vsm, cg, span, stream);
+    else launch_waves<kWavesLarge>(a, grid, chunked, vsm, cg, span, stream);
     return hipGetLastError();
 }
 

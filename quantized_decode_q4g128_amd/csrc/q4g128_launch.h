@@ -8,21 +8,34 @@
 
 namespace q4g128 {
 
-#ifndef Q4G128_WAVES
-#define Q4G128_WAVES 4
+#ifndef Q4G128_WAVES_SMALL
+#define Q4G128_WAVES_SMALL 2
+#endif
+#ifndef Q4G128_WAVES_LARGE
+#define Q4G128_WAVES_LARGE 4
+#endif
+#ifndef Q4G128_SMALL_M
+#define Q4G128_SMALL_M 2
 #endif
 #ifndef Q4G128_RING
-#define Q4G128_RING 8
+#define Q4G128_RING 4
+#endif
+#ifndef Q4G128_QUAD
+#define Q4G128_QUAD 1
 #endif
 #ifndef Q4G128_STAGE
-#define Q4G128_STAGE 10
+#define Q4G128_STAGE 16
 #endif
 
 constexpr int kMaxM = 8;
-constexpr int kWaves = Q4G128_WAVES;       // waves per workgroup (share one LDS copy of x)
-constexpr int kThreads = 64 * kWaves;
+// Waves per workgroup (they share one LDS copy of x): few for small M, where
+// x is small and finer workgroups spread more evenly over the CUs; more for
+// large M, whose x would not fit in LDS once per small workgroup.
+constexpr int kWavesSmall = Q4G128_WAVES_SMALL;
+constexpr int kWavesLarge = Q4G128_WAVES_LARGE;
+constexpr int kSmallM = Q4G128_SMALL_M;
 constexpr int kRing = 8;                   // K splits align to blocks of 8 groups (1024 k)
-constexpr int kRingDepth = Q4G128_RING;    // groups of codes in flight per wave (8 or 16)
+constexpr int kRingDepth = Q4G128_RING;    // groups of codes in flight per wave (4, 8 or 16)
 constexpr int kStageMax = Q4G128_STAGE;    // 16-byte x pieces staged per thread per chunk
 
 struct GemvArgs {
@@ -65,8 +78,9 @@ size_t streamk_lds_bytes(const SkShape &p, int M);
 hipError_t launch_gemv_streamk(const GemvArgs &a, const SkShape &p, float *parts, uint32_t *cnt,
                                hipStream_t stream);
 
-// Output columns one workgroup covers for a given tiles-per-wave setting.
-int columns_per_block(int tpw);
+// Waves per workgroup and output columns per workgroup for M rows.
+int waves_for(int M);
+int columns_per_block(int tpw, int M);
 
 hipError_t launch_gemv(const GemvArgs &a, int tpw, hipStream_t stream);
 hipError_t launch_splitk_sum(const float *P, int S, size_t MN, float *y, hipStream_t stream);

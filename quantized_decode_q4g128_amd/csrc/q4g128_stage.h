@@ -44,44 +44,65 @@ __device__ __forceinline__ float row16_sum(float v)
 // p / pr, block p % pr, pr = 16 * (ce - cs); the 16 pieces of one (row,
 // group) sit in one 16-lane row of a wave, whose lanes add their pieces'
 // sums by a fixed tree.  NT threads take at most SMAX pieces each.
+//
+// load() issues the global reads; store() waits for them and writes LDS.
+// Loads issued between the two (the first code loads) stay in flight: the
+// wait only covers memory operations older than them.
+template <int NT, int SMAX>
+struct XStage {
+    u32x4 st[SMAX];
+    int pieces, pr;
+
+    __device__ __forceinline__ void load(const uint16_t *__restrict__ x, int M, int K, int cs, int ce)
+    {
+        const int tid = threadIdx.x;
+        pr = (ce - cs) * 16;
+        pieces = M * pr;
+#pragma unroll
+        for (int j = 0; j < SMAX; ++j) {
+            if (NT * j < pieces) {            // workgroup-uniform
+                const int p = min(tid + NT * j, pieces - 1);
+                const int row = p / pr, blk = p - row * pr;
+                st[j] = *reinterpret_cast<const u32x4 *>(x + (size_t)row * K + (size_t)cs * 128 + blk * 8);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(uint16_t *xs, int M, int cs, int ce)
+    {
+        typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+        const int tid = threadIdx.x;
+        const int ng = ce - cs;
+        float *Xs = reinterpret_cast<float *>(xs + M * ng * 128);
+        const bf16x2 ones = __builtin_bit_cast(bf16x2, kOnePair);
+#pragma unroll
+        for (int j = 0; j < SMAX; ++j) {
+            if (NT * j < pieces) {
+                const int pu = tid + NT * j;
+                const int p = min(pu, pieces - 1);
+                const int row = p / pr, blk = p - row * pr;
+                *reinterpret_cast<u32x4 *>(&xs[(row * pr + swz(blk, row)) * 8]) = pair_order(st[j]);
+                // Each element goes through a scalar before the bit cast: this
+                // compiler bit-casts a vector element expression as element 0.
+                const uint32_t w0 = st[j].x, w1 = st[j].y, w2 = st[j].z, w3 = st[j].w;
+                float part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, 0.0f, false);
+                part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, part, false);
+                part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, part, false);
+                part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, part, false);
+                const float tot = row16_sum(part);
+                if ((tid & 15) == 15 && pu < pieces) Xs[(blk >> 4) * 8 + row] = tot;
+            }
+        }
+    }
+};
+
 template <int NT, int SMAX>
 __device__ __forceinline__ void stage_x(uint16_t *xs, const uint16_t *__restrict__ x, int M, int K, int cs,
                                         int ce)
 {
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-    const int tid = threadIdx.x;
-    const int ng = ce - cs;
-    const int pr = ng * 16;
-    const int pieces = M * pr;
-    float *Xs = reinterpret_cast<float *>(xs + M * ng * 128);
-    u32x4 st[SMAX];
-#pragma unroll
-    for (int j = 0; j < SMAX; ++j) {
-        if (NT * j < pieces) {            // workgroup-uniform
-            const int p = min(tid + NT * j, pieces - 1);
-            const int row = p / pr, blk = p - row * pr;
-            st[j] = *reinterpret_cast<const u32x4 *>(x + (size_t)row * K + (size_t)cs * 128 + blk * 8);
-        }
-    }
-    const bf16x2 ones = __builtin_bit_cast(bf16x2, kOnePair);
-#pragma unroll
-    for (int j = 0; j < SMAX; ++j) {
-        if (NT * j < pieces) {
-            const int pu = tid + NT * j;
-            const int p = min(pu, pieces - 1);
-            const int row = p / pr, blk = p - row * pr;
-            *reinterpret_cast<u32x4 *>(&xs[(row * pr + swz(blk, row)) * 8]) = pair_order(st[j]);
-            // Each element goes through a scalar before the bit cast: this
-            // compiler bit-casts a vector element expression as element 0.
-            const uint32_t w0 = st[j].x, w1 = st[j].y, w2 = st[j].z, w3 = st[j].w;
-            float part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, 0.0f, false);
-            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, part, false);
-            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, part, false);
-            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, part, false);
-            const float tot = row16_sum(part);
-            if ((tid & 15) == 15 && pu < pieces) Xs[(blk >> 4) * 8 + row] = tot;
-        }
-    }
+    XStage<NT, SMAX> xst;
+    xst.load(x, M, K, cs, ce);
+    xst.store(xs, M, cs, ce);
 }
 
 }  // namespace q4g128
