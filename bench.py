@@ -9,7 +9,9 @@ timed region.  Each step reads a different copy of the weights, cycling over
 >= 1.2 GB of copies, so no step is served from the 256 MB last-level cache.
 
 Reported: algorithmic bytes per step / time as GB/s (value), the same at M=7
-(speculative verify) and the verify/decode time ratio, the dominant kernel's
+(speculative verify) and the verify/decode time ratio, the down projection
+(split-K) and the full synthetic decode-step stream (257 launches, 12.7 GB)
+as extra fields, the dominant kernel's
 roofline (HIP-event kernel durations; bytes from the format: K*N/2 codes +
 4*N*K/128 scale/min + 2*M*K x + 4*M*N y), and the fp64 CPU oracle's rate on
 the host as a baseline.  A result that fails parity against the oracle is not
@@ -63,6 +65,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="bounded CPU time budget for the oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-stream", action="store_true", help="skip the 12.7 GB decode-step stream")
     p.add_argument("--pmc-workload", action="store_true",
                    help="run the counter workload (a known-size copy, then decode launches) and exit")
     p.add_argument("--pmc-summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
@@ -119,6 +122,106 @@ class Rotation:
         t1.record(stream)
         torch.cuda.synchronize()
         return t0.elapsed_time(t1)
+
+
+class RawCalls:
+    """Launches through the C ABI with prepared pointers (no per-call Python
+    checks), so that streams of many launches are not limited by the host."""
+
+    def __init__(self, torch, q):
+        self.torch, self.q, self.L = torch, q, q.lib()
+        self.keep = []
+
+    def prepare(self, case, copies, splits=None):
+        """Device copies of the case's weights; returns a list of launch closures,
+        one per copy."""
+        torch, q, L = self.torch, self.q, self.L
+        dev = torch.device("cuda:0")
+        wt = case.weights
+        W = torch.from_numpy(wt.W.view(np.int32)).to(dev)
+        s = torch.from_numpy(wt.scale.view(np.int16)).to(dev)
+        m = torch.from_numpy(wt.mn.view(np.int16)).to(dev)
+        x = torch.from_numpy(case.x.view(np.int16)).to(dev)
+        y = torch.empty((case.M, case.N), dtype=torch.float32, device=dev)
+        if splits is None:
+            splits = q.q4g128_splitk_default_splits(case.K, case.N)
+        ws_bytes = q.q4g128_splitk_workspace_bytes(case.M, case.N, splits) if splits > 1 else 0
+        ws = torch.empty(max(ws_bytes, 4) // 4, dtype=torch.float32, device=dev)
+        sets = [(W, s, m)] + [(W.clone(), s.clone(), m.clone()) for _ in range(copies - 1)]
+        self.keep += [x, y, ws, sets]
+        M, K, N = case.M, case.K, case.N
+        calls = []
+        for Wi, si, mi in sets:
+            if splits > 1:
+                args = (x.data_ptr(), M, K, Wi.data_ptr(), si.data_ptr(), mi.data_ptr(), N, y.data_ptr(),
+                        splits, ws.data_ptr(), ws_bytes)
+                calls.append(lambda st, a=args: L.q4g128_gemm_splitk(*a, st))
+            else:
+                args = (x.data_ptr(), M, K, Wi.data_ptr(), si.data_ptr(), mi.data_ptr(), N, y.data_ptr())
+                calls.append(lambda st, a=args: L.q4g128_gemm(*a, st))
+        return calls, splits
+
+
+def timed_calls(torch, seq, reps, warmup):
+    """Milliseconds for `reps` passes over the launch sequence `seq`, bracketed
+    by HIP events on the launching stream."""
+    stream = torch.cuda.current_stream()
+    st = stream.cuda_stream
+    for _ in range(warmup):
+        for c in seq:
+            if c(st) != 0:
+                raise RuntimeError("launch failed")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(reps):
+        for c in seq:
+            c(st)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1)
+
+
+def measure_down(torch, q, steps, warmup):
+    """Decode down projection (M=1, K=17408, N=5120; split-K with the default
+    split count, partial sums reduced in split order)."""
+    case = synth.make_case("down")
+    B = synth.algorithmic_bytes(case.M, case.K, case.N)
+    rc = RawCalls(torch, q)
+    calls, splits = rc.prepare(case, max(2, math.ceil(ROTATE_BYTES / B)))
+    ms = timed_calls(torch, calls, max(1, steps // len(calls)), 1)
+    n = max(1, steps // len(calls)) * len(calls)
+    t = ms * 1e-3 / n
+    return {"us_per_call": round(t * 1e6, 3), "GBps": round(B / t / 1e9, 1), "splits": splits,
+            "bytes_per_call": B, "kernels_per_call": 2 if splits > 1 else 1}
+
+
+def measure_stream(torch, q, reps=5, warmup=2):
+    """The full synthetic decode-step weight stream at M=1: 64 layers of four
+    projections (5120->12288, 6144->5120, 5120->34816, 17408->5120), then the
+    5120->131072 output projection, 257 launches back to back on one stream,
+    every layer reading its own copy of the weights."""
+    rc = RawCalls(torch, q)
+    per_shape = []
+    B_layer = 0
+    for K, N, seed in synth.stream_shapes()[:-1]:
+        case = synth.make_random(1, K, N, seed)
+        calls, _ = rc.prepare(case, synth.STREAM_LAYERS)
+        per_shape.append(calls)
+        B_layer += synth.algorithmic_bytes(1, K, N)
+    K, N, seed = synth.stream_shapes()[-1]
+    head, _ = rc.prepare(synth.make_random(1, K, N, seed), 1)
+    seq = [per_shape[j][layer] for layer in range(synth.STREAM_LAYERS) for j in range(len(per_shape))] + head
+    B = synth.STREAM_LAYERS * B_layer + synth.algorithmic_bytes(1, K, N)
+    ms = timed_calls(torch, seq, reps, warmup)
+    t = ms * 1e-3 / reps
+    out = {"launches_per_step": len(seq), "bytes_per_step": B, "ms_per_step": round(t * 1e3, 4),
+           "GBps_wall": round(B / t / 1e9, 1), "steps_per_s": round(1.0 / t, 2),
+           "note": "wall time of back-to-back launches, gaps between kernels included"}
+    del rc
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(case, budget_s):
@@ -282,6 +385,8 @@ def main():
     achieved = dec.bytes / t_dec / 1e9
     ver_gbps = ver.bytes / t_ver / 1e9
     traffic = traffic_from_summary()
+    down = measure_down(torch, q, args.steps, args.warmup)
+    stream_step = measure_stream(torch, q) if not args.no_stream else None
 
     line = {
         "metric": METRIC,
@@ -304,6 +409,8 @@ def main():
         "verify_M7": {"GBps": round(ver_gbps, 1) if ok_ver else None, "us_per_call": round(t_ver * 1e6, 3),
                       "bytes_per_call": ver.bytes,
                       "time_ratio_vs_M1": round(t_ver / t_dec, 4) if ok_ver and ok_dec else None},
+        "down_M1": down,
+        "decode_step_stream": stream_step,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": round(traffic) if traffic is not None else None,

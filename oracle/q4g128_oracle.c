@@ -9,17 +9,17 @@
  *
  * What it computes follows the Token Rush README (github.com/zyhector/
  * token-rush):
- *   - the weight format paragraph ("group-wise asymmetric int4"): every 128
- *     consecutive weights share one bf16 scale and one bf16 minimum, 4.25
+ *   - its weight format paragraph: asymmetric int4 by groups, every 128
+ *     consecutive weights sharing one bf16 scale and one bf16 minimum, 4.25
  *     bits per weight;
- *   - the constraints list ("4.25 bits per weight ... 128-group scale and
- *     minimum");
- *   - the bandwidth paragraph: a decode step is a product of the activation
- *     with every streamed weight matrix;
- *   - the steps table, rows 13-14 and 28: an M-row verify step is the same
- *     product with M activation rows.
- * and the bw24 article (wpnews.pro), exactness paragraph: verify and decode
- * must agree exactly, and summation order is part of the contract.
+ *   - its list of constraints, which gives the same format;
+ *   - its bandwidth paragraph: a decode step multiplies the activation by
+ *     every streamed weight matrix;
+ *   - its steps table, rows 13-14 and 28: a verify step is the same product
+ *     with M activation rows.
+ * and the bw24 article (wpnews.pro), exactness paragraph: verify must agree
+ * with plain decode exactly, and the order of summation is part of that
+ * contract.
  *
  * Readings taken where the pages leave a step open (all listed in the design
  * notes): a weight is w = q*s + m (q = 0 maps to the minimum); the 128-weight
