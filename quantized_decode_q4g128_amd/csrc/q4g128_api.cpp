@@ -47,6 +47,49 @@ int plan_tiles_per_wave(int /*K*/, int /*N*/) { return 1; }
 // enough loads in flight per CU to cover HBM latency.
 constexpr long kTargetWaves = 2048;
 
+// Compute units of the calling thread's current device, or -1.  Cached per
+// device (every thread that fills an entry writes the same value).
+int device_cus()
+{
+    static int cache[64];
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    if (dev >= 0 && dev < 64) cache[dev] = ncu;
+    return ncu;
+}
+
+// Balanced plan: workgroups per K split for gemv_q4g128_bal (at most one per
+// CU), or 0 when the shape needs the per-tile kernel (K not a multiple of
+// 1024, unaligned scale/min, x or LDS too large, huge y).  Which workgroup
+// owns a column never changes its arithmetic, so the plan may depend on M
+// and on the CU count.
+int plan_bal(int M, int K, int N, int S, const void *scale, const void *min)
+{
+    using namespace q4g128;
+    // One K split only: with several, fewer workgroups per split leave some
+    // CUs a larger share than the per-tile kernel does.
+    if (S != 1) return 0;
+    if (K % 1024 != 0 || !aligned(scale, 16) || !aligned(min, 16)) return 0;
+    if ((long)M * N * 4 >= (1L << 31)) return 0;
+    const int nb = K / 1024;
+    if (S < 1 || S > nb) return 0;
+    const int nbmax = (nb + S - 1) / S;
+    if (16 * nbmax > 64 * kBalSmRounds) return 0;
+    const int ngmax = 8 * nbmax;
+    if ((long)M * ngmax * 16 > (long)kBalThreads * kBalStage) return 0;
+    const int ncu = device_cus();
+    if (ncu < 1) return 0;
+    const int T = (N + 15) / 16;
+    int gx = ncu / S;
+    if (gx < 1) gx = 1;
+    if (gx > T) gx = T;
+    const int nwmax = (T + gx - 1) / gx < kBalWaves ? (T + gx - 1) / gx : kBalWaves;
+    if (bal_lds_bytes(M, ngmax, nwmax, nbmax | 1) > kBalMaxLds) return 0;
+    return gx;
+}
+
 q4g128_status run_gemv(const void *x, int M, int K, const uint32_t *W, const void *scale,
                        const void *min, int N, float *out, int S, hipStream_t stream)
 {
@@ -60,7 +103,9 @@ q4g128_status run_gemv(const void *x, int M, int K, const uint32_t *W, const voi
     a.N = N;
     a.out = out;
     a.S = S;
-    hipError_t e = q4g128::launch_gemv(a, plan_tiles_per_wave(K, N), stream);
+    const int gx = plan_bal(M, K, N, S, scale, min);
+    hipError_t e = gx > 0 ? q4g128::launch_gemv_bal(a, gx, stream)
+                          : q4g128::launch_gemv(a, plan_tiles_per_wave(K, N), stream);
     if (e != hipSuccess) {
         set_error("gemv launch", e);
         return Q4G128_EHIP;
@@ -75,15 +120,6 @@ size_t streamk_ws_bytes(int N)
 {
     const size_t tiles = ((size_t)N + 15) / 16;
     return (kSkPartBytes + tiles * 4 + 255) / 256 * 256;
-}
-
-// Compute units of the calling thread's current device, or -1.
-int device_cus()
-{
-    int dev = 0, ncu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return -1;
-    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-    return ncu;
 }
 
 }  // namespace

@@ -31,6 +31,8 @@
 // processed with scale and minimum forced to zero.  Which wave or workgroup
 // owns a column never changes the instructions that compute it, so the
 // choice of WAVES by M keeps rows bit-identical across M.
+#include <algorithm>
+
 #include "q4g128_device.h"
 #include "q4g128_launch.h"
 #include "q4g128_stage.h"
@@ -49,10 +51,14 @@ namespace q4g128 {
 // minimum ride in the code ring, and a range may end inside a block: the
 // groups past its end are processed with scale and minimum zero (exact zeros)
 // on a copy of its last group's x.
-template <int TPW, bool VSM, int RING>
+template <int TPW, bool VSM, int RING, bool SML = false>
 struct Tile {
     int i, h, M, K, G, gs, ge;
     int src;                                      // lane holding this lane's code piece
+    // SML: scales and minimums of the wave's tile sit in LDS ([scale, min]
+    // [column][block of 8 groups from smg0], nbl blocks per column row).
+    const uint16_t *sml;
+    int nbl, smg0;
     size_t K8;
     __amdgpu_buffer_rsrc_t rw, rs, rm;
     uint32_t vw[TPW], vs[TPW];
@@ -75,6 +81,12 @@ struct Tile {
 
     __device__ __forceinline__ void fetch_sm(int set, int g8)
     {
+        if (SML) {
+            const int b = (g8 - smg0) >> 3;
+            sm[set][0][0] = *reinterpret_cast<const u32x4 *>(sml + (i * nbl + b) * 8);
+            sm[set][1][0] = *reinterpret_cast<const u32x4 *>(sml + ((16 + i) * nbl + b) * 8);
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             sm[set][0][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, vs[u], 2 * g8, 0);
@@ -88,7 +100,7 @@ struct Tile {
     {
         // Scales and minimums first: the loop's first wait for them then
         // leaves the code loads in flight.
-        if (VSM) fetch_sm(0, cs);
+        if (VSM && !SML) fetch_sm(0, cs);        // SML: read from LDS once it is written
 #pragma unroll
         for (int q = 0; q < RING; ++q) fetch(q, min(cs + q, ce - 1));
     }
@@ -130,7 +142,7 @@ struct Tile {
             bq[u][2] = unpack_biased(c[u].z, uc);
             bq[u][3] = unpack_biased(c[u].w, uc);
 #if Q4G128_QUAD
-            if (VSM && j == 0) {                  // first group of a block: gather its scales/minimums
+            if (VSM && !SML && j == 0) {          // first group of a block: gather its scales/minimums
                 sm[set][0][u] = lane_gather(sm[set][0][u], src);
                 sm[set][1][u] = lane_gather(sm[set][1][u], src);
             }
@@ -306,6 +318,159 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
     }
 }
 
+// ---- balanced kernel: one workgroup per compute unit ---------------------------
+//
+// A stream only reaches full rate when every compute unit moves about the
+// same number of bytes (Token Rush README, bandwidth paragraph: decode is
+// bound by streaming the weights).  Here the grid is gx workgroups per K split,
+// at most one per CU (the LDS request is sized so two never share a CU), and
+// workgroup c of a split owns the tiles [c*T/gx, (c+1)*T/gx): 8 or 9 tiles
+// each for the 2176 tiles of N = 34816 on 256 CUs.  Each of up to 16 waves
+// takes one tile at a time.  x is staged once per workgroup; each wave copies
+// its tile's scales and minimums into its own LDS area with 16-byte loads of
+// consecutive pieces, so the main loop streams nothing but codes.  The
+// per-column instructions are those of gemv_q4g128, so results are the same
+// bits.  Needs K/128 a multiple of 8 and 16-byte aligned scale/min.
+
+template <int RING>
+struct BalTile : Tile<1, true, RING, true> {
+    typedef Tile<1, true, RING, true> Base;
+    int la, lb, nblk, ncols;
+
+    // Descriptors and lane offsets for tile t.
+    __device__ __forceinline__ void setup(const uint32_t *W, const uint16_t *scale, const uint16_t *mn, int N,
+                                          int t)
+    {
+        const int cbase = __builtin_amdgcn_readfirstlane(min(16 * t, N - 1));
+        ncols = __builtin_amdgcn_readfirstlane(max(1, min(16, N - cbase)));
+        this->rw = make_rsrc(W + (size_t)cbase * this->K8, (uint32_t)((size_t)ncols * this->K8 * 4));
+        this->rs = make_rsrc(scale + (size_t)cbase * this->G, (uint32_t)(ncols * this->G * 2));
+        this->rm = make_rsrc(mn + (size_t)cbase * this->G, (uint32_t)(ncols * this->G * 2));
+        this->vw[0] = (uint32_t)((size_t)min(la, ncols - 1) * this->K8 * 4 + 16 * lb);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) this->acc[0][r] = 0.0f;
+    }
+
+    // Scale/minimum pieces (16 bytes = 8 groups of one column) of the tile's
+    // K range: piece q = column q / nblk, block q % nblk; lane takes q = lane + 64r.
+    __device__ __forceinline__ void sm_load(u32x4 (&sr)[kBalSmRounds], u32x4 (&mr)[kBalSmRounds], int lane) const
+    {
+        const int pieces = 16 * nblk;
+#pragma unroll
+        for (int r = 0; r < kBalSmRounds; ++r) {
+            if (64 * r < pieces) {                         // wave-uniform
+                const int q = min(lane + 64 * r, pieces - 1);
+                const int col = min(q / nblk, ncols - 1), b = q - (q / nblk) * nblk;
+                const uint32_t off = (uint32_t)(col * this->G + this->gs + 8 * b) * 2;
+                sr[r] = __builtin_amdgcn_raw_buffer_load_b128(this->rs, off, 0, 0);
+                mr[r] = __builtin_amdgcn_raw_buffer_load_b128(this->rm, off, 0, 0);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void sm_store(const u32x4 (&sr)[kBalSmRounds], const u32x4 (&mr)[kBalSmRounds],
+                                             int lane) const
+    {
+        const int pieces = 16 * nblk;
+        uint16_t *dst = const_cast<uint16_t *>(this->sml);
+#pragma unroll
+        for (int r = 0; r < kBalSmRounds; ++r) {
+            const int q = lane + 64 * r;
+            if (64 * r < pieces && q < pieces) {
+                const int col = q / nblk, b = q - col * nblk;
+                *reinterpret_cast<u32x4 *>(dst + (col * this->nbl + b) * 8) = sr[r];
+                *reinterpret_cast<u32x4 *>(dst + ((16 + col) * this->nbl + b) * 8) = mr[r];
+            }
+        }
+    }
+
+    // y rows < M of tile t through a descriptor over [M][N] fp32 (M*N*4 < 2^31):
+    // 32-bit offsets, no 64-bit addresses to keep live across tiles.
+    __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t ry, int N, int t) const
+    {
+        const int n = 16 * t + this->i;
+        if (n < N) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * this->h + r;
+                if (row < this->M)
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, this->acc[0][r]), ry,
+                                                          (uint32_t)(row * N + n) * 4, 0, 0);
+            }
+        }
+    }
+};
+
+template <int RING>
+__global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
+    const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,
+    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ mn, int N,
+    float *__restrict__ out, int S, int nblp)
+{
+    extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = K >> 7;
+    const int nb = G >> 3;
+    const int split = blockIdx.y;
+    const int gs = (split * nb / S) * 8;
+    const int ge = ((split + 1) * nb / S) * 8;
+    const int ng = ge - gs;
+    const int T = (N + 15) >> 4;
+    const int gx = gridDim.x;
+    const int t0 = (int)((long)blockIdx.x * T / gx);
+    const int t1 = (int)((long)(blockIdx.x + 1) * T / gx);
+    const bool active = wave < t1 - t0;                   // wave-uniform
+
+    BalTile<RING> B;
+    B.i = lane & 15;
+    B.h = lane >> 4;
+    B.la = lane >> 2;
+    B.lb = lane & 3;
+    B.src = 4 * B.i + B.h;
+    B.M = M;
+    B.K = K;
+    B.G = G;
+    B.K8 = (size_t)(K >> 3);
+    B.gs = gs;
+    B.ge = ge;
+    B.nblk = ng >> 3;
+    B.nbl = nblp;
+    B.smg0 = gs;
+    // LDS: x [M][ng*128] bf16, row sums [ng][8] fp32, then one scale/minimum
+    // area of 2*16*nblp*8 bf16 per wave.
+    B.sml = xs + M * ng * 128 + ng * 16 + wave * (2 * 16 * nblp * 8);
+
+    XStage<kBalThreads, kBalStage> xst;
+    xst.load(x, M, K, gs, ge);                            // first: waiting for x leaves the codes in flight
+    u32x4 sr[kBalSmRounds], mr[kBalSmRounds];
+    int t = t0 + wave;
+    if (active) {
+        B.setup(W, scale, mn, N, t);
+        B.sm_load(sr, mr, lane);
+        B.prime(gs, ge);
+    }
+    xst.store(xs, M, gs, ge);
+    if (active) B.sm_store(sr, mr, lane);
+    lds_barrier();
+    if (!active) return;
+
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(out + (size_t)split * (size_t)M * (size_t)N, (uint32_t)(M * N * 4));
+    for (;;) {
+        B.fetch_sm(0, gs);
+        B.run(xs, gs, ge);
+        B.store(ry, N, t);
+        t += kBalWaves;
+        if (t >= t1) break;
+        B.setup(W, scale, mn, N, t);                      // next tile of this wave (N > 16 tiles per CU)
+        B.sm_load(sr, mr, lane);
+        B.prime(gs, ge);
+        B.sm_store(sr, mr, lane);                         // own area; LDS ops of a wave stay in order
+    }
+}
+
 // y[e] = P[0][e] + P[1][e] + ... + P[S-1][e], in ascending s.
 __global__ __launch_bounds__(256) void splitk_sum(const float *__restrict__ P, int S, size_t MN,
                                                   float *__restrict__ y)
@@ -396,6 +561,29 @@ hipError_t launch_gemv(const GemvArgs &a, int tpw, hipStream_t stream)
     dim3 grid((unsigned)((a.N + cpb - 1) / cpb), (unsigned)a.S, 1);
     if (waves == kWavesSmall) launch_waves<kWavesSmall>(a, grid, chunked, vsm, cg, span, stream);
     else launch_waves<kWavesLarge>(a, grid, chunked, vsm, cg, span, stream);
+    return hipGetLastError();
+}
+
+size_t bal_lds_bytes(int M, int ngmax, int nwmax, int nblp)
+{
+    return (size_t)M * ngmax * 256 + (size_t)ngmax * 32 + (size_t)nwmax * 2 * 16 * nblp * 16;
+}
+
+hipError_t launch_gemv_bal(const GemvArgs &a, int gx, hipStream_t stream)
+{
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        160 * 1024);
+    if (attr != hipSuccess) return attr;
+    const int nb = a.K / 1024;
+    const int nbmax = (nb + a.S - 1) / a.S;
+    const int T = (a.N + 15) / 16;
+    const int nwmax = std::min(kBalWaves, (T + gx - 1) / gx);
+    const int nblp = nbmax | 1;
+    size_t lds = bal_lds_bytes(a.M, nbmax * 8, nwmax, nblp);
+    if (lds < kBalOwnCu) lds = kBalOwnCu;
+    hipLaunchKernelGGL((gemv_q4g128_bal<kBalRing>), dim3((unsigned)gx, (unsigned)a.S, 1), dim3(kBalThreads, 1, 1),
+                       lds, stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.S, nblp);
     return hipGetLastError();
 }
 

@@ -53,6 +53,29 @@ struct GemvArgs {
 // x chunk (in 128-groups, a multiple of kRing) staged in LDS for M rows.
 int chunk_groups(int M);
 
+// ---- balanced kernel: one workgroup per CU --------------------------------------
+#ifndef Q4G128_BAL_WAVES
+#define Q4G128_BAL_WAVES 16
+#endif
+#ifndef Q4G128_BAL_RING
+#define Q4G128_BAL_RING 4
+#endif
+constexpr int kBalWaves = Q4G128_BAL_WAVES; // waves per workgroup; each takes one tile at a time
+constexpr int kBalRing = Q4G128_BAL_RING;   // groups of codes in flight per wave
+constexpr int kBalThreads = 64 * kBalWaves;
+constexpr int kBalStage = 5;                // x pieces per thread: M * ng * 16 <= 5120
+constexpr int kBalSmRounds = 2;             // scale/min pieces per lane: 16 * nblk <= 128, nblk <= 8
+constexpr size_t kBalOwnCu = 80 * 1024 + 1024;   // LDS request that keeps two workgroups off one CU
+constexpr size_t kBalMaxLds = 160 * 1024;
+
+// LDS of one workgroup: x for M rows over ngmax groups, their row sums, and
+// nwmax waves' scale/minimum areas (nblp blocks per column row).
+size_t bal_lds_bytes(int M, int ngmax, int nwmax, int nblp);
+// y (S == 1) or partials [S][M][N] (S > 1) with gx workgroups per split.
+// Requires K % 1024 == 0, 16-byte aligned scale/min, and the plan checks of
+// plan_bal (x and LDS fit).
+hipError_t launch_gemv_bal(const GemvArgs &a, int gx, hipStream_t stream);
+
 // ---- work-balanced (stream-K) kernel ----------------------------------------
 constexpr int kSkWaves = 8;                 // waves per workgroup, one workgroup per CU
 constexpr int kSkThreads = 64 * kSkWaves;
