@@ -81,11 +81,12 @@ int plan_bal(int M, int K, int N, int S, const void *scale, const void *min)
     if ((long)M * ngmax * 16 > (long)kBalThreads * kBalStage) return 0;
     const int ncu = device_cus();
     if (ncu < 1) return 0;
-    const int T = (N + 15) / 16;
+    const int N8 = (N + 7) / 8;                // columns are shared out in units of 8
     int gx = ncu / S;
     if (gx < 1) gx = 1;
-    if (gx > T) gx = T;
-    const int nwmax = (T + gx - 1) / gx < kBalWaves ? (T + gx - 1) / gx : kBalWaves;
+    if (gx > N8) gx = N8;
+    const int tiles = ((N8 + gx - 1) / gx * 8 + 15) / 16;
+    const int nwmax = tiles < kBalWaves ? tiles : kBalWaves;
     if (bal_lds_bytes(M, ngmax, nwmax, nbmax | 1) > kBalMaxLds) return 0;
     return gx;
 }

@@ -332,21 +332,23 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
 // per-column instructions are those of gemv_q4g128, so results are the same
 // bits.  Needs K/128 a multiple of 8 and 16-byte aligned scale/min.
 
-template <int RING>
-struct BalTile : Tile<1, true, RING, true> {
-    typedef Tile<1, true, RING, true> Base;
+template <int RING, bool SML>
+struct BalTile : Tile<1, true, RING, SML> {
+    typedef Tile<1, true, RING, SML> Base;
     int la, lb, nblk, ncols;
 
-    // Descriptors and lane offsets for tile t.
-    __device__ __forceinline__ void setup(const uint32_t *W, const uint16_t *scale, const uint16_t *mn, int N,
-                                          int t)
+    // Descriptors and lane offsets for the tile of `width` (1..16) columns
+    // from cbase; lanes past the width read its last column.
+    __device__ __forceinline__ void setup(const uint32_t *W, const uint16_t *scale, const uint16_t *mn, int cbase_,
+                                          int width)
     {
-        const int cbase = __builtin_amdgcn_readfirstlane(min(16 * t, N - 1));
-        ncols = __builtin_amdgcn_readfirstlane(max(1, min(16, N - cbase)));
+        const int cbase = __builtin_amdgcn_readfirstlane(cbase_);
+        ncols = __builtin_amdgcn_readfirstlane(width);
         this->rw = make_rsrc(W + (size_t)cbase * this->K8, (uint32_t)((size_t)ncols * this->K8 * 4));
         this->rs = make_rsrc(scale + (size_t)cbase * this->G, (uint32_t)(ncols * this->G * 2));
         this->rm = make_rsrc(mn + (size_t)cbase * this->G, (uint32_t)(ncols * this->G * 2));
         this->vw[0] = (uint32_t)((size_t)min(la, ncols - 1) * this->K8 * 4 + 16 * lb);
+        this->vs[0] = (uint32_t)(min(la, ncols - 1) * this->G * 2);   // !SML: per-block loads, quad order
 #pragma unroll
         for (int r = 0; r < 4; ++r) this->acc[0][r] = 0.0f;
     }
@@ -355,12 +357,12 @@ struct BalTile : Tile<1, true, RING, true> {
     // K range: piece q = column q / nblk, block q % nblk; lane takes q = lane + 64r.
     __device__ __forceinline__ void sm_load(u32x4 (&sr)[kBalSmRounds], u32x4 (&mr)[kBalSmRounds], int lane) const
     {
-        const int pieces = 16 * nblk;
+        const int pieces = ncols * nblk;
 #pragma unroll
         for (int r = 0; r < kBalSmRounds; ++r) {
             if (64 * r < pieces) {                         // wave-uniform
                 const int q = min(lane + 64 * r, pieces - 1);
-                const int col = min(q / nblk, ncols - 1), b = q - (q / nblk) * nblk;
+                const int col = q / nblk, b = q - col * nblk;
                 const uint32_t off = (uint32_t)(col * this->G + this->gs + 8 * b) * 2;
                 sr[r] = __builtin_amdgcn_raw_buffer_load_b128(this->rs, off, 0, 0);
                 mr[r] = __builtin_amdgcn_raw_buffer_load_b128(this->rm, off, 0, 0);
@@ -371,7 +373,7 @@ struct BalTile : Tile<1, true, RING, true> {
     __device__ __forceinline__ void sm_store(const u32x4 (&sr)[kBalSmRounds], const u32x4 (&mr)[kBalSmRounds],
                                              int lane) const
     {
-        const int pieces = 16 * nblk;
+        const int pieces = ncols * nblk;
         uint16_t *dst = const_cast<uint16_t *>(this->sml);
 #pragma unroll
         for (int r = 0; r < kBalSmRounds; ++r) {
@@ -384,12 +386,12 @@ struct BalTile : Tile<1, true, RING, true> {
         }
     }
 
-    // y rows < M of tile t through a descriptor over [M][N] fp32 (M*N*4 < 2^31):
-    // 32-bit offsets, no 64-bit addresses to keep live across tiles.
-    __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t ry, int N, int t) const
+    // y rows < M of the tile's columns through a descriptor over [M][N] fp32
+    // (M*N*4 < 2^31): 32-bit offsets, no 64-bit addresses live across tiles.
+    __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t ry, int N, int cbase) const
     {
-        const int n = 16 * t + this->i;
-        if (n < N) {
+        const int n = cbase + this->i;
+        if (this->i < ncols) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 4 * this->h + r;
@@ -401,7 +403,7 @@ struct BalTile : Tile<1, true, RING, true> {
     }
 };
 
-template <int RING>
+template <int RING, bool SML>
 __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ mn, int N,
@@ -418,13 +420,20 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     const int gs = (split * nb / S) * 8;
     const int ge = ((split + 1) * nb / S) * 8;
     const int ng = ge - gs;
-    const int T = (N + 15) >> 4;
     const int gx = gridDim.x;
-    const int t0 = (int)((long)blockIdx.x * T / gx);
-    const int t1 = (int)((long)(blockIdx.x + 1) * T / gx);
-    const bool active = wave < t1 - t0;                   // wave-uniform
+    // Workgroups are dealt to the 8 XCDs in turn (c -> XCD c % 8); numbering
+    // them XCD by XCD before cutting the column range gives every XCD the same
+    // mix of larger and smaller shares.
+    const int c = (gx % 8 == 0) ? (int)(blockIdx.x % 8) * (gx / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    // Columns [n0, n1), cut in units of 8 so every CU streams the same bytes to
+    // within 8 columns (N = 34816 on 256 CUs: 136 each, 8 tiles of 16 + 1 of 8).
+    const int N8 = (N + 7) >> 3;
+    const int n0 = (int)((long)c * N8 / gx) * 8;
+    const int n1 = min((int)((long)(c + 1) * N8 / gx) * 8, N);
+    const int nchunk = (n1 - n0 + 15) >> 4;               // tiles of up to 16 columns
+    const bool active = wave < nchunk;                    // wave-uniform
 
-    BalTile<RING> B;
+    BalTile<RING, SML> B;
     B.i = lane & 15;
     B.h = lane >> 4;
     B.la = lane >> 2;
@@ -443,31 +452,35 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     // area of 2*16*nblp*8 bf16 per wave.
     B.sml = xs + M * ng * 128 + ng * 16 + wave * (2 * 16 * nblp * 8);
 
+    // x first, and alone: every wave's code and scale/minimum loads wait until
+    // the workgroup's x is in LDS.  Issued together, its few kilobytes queue
+    // behind megabytes of weight requests from all CUs, and the barrier waits
+    // for the slowest wave's x.
     XStage<kBalThreads, kBalStage> xst;
-    xst.load(x, M, K, gs, ge);                            // first: waiting for x leaves the codes in flight
-    u32x4 sr[kBalSmRounds], mr[kBalSmRounds];
-    int t = t0 + wave;
-    if (active) {
-        B.setup(W, scale, mn, N, t);
-        B.sm_load(sr, mr, lane);
-        B.prime(gs, ge);
-    }
+    xst.load(x, M, K, gs, ge);
     xst.store(xs, M, gs, ge);
-    if (active) B.sm_store(sr, mr, lane);
     lds_barrier();
     if (!active) return;
+    u32x4 sr[kBalSmRounds], mr[kBalSmRounds];
+    int k = wave;                                         // this wave's tiles: k, k + kBalWaves, ...
+    int cb = n0 + 16 * k;
+    B.setup(W, scale, mn, cb, min(16, n1 - cb));
+    if (SML) B.sm_load(sr, mr, lane);                     // before the codes: waiting for them leaves the codes in flight
+    B.prime(gs, ge);
+    if (SML) B.sm_store(sr, mr, lane);                    // the wave's own LDS area
 
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(out + (size_t)split * (size_t)M * (size_t)N, (uint32_t)(M * N * 4));
     for (;;) {
-        B.fetch_sm(0, gs);
+        if (SML) B.fetch_sm(0, gs);                       // (!SML: the prime loaded it)
         B.run(xs, gs, ge);
-        B.store(ry, N, t);
-        t += kBalWaves;
-        if (t >= t1) break;
-        B.setup(W, scale, mn, N, t);                      // next tile of this wave (N > 16 tiles per CU)
-        B.sm_load(sr, mr, lane);
+        B.store(ry, N, cb);
+        k += kBalWaves;
+        if (k >= nchunk) break;
+        cb = n0 + 16 * k;
+        B.setup(W, scale, mn, cb, min(16, n1 - cb));      // next tile of this wave (> 16 tiles per CU)
+        if (SML) B.sm_load(sr, mr, lane);
         B.prime(gs, ge);
-        B.sm_store(sr, mr, lane);                         // own area; LDS ops of a wave stay in order
+        if (SML) B.sm_store(sr, mr, lane);                // own area; LDS ops of a wave stay in order
     }
 }
 
@@ -572,17 +585,17 @@ size_t bal_lds_bytes(int M, int ngmax, int nwmax, int nblp)
 hipError_t launch_gemv_bal(const GemvArgs &a, int gx, hipStream_t stream)
 {
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing, kBalSml>), hipFuncAttributeMaxDynamicSharedMemorySize,
         160 * 1024);
     if (attr != hipSuccess) return attr;
     const int nb = a.K / 1024;
     const int nbmax = (nb + a.S - 1) / a.S;
-    const int T = (a.N + 15) / 16;
-    const int nwmax = std::min(kBalWaves, (T + gx - 1) / gx);
+    const int N8 = (a.N + 7) / 8;
+    const int nwmax = std::min(kBalWaves, ((N8 + gx - 1) / gx * 8 + 15) / 16);
     const int nblp = nbmax | 1;
-    size_t lds = bal_lds_bytes(a.M, nbmax * 8, nwmax, nblp);
+    size_t lds = bal_lds_bytes(a.M, nbmax * 8, kBalSml ? nwmax : 0, nblp);
     if (lds < kBalOwnCu) lds = kBalOwnCu;
-    hipLaunchKernelGGL((gemv_q4g128_bal<kBalRing>), dim3((unsigned)gx, (unsigned)a.S, 1), dim3(kBalThreads, 1, 1),
+    hipLaunchKernelGGL((gemv_q4g128_bal<kBalRing, kBalSml>), dim3((unsigned)gx, (unsigned)a.S, 1), dim3(kBalThreads, 1, 1),
                        lds, stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.S, nblp);
     return hipGetLastError();
 }

@@ -55,15 +55,19 @@ int chunk_groups(int M);
 
 // ---- balanced kernel: one workgroup per CU --------------------------------------
 #ifndef Q4G128_BAL_WAVES
-#define Q4G128_BAL_WAVES 16
+#define Q4G128_BAL_WAVES 12
 #endif
 #ifndef Q4G128_BAL_RING
 #define Q4G128_BAL_RING 4
 #endif
 constexpr int kBalWaves = Q4G128_BAL_WAVES; // waves per workgroup; each takes one tile at a time
 constexpr int kBalRing = Q4G128_BAL_RING;   // groups of codes in flight per wave
+#ifndef Q4G128_BAL_SML
+#define Q4G128_BAL_SML 1
+#endif
+constexpr bool kBalSml = Q4G128_BAL_SML;    // scales/minimums staged in LDS per tile (else loaded per block)
 constexpr int kBalThreads = 64 * kBalWaves;
-constexpr int kBalStage = 5;                // x pieces per thread: M * ng * 16 <= 5120
+constexpr int kBalStage = 7;                // x pieces per thread: M * ng * 16 <= 5376 (M = 8 at K = 5120)
 constexpr int kBalSmRounds = 2;             // scale/min pieces per lane: 16 * nblk <= 128, nblk <= 8
 constexpr size_t kBalOwnCu = 80 * 1024 + 1024;   // LDS request that keeps two workgroups off one CU
 constexpr size_t kBalMaxLds = 160 * 1024;
