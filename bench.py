@@ -66,10 +66,18 @@ def parse():
                    help="bounded CPU time budget for the oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-stream", action="store_true", help="skip the 12.7 GB decode-step stream")
+    p.add_argument("--no-verify", action="store_true", help="skip the M=7 verify step (profiling decode alone)")
+    p.add_argument("--no-down", action="store_true", help="skip the down projection")
     p.add_argument("--pmc-workload", action="store_true",
                    help="run the counter workload (a known-size copy, then decode launches) and exit")
     p.add_argument("--pmc-summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                    help="turn two rocprofv3 counter runs of --pmc-workload into a traffic summary")
+    p.add_argument("--trace-summarize", nargs=2, metavar=("TRACE_DIR", "OUT"),
+                   help="per-launch-shape durations from a rocprofv3 --kernel-trace run of bench.py")
+    p.add_argument("--trace-command", default="rocprofv3 --kernel-trace --stats -d OUT -o run --output-format csv "
+                   "-- python3 REPO/bench.py --steps 208 --warmup 26 --no-cpu-baseline --no-stream --no-verify "
+                   "--no-down",
+                   help="the profiling command, recorded in the trace summary")
     return p.parse_args()
 
 
@@ -82,46 +90,6 @@ def kernel_source_hash() -> str:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
-
-
-class Rotation:
-    """R device copies of one weight set plus one x; call i uses copy i % R."""
-
-    def __init__(self, case, torch, q, copies=None):
-        self.torch, self.q = torch, q
-        wt = case.weights
-        self.M, self.K, self.N = case.M, case.K, case.N
-        self.bytes = synth.algorithmic_bytes(self.M, self.K, self.N)
-        self.R = copies or max(2, math.ceil(ROTATE_BYTES / self.bytes))
-        dev = torch.device("cuda:0")
-        W = torch.from_numpy(wt.W.view(np.int32)).to(dev)
-        s = torch.from_numpy(wt.scale.view(np.int16)).to(dev)
-        m = torch.from_numpy(wt.mn.view(np.int16)).to(dev)
-        self.sets = [(W, s, m)] + [(W.clone(), s.clone(), m.clone()) for _ in range(self.R - 1)]
-        self.x = torch.from_numpy(case.x.view(np.int16)).to(dev)
-        self.y = torch.empty((self.M, self.N), dtype=torch.float32, device=dev)
-
-    def call(self, i, stream):
-        W, s, m = self.sets[i % self.R]
-        self.q.q4g128_gemm(self.x, W, s, m, y=self.y, stream=stream)
-
-    def timed(self, steps, warmup):
-        """Milliseconds for `steps` back-to-back calls, bracketed by HIP events
-        recorded on the stream the kernels run on (events around every single
-        launch would add their own overhead to each call)."""
-        torch = self.torch
-        stream = torch.cuda.current_stream()
-        for i in range(warmup):
-            self.call(i, stream)
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0.record(stream)
-        for i in range(steps):
-            self.call(warmup + i, stream)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1)
 
 
 class RawCalls:
@@ -149,6 +117,7 @@ class RawCalls:
         ws = torch.empty(max(ws_bytes, 4) // 4, dtype=torch.float32, device=dev)
         sets = [(W, s, m)] + [(W.clone(), s.clone(), m.clone()) for _ in range(copies - 1)]
         self.keep += [x, y, ws, sets]
+        self.ys = getattr(self, "ys", [])
         M, K, N = case.M, case.K, case.N
         calls = []
         for Wi, si, mi in sets:
@@ -159,7 +128,12 @@ class RawCalls:
             else:
                 args = (x.data_ptr(), M, K, Wi.data_ptr(), si.data_ptr(), mi.data_ptr(), N, y.data_ptr())
                 calls.append(lambda st, a=args: L.q4g128_gemm(*a, st))
+        self.ys.append((calls, y))
         return calls, splits
+
+    def y_of(self, calls):
+        """The output tensor the launch list writes."""
+        return next(y for c, y in self.ys if c is calls)
 
 
 def timed_calls(torch, seq, reps, warmup):
@@ -255,10 +229,13 @@ def pmc_workload():
     torch.cuda.synchronize()
     torch.mul(src, 1, out=dst)              # an elementwise kernel: reads and writes COPY_BYTES
     torch.cuda.synchronize()
-    rot = Rotation(synth.make_case("gateup"), torch, q)
-    stream = torch.cuda.current_stream()
+    case = synth.make_case("gateup")
+    raw = RawCalls(torch, q)
+    calls, _ = raw.prepare(case, max(2, math.ceil(ROTATE_BYTES / synth.algorithmic_bytes(case.M, case.K, case.N))),
+                           splits=1)
+    st = torch.cuda.current_stream().cuda_stream
     for i in range(PMC_LAUNCHES):
-        rot.call(i, stream)
+        calls[i % len(calls)](st)
     torch.cuda.synchronize()
     print(f"pmc workload: copy {COPY_BYTES} B, {PMC_LAUNCHES} launches of {KERNEL}", flush=True)
 
@@ -317,6 +294,33 @@ def pmc_summarize(fetch_dir, write_dir, out):
     print(open(out).read())
 
 
+def trace_summarize(trace_dir, out, command):
+    """Per-launch-shape kernel durations from a rocprofv3 --kernel-trace run
+    (launches of one kernel with different LDS sizes or grids are listed
+    apart: the M=1 and M=7 launches of the product differ in LDS)."""
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    rows = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            key = (name, int(r["LDS_Block_Size"]), int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]),
+                   int(r["Workgroup_Size_X"]))
+            rows.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    with open(out, "w") as f:
+        f.write("# rocprofv3 kernel trace of bench.py on one MI355X (gfx950), per launch shape\n")
+        f.write("# command (rocprofv3 started from /tmp with TMPDIR=/tmp; REPO = repository root):\n")
+        f.write(f"#   {command}\n")
+        f.write(f"#   python3 bench.py --trace-summarize OUT {os.path.relpath(out, ROOT)}\n")
+        f.write("# kernel | grid x,y | workgroup | launches | avg us | median us | min us | max us\n")
+        for key in sorted(rows, key=lambda k: -sum(rows[k])):
+            v = np.array(rows[key])
+            f.write(f"{key[0]} | {key[2]},{key[3]} | {key[4]} | {len(v)} | {v.mean():.3f} | {np.median(v):.3f} | "
+                    f"{v.min():.3f} | {v.max():.3f}\n")
+    print(open(out).read())
+
+
 def traffic_from_summary():
     """HBM bytes per launch from the committed counter summary, or None when
     it is missing or was taken on other kernel sources."""
@@ -341,6 +345,9 @@ def main():
     if args.pmc_summarize:
         pmc_summarize(*args.pmc_summarize)
         return
+    if args.trace_summarize:
+        trace_summarize(*args.trace_summarize, args.trace_command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the product runs on one GPU's "
               f"share of the weights and has no multi-GPU path", file=sys.stderr)
@@ -356,15 +363,23 @@ def main():
 
     dec_case = synth.make_case("gateup")
     ver_case = synth.make_case("verify", 7)
-    dec = Rotation(dec_case, torch, q)
-    ver = Rotation(ver_case, torch, q)
+    B_dec = synth.algorithmic_bytes(dec_case.M, dec_case.K, dec_case.N)
+    B_ver = synth.algorithmic_bytes(ver_case.M, ver_case.K, ver_case.N)
+    # Launches through the C ABI with prepared pointers: per-call Python
+    # checks would otherwise leave the GPU waiting on the host between
+    # 20-microsecond kernels.
+    raw = RawCalls(torch, q)
+    dec_calls, _ = raw.prepare(dec_case, max(2, math.ceil(ROTATE_BYTES / B_dec)), splits=1)
+    ver_calls = None if args.no_verify else raw.prepare(ver_case, max(2, math.ceil(ROTATE_BYTES / B_ver)),
+                                                         splits=1)[0]
 
     # Parity gate on the exact launches that get timed (first rotation set).
-    stream = torch.cuda.current_stream()
-    dec.call(0, stream)
-    y_dec = dec.y.cpu().numpy()
-    ver.call(0, stream)
-    y_ver = ver.y.cpu().numpy()
+    st = torch.cuda.current_stream().cuda_stream
+    if dec_calls[0](st) != 0 or (ver_calls and ver_calls[0](st) != 0):
+        raise SystemExit("launch failed: " + q.q4g128_last_error())
+    torch.cuda.synchronize()
+    y_dec = raw.y_of(dec_calls).cpu().numpy()
+    y_ver = raw.y_of(ver_calls).cpu().numpy() if ver_calls else None
 
     cpu = None
     import oracle
@@ -373,19 +388,34 @@ def main():
     else:
         yr, ar = oracle.load().gemm(dec_case.x, dec_case.weights.W, dec_case.weights.scale, dec_case.weights.mn)
     ok_dec = bool(oracle.within_tolerance(y_dec, yr, ar).all())
-    yv, av = oracle.load().gemm(ver_case.x, ver_case.weights.W, ver_case.weights.scale, ver_case.weights.mn)
-    ok_ver = bool(oracle.within_tolerance(y_ver, yv, av).all())
+    ok_ver = None
+    if ver_calls:
+        yv, av = oracle.load().gemm(ver_case.x, ver_case.weights.W, ver_case.weights.scale, ver_case.weights.mn)
+        ok_ver = bool(oracle.within_tolerance(y_ver, yv, av).all())
 
-    wall_d = dec.timed(args.steps, args.warmup)
-    wall_v = ver.timed(args.steps, args.warmup)
-    ms_step = wall_d / args.steps
-    t_dec = wall_d * 1e-3 / args.steps            # s per launch (back to back)
-    t_ver = wall_v * 1e-3 / args.steps
-    gbps = dec.bytes * args.steps / (wall_d * 1e-3) / 1e9
-    achieved = dec.bytes / t_dec / 1e9
-    ver_gbps = ver.bytes / t_ver / 1e9
+    # Bring the GPU out of its idle clocks (the oracle just kept it idle for
+    # seconds) before anything is timed: ~0.5 s of decode launches.
+    t_end = time.perf_counter() + 0.5
+    while time.perf_counter() < t_end:
+        for c in dec_calls:
+            c(st)
+        torch.cuda.synchronize()
+    n_dec = max(1, args.steps // len(dec_calls)) * len(dec_calls)      # whole passes over the copies
+    wall_d = timed_calls(torch, dec_calls, n_dec // len(dec_calls), max(1, args.warmup // len(dec_calls)))
+    ms_step = wall_d / n_dec
+    t_dec = wall_d * 1e-3 / n_dec                 # s per launch (back to back)
+    gbps = B_dec * n_dec / (wall_d * 1e-3) / 1e9
+    achieved = B_dec / t_dec / 1e9
+    verify = None
+    if ver_calls:
+        n_ver = max(1, args.steps // len(ver_calls)) * len(ver_calls)
+        wall_v = timed_calls(torch, ver_calls, n_ver // len(ver_calls), max(1, args.warmup // len(ver_calls)))
+        t_ver = wall_v * 1e-3 / n_ver
+        verify = {"GBps": round(B_ver / t_ver / 1e9, 1) if ok_ver else None, "us_per_call": round(t_ver * 1e6, 3),
+                  "bytes_per_call": B_ver,
+                  "time_ratio_vs_M1": round(t_ver / t_dec, 4) if ok_ver and ok_dec else None}
     traffic = traffic_from_summary()
-    down = measure_down(torch, q, args.steps, args.warmup)
+    down = None if args.no_down else measure_down(torch, q, args.steps, args.warmup)
     stream_step = measure_stream(torch, q) if not args.no_stream else None
 
     line = {
@@ -393,7 +423,7 @@ def main():
         "value": round(gbps, 1) if ok_dec else None,
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": n_dec,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
@@ -402,20 +432,19 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "decode gate/up projection, int4-g128, M=1 K=5120 N=34816",
-                   "M": 1, "K": 5120, "N": 34816, "bytes_per_step": dec.bytes,
-                   "weight_copies_rotated": dec.R, "accumulate": "fp32"},
+                   "M": 1, "K": 5120, "N": 34816, "bytes_per_step": B_dec,
+                   "weight_copies_rotated": len(dec_calls), "accumulate": "fp32"},
         "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2) if ok_dec else None,
-        "parity": {"decode_M1": "pass" if ok_dec else "FAIL", "verify_M7": "pass" if ok_ver else "FAIL"},
-        "verify_M7": {"GBps": round(ver_gbps, 1) if ok_ver else None, "us_per_call": round(t_ver * 1e6, 3),
-                      "bytes_per_call": ver.bytes,
-                      "time_ratio_vs_M1": round(t_ver / t_dec, 4) if ok_ver and ok_dec else None},
+        "parity": {"decode_M1": "pass" if ok_dec else "FAIL",
+                   "verify_M7": None if ok_ver is None else ("pass" if ok_ver else "FAIL")},
+        "verify_M7": verify,
         "down_M1": down,
         "decode_step_stream": stream_step,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": round(traffic) if traffic is not None else None,
                      "kernel": KERNEL, "us_per_launch": round(t_dec * 1e6, 3),
-                     "algorithmic_bytes_per_launch": dec.bytes},
+                     "algorithmic_bytes_per_launch": B_dec},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
