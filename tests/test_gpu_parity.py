@@ -205,3 +205,30 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert e.value.status == q.Q4G128_EWORKSPACE
     with pytest.raises(ValueError):
         q.q4g128_gemm(x[:, :128].contiguous(), W, s, m)
+
+
+# K = 6144 and 8192 run the balanced one-workgroup-per-CU kernel for small M
+# and the per-tile kernel once M*K/128*16 exceeds what the balanced kernel
+# stages; both must give the same bits, row by row.
+@pytest.mark.parametrize("K,N", [(6144, 1000), (8192, 777)])
+def test_rows_bit_identical_across_kernel_choice(K, N):
+    case = synth.make_random(8, K, N, 31 + K // 1024)
+    W, s, m = dev_weights(case.weights)
+    x8 = dev_x(case.x)
+    y8 = host_f32(q.q4g128_gemm(x8, W, s, m))
+    for M in range(1, 8):
+        yM = host_f32(q.q4g128_gemm(x8[:M].contiguous(), W, s, m))
+        assert np.array_equal(bits(yM), bits(y8[:M])), M
+
+
+# Column sharing of the balanced kernel: N not a multiple of 8, fewer than 8
+# columns per CU, one tile per wave with an 8-column tail, and more tiles per
+# workgroup than waves (several tiles per wave).
+@pytest.mark.parametrize("M,N", [(1, 1001), (3, 200), (1, 7), (2, 34816), (1, 131072), (5, 50000)])
+def test_balanced_column_sharing(orc, M, N):
+    K = 1024 if N > 40000 else 2048
+    case = synth.make_random(M, K, N, 40 + M + N % 97)
+    wt = case.weights
+    y_ref, a_ref = orc.gemm(case.x, wt.W, wt.scale, wt.mn)
+    y = host_f32(q.q4g128_gemm(dev_x(case.x), *dev_weights(wt)))
+    assert_within_tolerance(y, y_ref, a_ref, f"balanced M={M} N={N}")
