@@ -7,6 +7,7 @@ not know the feature, which is harmless.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 
@@ -34,16 +35,36 @@ def compile_flags(arch: str = ARCH):
             "-I", INCLUDE, "-I", CSRC]
 
 
+def _scratch_users(msgs):
+    """Kernels that the compiler's resource report shows using scratch."""
+    users, name = [], None
+    for line in msgs:
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            users.append((name, int(m.group(1))))
+    return users
+
+
 def build_library(out: str = LIB_PATH, extra_flags=(), quiet: bool = True) -> str:
+    """Compile the library.  Fails if a kernel spills to scratch: a kernel
+    with scratch gets fewer waves in flight and streams markedly slower."""
     tmp = out + ".tmp"
-    cmd = [hipcc()] + compile_flags() + list(extra_flags) + ["-shared"] + SOURCES + ["-o", tmp]
+    cmd = ([hipcc()] + compile_flags() + list(extra_flags) + ["-Rpass-analysis=kernel-resource-usage", "-shared"]
+           + SOURCES + ["-o", tmp])
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = [l for l in (res.stdout + res.stderr).splitlines() if l.strip() and noise not in l]
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
-    if msgs and not quiet:
-        print("\n".join(msgs))
+    spills = _scratch_users(msgs)
+    if spills:
+        os.remove(tmp)
+        raise RuntimeError("kernels use scratch (register spills): " + ", ".join(f"{n} {b} B/lane" for n, b in spills))
+    if not quiet:
+        print("\n".join(l for l in msgs if "remark" not in l))
     os.replace(tmp, out)
     return out
 

@@ -60,35 +60,64 @@ int device_cus()
     return ncu;
 }
 
-// Balanced plan: workgroups per K split for gemv_q4g128_bal (at most one per
-// CU), or 0 when the shape needs the per-tile kernel (K not a multiple of
-// 1024, unaligned scale/min, x or LDS too large, huge y).  Which workgroup
-// owns a column never changes its arithmetic, so the plan may depend on M
-// and on the CU count.
-int plan_bal(int M, int K, int N, int S, const void *scale, const void *min)
+// Balanced plan for gemv_q4g128_bal: workgroups per K split (at most one per
+// CU) and K parts per tile, or gx = 0 when the shape needs the per-tile
+// kernel (K not a multiple of 1024, unaligned scale/min, several K splits,
+// x or LDS too large, huge y).
+struct BalChoice {
+    int gx;
+    int P;
+};
+
+// Tiles of 16 columns a workgroup gets when N is shared out in units of 8.
+int bal_tiles(int N, int gx)
+{
+    const int N8 = (N + 7) / 8;
+    return ((N8 + gx - 1) / gx * 8 + 15) / 16;
+}
+
+// K parts per tile: 1 when a workgroup has enough tiles for its waves, else
+// enough parts to occupy them, each part at least kBalMinPart groups long.
+// Depends on (K, N) and the CU count only.
+int bal_parts(int K, int N, int gx)
 {
     using namespace q4g128;
+    const int tiles = bal_tiles(N, gx);
+    if (tiles >= kBalMinTiles) return 1;
+    int P = kBalWaves / tiles;
+    if (P > K / 128 / kBalMinPart) P = K / 128 / kBalMinPart;
+    return P < 1 ? 1 : P;
+}
+
+// Whether x for M rows over all of K fits the balanced kernel's staging and LDS.
+bool bal_fits(int M, int K, int N, int gx, int P)
+{
+    using namespace q4g128;
+    const int ng = K / 128;
+    if ((long)M * ng * 16 > (long)kBalThreads * kBalStage) return false;       // x staging registers
+    const int part = P > 1 ? 2 * ((ng / 2 + P - 1) / P) : ng;                    // longest part, groups
+    if (16 * ((part + 7) / 8) > 64 * kBalSmRounds) return false;                 // scale/min pieces per lane
+    return bal_plan(M, K, N, 1, gx, P).lds <= kBalMaxLds;
+}
+
+BalChoice plan_bal(int M, int K, int N, int S, const void *scale, const void *min)
+{
+    BalChoice no = {0, 1};
     // One K split only: with several, fewer workgroups per split leave some
     // CUs a larger share than the per-tile kernel does.
-    if (S != 1) return 0;
-    if (K % 1024 != 0 || !aligned(scale, 16) || !aligned(min, 16)) return 0;
-    if ((long)M * N * 4 >= (1L << 31)) return 0;
-    const int nb = K / 1024;
-    if (S < 1 || S > nb) return 0;
-    const int nbmax = (nb + S - 1) / S;
-    if (16 * nbmax > 64 * kBalSmRounds) return 0;
-    const int ngmax = 8 * nbmax;
-    if ((long)M * ngmax * 16 > (long)kBalThreads * kBalStage) return 0;
+    if (S != 1) return no;
+    if (K % 1024 != 0 || !aligned(scale, 16) || !aligned(min, 16)) return no;
+    if ((long)M * N * 4 >= (1L << 31)) return no;
     const int ncu = device_cus();
-    if (ncu < 1) return 0;
-    const int N8 = (N + 7) / 8;                // columns are shared out in units of 8
-    int gx = ncu / S;
-    if (gx < 1) gx = 1;
-    if (gx > N8) gx = N8;
-    const int tiles = ((N8 + gx - 1) / gx * 8 + 15) / 16;
-    const int nwmax = tiles < kBalWaves ? tiles : kBalWaves;
-    if (bal_lds_bytes(M, ngmax, nwmax, nbmax | 1) > kBalMaxLds) return 0;
-    return gx;
+    if (ncu < 1) return no;
+    const int N8 = (N + 7) / 8;
+    const int gx = ncu < N8 ? ncu : N8;
+    const int P = bal_parts(K, N, gx);
+    // With P > 1 the sums differ in rounding from the per-tile kernel's, so a
+    // shape takes this path for every M or for none: x is checked at M = 8.
+    if (!bal_fits(P > 1 ? Q4G128_MAX_M : M, K, N, gx, P)) return no;
+    BalChoice c = {gx, P};
+    return c;
 }
 
 q4g128_status run_gemv(const void *x, int M, int K, const uint32_t *W, const void *scale,
@@ -104,9 +133,9 @@ q4g128_status run_gemv(const void *x, int M, int K, const uint32_t *W, const voi
     a.N = N;
     a.out = out;
     a.S = S;
-    const int gx = plan_bal(M, K, N, S, scale, min);
-    hipError_t e = gx > 0 ? q4g128::launch_gemv_bal(a, gx, stream)
-                          : q4g128::launch_gemv(a, plan_tiles_per_wave(K, N), stream);
+    const BalChoice bc = plan_bal(M, K, N, S, scale, min);
+    hipError_t e = bc.gx > 0 ? q4g128::launch_gemv_bal(a, bc.gx, bc.P, stream)
+                             : q4g128::launch_gemv(a, plan_tiles_per_wave(K, N), stream);
     if (e != hipSuccess) {
         set_error("gemv launch", e);
         return Q4G128_EHIP;
@@ -151,6 +180,9 @@ size_t q4g128_splitk_workspace_bytes(int M, int N, int splits)
 int q4g128_splitk_default_splits(int K, int N)
 {
     if (K <= 0 || K % Q4G128_GROUP != 0 || N <= 0 || K > kMaxK || N > kMaxN) return 0;
+    // The balanced kernel spreads any N over every CU without K splits when
+    // x for 8 rows of all of K fits its LDS.
+    if (K % 1024 == 0 && 8L * (K / 128) * 16 <= (long)q4g128::kBalThreads * q4g128::kBalStage) return 1;
     const long nb = max_splits(K);
     const long tpw = plan_tiles_per_wave(K, N);
     const long waves = ((long)N + 16 * tpw - 1) / (16 * tpw);

@@ -51,8 +51,11 @@ namespace q4g128 {
 // minimum ride in the code ring, and a range may end inside a block: the
 // groups past its end are processed with scale and minimum zero (exact zeros)
 // on a copy of its last group's x.
-template <int TPW, bool VSM, int RING, bool SML = false>
+template <int TPW, bool VSM, int RING, bool SML = false, bool PAD = false>
 struct Tile {
+    // PAD (with VSM): the range may end inside an 8-group block; groups past
+    // its end are processed with scale and minimum zero, as without VSM.
+    static constexpr bool kClamp = !VSM || PAD;
     int i, h, M, K, G, gs, ge;
     int src;                                      // lane holding this lane's code piece
     // SML: scales and minimums of the wave's tile sit in LDS ([scale, min]
@@ -122,11 +125,7 @@ struct Tile {
         float s[TPW], m[TPW];
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
-#if Q4G128_QUAD
             c[u] = lane_gather(cb[q][u], src);
-#else
-            c[u] = cb[q][u];
-#endif
             if (!VSM) {                           // scale and minimum ride in the same slot
                 s[u] = bf16_lo(sb[q][u]);
                 m[u] = bf16_lo(mb[q][u]);
@@ -141,12 +140,10 @@ struct Tile {
             bq[u][1] = unpack_biased(c[u].y, uc);
             bq[u][2] = unpack_biased(c[u].z, uc);
             bq[u][3] = unpack_biased(c[u].w, uc);
-#if Q4G128_QUAD
             if (VSM && !SML && j == 0) {          // first group of a block: gather its scales/minimums
                 sm[set][0][u] = lane_gather(sm[set][0][u], src);
                 sm[set][1][u] = lane_gather(sm[set][1][u], src);
             }
-#endif
             if (VSM) {
                 s[u] = bf16_at(sm[set][0][u], j);
                 m[u] = bf16_at(sm[set][1][u], j);
@@ -159,7 +156,7 @@ struct Tile {
             for (int t = 0; t < 4; ++t) d = mfma_16x16x32(a[t], bq[u][t], d);
             float sc = s[u];
             float m_adj = fmaf(-kBias, s[u], m[u]);      // mn - 128*s, one rounding
-            if (!VSM && g >= ce) {                        // wave-uniform padding group
+            if (kClamp && g >= ce) {                      // wave-uniform padding group
                 sc = 0.0f;
                 m_adj = 0.0f;
             }
@@ -171,15 +168,17 @@ struct Tile {
         }
     }
 
-    // Groups [cs, ce), cs a multiple of 8 past gs; with VSM ce - cs is a
-    // multiple of 8 too.  The ring is refilled up to ce - 1.
-    __device__ __forceinline__ void run(const uint16_t *xs, int cs, int ce)
+    // Groups [cs, ce) of x staged in LDS for the groups [xg0, xg0 + xng)
+    // (row stride xng * 128).  With VSM and !PAD, ce - cs is a multiple of 8.
+    // The ring is refilled up to ce - 1.
+    __device__ __forceinline__ void run(const uint16_t *xs, int xg0, int xng, int cs, int ce)
     {
         const UnpackConsts uc = unpack_consts();
         const int ng = ce - cs;
         const int arow = min(i, M - 1);          // rows >= M read a real row; never stored
-        const uint16_t *rbase = xs + arow * ng * 128;
-        const float *xrow = reinterpret_cast<const float *>(xs + M * ng * 128) + 4 * (h & 1);
+        const uint16_t *rbase = xs + arow * xng * 128;
+        const float *xrow = reinterpret_cast<const float *>(xs + M * xng * 128) + 4 * (h & 1);
+        const int lg0 = cs - xg0;                // LDS group index of cs
         int aoff[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) aoff[t] = swz(4 * h + t, arow) * 8;
@@ -196,14 +195,14 @@ struct Tile {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int g = g0 + j;
-                group(rbase, aoff, xrow, ce, j % RING, g, g - cs, 0, j, uc);
+                group(rbase, aoff, xrow, ce, j % RING, g, lg0 + g - cs, 0, j, uc);
             }
             if (VSM) fetch_sm(0, min(g0 + 16, last8));
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int g = g0 + 8 + j;
-                const int lg = VSM ? g - cs : min(g - cs, ng - 1);
+                const int lg = lg0 + (kClamp ? min(g - cs, ng - 1) : g - cs);
                 group(rbase, aoff, xrow, ce, (8 + j) % RING, g, lg, 1, j, uc);
             }
         }
@@ -212,7 +211,7 @@ struct Tile {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int g = g0 + j;
-                const int lg = VSM ? g - cs : min(g - cs, ng - 1);
+                const int lg = lg0 + (kClamp ? min(g - cs, ng - 1) : g - cs);
                 group(rbase, aoff, xrow, ce, j % RING, g, lg, 0, j, uc);
             }
         }
@@ -264,20 +263,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
     // consecutive lanes covers 64 contiguous bytes (the memory pipeline only
     // merges neighbouring lanes); the MFMA wants piece h of column i in lane
     // i + 16h, which fetches it from lane 4i + h when it is consumed.
-#if Q4G128_QUAD
     const int la = lane >> 2, lb = lane & 3;
     T.src = 4 * T.i + T.h;
-#else
-    const int la = T.i, lb = T.h;
-    T.src = lane;
-#endif
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         const int cl = min(16 * u + la, ncols - 1);   // ragged tail: read a real column
         T.vw[u] = (uint32_t)((size_t)cl * T.K8 * 4 + 16 * lb);
         // 16-byte scale/minimum loads (VSM) follow the same quad order and are
         // gathered once per block; 2-byte ones are read by the lane using them.
-        const int c = min(16 * u + ((VSM && Q4G128_QUAD) ? la : T.i), ncols - 1);
+        const int c = min(16 * u + (VSM ? la : T.i), ncols - 1);
         T.vs[u] = (uint32_t)(c * G * 2);
 #pragma unroll
         for (int r = 0; r < 4; ++r) T.acc[u][r] = 0.0f;
@@ -289,7 +283,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
         T.prime(T.gs, T.ge);
         xst.store(xs, M, T.gs, T.ge);
         lds_barrier();
-        T.run(xs, T.gs, T.ge);
+        T.run(xs, T.gs, T.ge - T.gs, T.gs, T.ge);
     } else {
         for (int cs = T.gs; cs < T.ge; cs += CG) {
             const int ce = min(cs + CG, T.ge);
@@ -298,7 +292,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
             T.prime(cs, ce);
             xst.store(xs, M, cs, ce);
             lds_barrier();
-            T.run(xs, cs, ce);
+            T.run(xs, cs, ce - cs, cs, ce);
             __builtin_amdgcn_s_waitcnt(0);      // chunk drained: ring and LDS reads done
             lds_barrier();
         }
@@ -332,9 +326,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
 // per-column instructions are those of gemv_q4g128, so results are the same
 // bits.  Needs K/128 a multiple of 8 and 16-byte aligned scale/min.
 
-template <int RING, bool SML>
-struct BalTile : Tile<1, true, RING, SML> {
-    typedef Tile<1, true, RING, SML> Base;
+template <int RING, bool SML, bool PAD>
+struct BalTile : Tile<1, true, RING, SML, PAD> {
+    typedef Tile<1, true, RING, SML, PAD> Base;
     int la, lb, nblk, ncols;
 
     // Descriptors and lane offsets for the tile of `width` (1..16) columns
@@ -403,11 +397,15 @@ struct BalTile : Tile<1, true, RING, SML> {
     }
 };
 
-template <int RING, bool SML>
+// PARTS: a workgroup with few tiles cuts each tile's K range into P parts
+// (one wave each, boundaries at even groups); the parts' fp32 sums go to LDS
+// and, after a barrier, are added in part order, so the result depends on
+// (K, N, P) only.  P comes from (K, N) and the CU count, never from M.
+template <int RING, bool SML, bool PARTS>
 __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ mn, int N,
-    float *__restrict__ out, int S, int nblp)
+    float *__restrict__ out, int S, int nblp, int P, int nps)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
 
@@ -431,9 +429,10 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     const int n0 = (int)((long)c * N8 / gx) * 8;
     const int n1 = min((int)((long)(c + 1) * N8 / gx) * 8, N);
     const int nchunk = (n1 - n0 + 15) >> 4;               // tiles of up to 16 columns
-    const bool active = wave < nchunk;                    // wave-uniform
+    const int nunit = PARTS ? nchunk * P : nchunk;        // (tile, part) units
+    const bool active = wave < nunit;                     // wave-uniform
 
-    BalTile<RING, SML> B;
+    BalTile<RING, SML, PARTS> B;
     B.i = lane & 15;
     B.h = lane >> 4;
     B.la = lane >> 2;
@@ -443,44 +442,65 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     B.K = K;
     B.G = G;
     B.K8 = (size_t)(K >> 3);
-    B.gs = gs;
-    B.ge = ge;
-    B.nblk = ng >> 3;
     B.nbl = nblp;
-    B.smg0 = gs;
-    // LDS: x [M][ng*128] bf16, row sums [ng][8] fp32, then one scale/minimum
-    // area of 2*16*nblp*8 bf16 per wave.
-    B.sml = xs + M * ng * 128 + ng * 16 + wave * (2 * 16 * nblp * 8);
+    // LDS: x [M][ng*128] bf16, row sums [ng][8] fp32, nps part slots of 128
+    // fp32 (PARTS), then one scale/minimum area of 2*16*nblp*8 bf16 per wave.
+    float *slots = reinterpret_cast<float *>(xs + M * ng * 128 + ng * 16);
+    B.sml = xs + M * ng * 128 + ng * 16 + nps * 256 + wave * (2 * 16 * nblp * 8);
 
     // x first, and alone: every wave's code and scale/minimum loads wait until
     // the workgroup's x is in LDS.  Issued together, its few kilobytes queue
     // behind megabytes of weight requests from all CUs, and the barrier waits
     // for the slowest wave's x.
+    // A unit's column base and group range.
+    auto unit = [&](int u, int &cb, int &cs, int &ce) {
+        const int k = PARTS ? u / P : u;
+        const int p = PARTS ? u - k * P : 0;
+        cb = n0 + 16 * k;
+        cs = PARTS ? gs + 2 * ((p * (ng >> 1)) / P) : gs;
+        ce = PARTS ? gs + 2 * (((p + 1) * (ng >> 1)) / P) : ge;
+    };
     XStage<kBalThreads, kBalStage> xst;
     xst.load(x, M, K, gs, ge);
     xst.store(xs, M, gs, ge);
     lds_barrier();
-    if (!active) return;
-    u32x4 sr[kBalSmRounds], mr[kBalSmRounds];
-    int k = wave;                                         // this wave's tiles: k, k + kBalWaves, ...
-    int cb = n0 + 16 * k;
-    B.setup(W, scale, mn, cb, min(16, n1 - cb));
-    if (SML) B.sm_load(sr, mr, lane);                     // before the codes: waiting for them leaves the codes in flight
-    B.prime(gs, ge);
-    if (SML) B.sm_store(sr, mr, lane);                    // the wave's own LDS area
+    if (!PARTS && !active) return;
 
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(out + (size_t)split * (size_t)M * (size_t)N, (uint32_t)(M * N * 4));
-    for (;;) {
-        if (SML) B.fetch_sm(0, gs);                       // (!SML: the prime loaded it)
-        B.run(xs, gs, ge);
-        B.store(ry, N, cb);
-        k += kBalWaves;
-        if (k >= nchunk) break;
-        cb = n0 + 16 * k;
-        B.setup(W, scale, mn, cb, min(16, n1 - cb));      // next tile of this wave (> 16 tiles per CU)
-        if (SML) B.sm_load(sr, mr, lane);
-        B.prime(gs, ge);
-        if (SML) B.sm_store(sr, mr, lane);                // own area; LDS ops of a wave stay in order
+    if (active) {
+        u32x4 sr[kBalSmRounds], mr[kBalSmRounds];
+        for (int u = wave; u < nunit; u += kBalWaves) {   // this wave's units
+            int cb, cs, ce;
+            unit(u, cb, cs, ce);
+            B.gs = cs;
+            B.ge = ce;
+            B.nblk = (ce - cs + 7) >> 3;
+            B.smg0 = cs;
+            B.setup(W, scale, mn, cb, min(16, n1 - cb));
+            if (SML) B.sm_load(sr, mr, lane);             // before the codes: waiting for them leaves the codes in flight
+            B.prime(cs, ce);
+            if (SML) B.sm_store(sr, mr, lane);            // the wave's own LDS area; its LDS ops stay in order
+            if (SML) B.fetch_sm(0, cs);                   // (!SML: the prime loaded it)
+            B.run(xs, gs, ng, cs, ce);
+            if (!PARTS) {
+                B.store(ry, N, cb);
+            } else if (lane < 32) {                       // rows 0..7 of the part's 16 columns
+                *reinterpret_cast<f32x4 *>(slots + u * 128 + lane * 4) =
+                    f32x4{B.acc[0][0], B.acc[0][1], B.acc[0][2], B.acc[0][3]};
+            }
+        }
+    }
+    if (PARTS) {
+        lds_barrier();                                    // every wave, with or without a unit
+        for (int k = wave; k < nchunk; k += kBalWaves) {
+            const int cb = n0 + 16 * k;
+            f32x4 v = *reinterpret_cast<const f32x4 *>(slots + (k * P) * 128 + (lane & 31) * 4);
+            for (int p = 1; p < P; ++p) v += *reinterpret_cast<const f32x4 *>(slots + (k * P + p) * 128 + (lane & 31) * 4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) B.acc[0][r] = v[r];
+            B.ncols = min(16, n1 - cb);
+            if (lane < 32) B.store(ry, N, cb);
+        }
     }
 }
 
@@ -577,27 +597,41 @@ hipError_t launch_gemv(const GemvArgs &a, int tpw, hipStream_t stream)
     return hipGetLastError();
 }
 
-size_t bal_lds_bytes(int M, int ngmax, int nwmax, int nblp)
+BalPlan bal_plan(int M, int K, int N, int S, int gx, int P)
 {
-    return (size_t)M * ngmax * 256 + (size_t)ngmax * 32 + (size_t)nwmax * 2 * 16 * nblp * 16;
+    BalPlan bp;
+    const int nb = K / 1024;
+    const int ngmax = (nb + S - 1) / S * 8;
+    const int N8 = (N + 7) / 8;
+    const int tiles = ((N8 + gx - 1) / gx * 8 + 15) / 16;      // most tiles of one workgroup
+    const int units = tiles * P;
+    const int nw = units < kBalWaves ? units : kBalWaves;
+    const int pg = P > 1 ? 2 * (((ngmax / 2) + P - 1) / P) : ngmax;   // longest part, in groups
+    bp.nblp = ((pg + 7) / 8) | 1;
+    bp.nps = P > 1 ? units : 0;
+    bp.lds = (size_t)M * ngmax * 256 + (size_t)ngmax * 32 + (size_t)bp.nps * 512 +
+             (size_t)(kBalSml ? nw : 0) * 2 * 16 * bp.nblp * 16;
+    if (bp.lds < kBalOwnCu) bp.lds = kBalOwnCu;
+    return bp;
 }
 
-hipError_t launch_gemv_bal(const GemvArgs &a, int gx, hipStream_t stream)
+template <bool PARTS>
+static hipError_t launch_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)
 {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing, kBalSml>), hipFuncAttributeMaxDynamicSharedMemorySize,
-        160 * 1024);
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing, kBalSml, PARTS>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
-    const int nb = a.K / 1024;
-    const int nbmax = (nb + a.S - 1) / a.S;
-    const int N8 = (a.N + 7) / 8;
-    const int nwmax = std::min(kBalWaves, ((N8 + gx - 1) / gx * 8 + 15) / 16);
-    const int nblp = nbmax | 1;
-    size_t lds = bal_lds_bytes(a.M, nbmax * 8, kBalSml ? nwmax : 0, nblp);
-    if (lds < kBalOwnCu) lds = kBalOwnCu;
-    hipLaunchKernelGGL((gemv_q4g128_bal<kBalRing, kBalSml>), dim3((unsigned)gx, (unsigned)a.S, 1), dim3(kBalThreads, 1, 1),
-                       lds, stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.S, nblp);
+    BalPlan bp = bal_plan(a.M, a.K, a.N, a.S, gx, P);
+    hipLaunchKernelGGL((gemv_q4g128_bal<kBalRing, kBalSml, PARTS>), dim3((unsigned)gx, (unsigned)a.S, 1),
+                       dim3(kBalThreads, 1, 1), bp.lds, stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.S,
+                       bp.nblp, P, bp.nps);
     return hipGetLastError();
+}
+
+hipError_t launch_gemv_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)
+{
+    return P > 1 ? launch_bal<true>(a, gx, P, stream) : launch_bal<false>(a, gx, 1, stream);
 }
 
 hipError_t launch_splitk_sum(const float *P, int S, size_t MN, float *y, hipStream_t stream)

@@ -20,9 +20,6 @@ namespace q4g128 {
 #ifndef Q4G128_RING
 #define Q4G128_RING 4
 #endif
-#ifndef Q4G128_QUAD
-#define Q4G128_QUAD 1
-#endif
 #ifndef Q4G128_STAGE
 #define Q4G128_STAGE 16
 #endif
@@ -67,18 +64,28 @@ constexpr int kBalRing = Q4G128_BAL_RING;   // groups of codes in flight per wav
 #endif
 constexpr bool kBalSml = Q4G128_BAL_SML;    // scales/minimums staged in LDS per tile (else loaded per block)
 constexpr int kBalThreads = 64 * kBalWaves;
-constexpr int kBalStage = 7;                // x pieces per thread: M * ng * 16 <= 5376 (M = 8 at K = 5120)
+constexpr int kBalStage = 8;                // x pieces per thread: M * ng * 16 <= 6144 (M = 8 at K = 6144)
 constexpr int kBalSmRounds = 2;             // scale/min pieces per lane: 16 * nblk <= 128, nblk <= 8
 constexpr size_t kBalOwnCu = 80 * 1024 + 1024;   // LDS request that keeps two workgroups off one CU
+constexpr int kBalMinTiles = 8;             // fewer tiles per workgroup: cut each tile's K into parts
+#ifndef Q4G128_BAL_MINPART
+#define Q4G128_BAL_MINPART 24
+#endif
+constexpr int kBalMinPart = Q4G128_BAL_MINPART;   // groups per K part, at least
 constexpr size_t kBalMaxLds = 160 * 1024;
 
-// LDS of one workgroup: x for M rows over ngmax groups, their row sums, and
-// nwmax waves' scale/minimum areas (nblp blocks per column row).
-size_t bal_lds_bytes(int M, int ngmax, int nwmax, int nblp);
+// Launch geometry of the balanced kernel for M rows, S K splits, gx
+// workgroups per split and P K parts per tile (P > 1 only with S == 1).
+struct BalPlan {
+    size_t lds;     // dynamic LDS bytes (at least kBalOwnCu: one workgroup per CU)
+    int nblp;       // 8-group blocks per column row of a wave's scale/min area (odd)
+    int nps;        // part-sum slots (P > 1)
+};
+BalPlan bal_plan(int M, int K, int N, int S, int gx, int P);
 // y (S == 1) or partials [S][M][N] (S > 1) with gx workgroups per split.
 // Requires K % 1024 == 0, 16-byte aligned scale/min, and the plan checks of
 // plan_bal (x and LDS fit).
-hipError_t launch_gemv_bal(const GemvArgs &a, int gx, hipStream_t stream);
+hipError_t launch_gemv_bal(const GemvArgs &a, int gx, int P, hipStream_t stream);
 
 // ---- work-balanced (stream-K) kernel ----------------------------------------
 constexpr int kSkWaves = 8;                 // waves per workgroup, one workgroup per CU

@@ -207,10 +207,11 @@ def test_invalid_arguments_are_rejected_before_launch():
         q.q4g128_gemm(x[:, :128].contiguous(), W, s, m)
 
 
-# K = 6144 and 8192 run the balanced one-workgroup-per-CU kernel for small M
-# and the per-tile kernel once M*K/128*16 exceeds what the balanced kernel
-# stages; both must give the same bits, row by row.
-@pytest.mark.parametrize("K,N", [(6144, 1000), (8192, 777)])
+# Rows of every M must be the same bits whichever kernel serves M: at
+# K = 7168, N = 32768 the balanced kernel takes M <= 6 and the per-tile
+# kernel M = 7, 8 (x no longer fits the balanced staging); at K = 6144 and
+# 8192 with small N the choice covers every M alike (K parts / per-tile).
+@pytest.mark.parametrize("K,N", [(7168, 32768), (6144, 1000), (8192, 777)])
 def test_rows_bit_identical_across_kernel_choice(K, N):
     case = synth.make_random(8, K, N, 31 + K // 1024)
     W, s, m = dev_weights(case.weights)
