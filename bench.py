@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--no-stream", action="store_true", help="skip the 12.7 GB decode-step stream")
     p.add_argument("--no-verify", action="store_true", help="skip the M=7 verify step (profiling decode alone)")
     p.add_argument("--no-down", action="store_true", help="skip the down projection")
+    p.add_argument("--stream-only", action="store_true",
+                   help="run only the decode-step stream (for a kernel trace of it) and print its fields")
     p.add_argument("--pmc-workload", action="store_true",
                    help="run the counter workload (a known-size copy, then decode launches) and exit")
     p.add_argument("--pmc-summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
@@ -193,9 +195,40 @@ def measure_stream(torch, q, reps=5, warmup=2):
     out = {"launches_per_step": len(seq), "bytes_per_step": B, "ms_per_step": round(t * 1e3, 4),
            "GBps_wall": round(B / t / 1e9, 1), "steps_per_s": round(1.0 / t, 2),
            "note": "wall time of back-to-back launches, gaps between kernels included"}
+    out["graph"] = graph_stream(torch, rc, seq, B, reps)
     del rc
     torch.cuda.empty_cache()
     return out
+
+
+def graph_stream(torch, rc, seq, B, reps):
+    """The same step captured once in a HIP graph and replayed; each replay's
+    outputs must equal the eager run's bit for bit."""
+    torch.cuda.synchronize()
+    eager = [y.clone() for _, y in rc.ys]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = torch.cuda.current_stream().cuda_stream
+        for c in seq:
+            c(st)
+    stream = torch.cuda.current_stream()
+    same = True
+    for _ in range(2):                       # replays checked against the eager result
+        for _, y in rc.ys:
+            y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        same = same and all(torch.equal(y, e) for (_, y), e in zip(rc.ys, eager))
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    t = t0.elapsed_time(t1) * 1e-3 / reps
+    return {"ms_per_step": round(t * 1e3, 4), "GBps_wall": round(B / t / 1e9, 1),
+            "replay_equals_eager": bool(same)}
 
 
 def cpu_baseline(case, budget_s):
@@ -210,9 +243,17 @@ def cpu_baseline(case, budget_s):
         reps += 1
     dt = (time.perf_counter() - t0) / reps
     B = synth.algorithmic_bytes(case.M, case.K, case.N)
+    # One thread, on a column sample of the same input (a bounded time).
+    cols = np.arange(0, case.N, 16, dtype=np.int64)
+    t1 = time.perf_counter()
+    orc.gemm(case.x, wt.W, wt.scale, wt.mn, cols=cols, nthreads=1)
+    dt1 = (time.perf_counter() - t1) * case.N / cols.size
     return {"value": round(B / dt / 1e9, 4), "unit": "GB/s", "cores": orc.max_threads(), "kind": "oracle",
             "sample": f"{reps} full fp64 oracle calls on the same M={case.M} K={case.K} N={case.N} "
-                      f"input ({dt * 1e3:.1f} ms per call, {reps * dt:.1f} s in all)"}, (y, a)
+                      f"input ({dt * 1e3:.1f} ms per call, {reps * dt:.1f} s in all)",
+            "one_thread": {"value": round(B / dt1 / 1e9, 4), "unit": "GB/s",
+                           "sample": f"every 16th column ({cols.size} of {case.N}) on 1 thread, scaled to all N"}}, \
+        (y, a)
 
 
 # ---- HBM traffic from counters ------------------------------------------------
@@ -359,6 +400,9 @@ def main():
         sys.exit(2)
     if args.pmc_workload:
         pmc_workload()
+        return
+    if args.stream_only:
+        print(json.dumps({"decode_step_stream": measure_stream(torch, q)}))
         return
 
     dec_case = synth.make_case("gateup")
