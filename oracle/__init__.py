@@ -16,6 +16,9 @@ format paragraph and bandwidth paragraph; bw24 article, exactness paragraph):
     a[m][n]  = sum over k of |x[m][k] * w[n][k]|                       (tolerance scale)
     w32      = w rounded once to fp32 (nearest, ties to even)
 
+and the quantizer that produces the format from bf16 weights (Token Rush
+README, quantization section; the steps are in q4g128_oracle.c).
+
 bf16 tensors are passed as their uint16 bit patterns.
 """
 from __future__ import annotations
@@ -56,8 +59,9 @@ class Oracle:
         L.q4o_dequant_f32.argtypes = [vp, vp, vp, lg, lg, vp]
         L.q4o_gemm_cols.argtypes = [vp, lg, lg, vp, vp, vp, lg, vp, lg, vp, vp, ci]
         L.q4o_gemm.argtypes = [vp, lg, lg, vp, vp, vp, lg, vp, vp, ci]
+        L.q4o_quantize.argtypes = [vp, lg, lg, ci, vp, vp, vp, vp, ci]
         for f in ("q4o_codes", "q4o_dequant_f64", "q4o_dequant_f32", "q4o_gemm_cols",
-                  "q4o_gemm", "q4o_abi_version", "q4o_plant", "q4o_max_threads"):
+                  "q4o_gemm", "q4o_quantize", "q4o_abi_version", "q4o_plant", "q4o_max_threads"):
             getattr(L, f).restype = ci
         self.plant = L.q4o_plant()
 
@@ -116,6 +120,23 @@ class Oracle:
                                         _ptr(cols), cols.size, _ptr(y), _ptr(a), int(nthreads))
         self._check(rc, "gemm")
         return y, a
+
+    def quantize(self, w, ncand: int = 9, nthreads: int = 0):
+        """bf16 weights [N][K] (uint16 bit patterns) -> (W [N][K/8] uint32,
+        scale [N][K/128] uint16, min [N][K/128] uint16, err [N][K/128] fp64):
+        per-group range search: each end of the range clipped toward the middle by
+        0, 1/20, .., (ncand-1)/20 of its half, ncand * ncand candidates (1 = round
+        to nearest)."""
+        w = np.ascontiguousarray(w, dtype=np.uint16)
+        N, K = w.shape
+        G = K // 128
+        W = np.empty((N, K // 8), dtype=np.uint32)
+        S = np.empty((N, G), dtype=np.uint16)
+        Mn = np.empty((N, G), dtype=np.uint16)
+        err = np.empty((N, G), dtype=np.float64)
+        self._check(self.lib.q4o_quantize(_ptr(w), K, N, int(ncand), _ptr(W), _ptr(S), _ptr(Mn), _ptr(err),
+                                          int(nthreads)), "quantize")
+        return W, S, Mn, err
 
     def max_threads(self) -> int:
         return int(self.lib.q4o_max_threads())

@@ -16,7 +16,7 @@ SOURCE = os.path.join(_HERE, "q4g128_oracle.c")
 def build_oracle(out: str | None = None, plant: int = 0, cc: str = "gcc") -> str:
     out = out or os.path.join(_HERE, "libq4g128_oracle.so")
     tmp = out + ".tmp"
-    cmd = [cc, "-O2", "-std=c11", "-Wall", "-Wextra", "-fopenmp", "-fPIC", "-shared",
+    cmd = [cc, "-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
            f"-DORACLE_PLANT={int(plant)}", SOURCE, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)

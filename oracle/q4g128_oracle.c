@@ -41,6 +41,7 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -260,6 +261,144 @@ int q4o_gemm(const uint16_t *x, long M, long K, const uint32_t *W,
              double *a, int nthreads)
 {
     return q4o_gemm_cols(x, M, K, W, S, Mn, N, NULL, N, y, a, nthreads);
+}
+
+/* ---- quantizer ---------------------------------------------------------------
+ *
+ * Producing the format from bf16 weights (Token Rush README, quantization
+ * section): codes, scale and minimum are chosen per group of 128 weights;
+ * plain round-to-nearest is the baseline there, and a per-group search over
+ * the range, scored by squared error, clips a few outliers so that the other
+ * weights get a finer grid.  The pages give no formula; the reading taken
+ * (one candidate = round-to-nearest):
+ *
+ *   v_k        the 128 weights of the group, decoded exactly to fp64
+ *   lo, hi     min and max of v;  c = (lo + hi) * 0.5
+ *   candidates (i, j), i = 0 .. ncand-1 outer, j = 0 .. ncand-1 inner:
+ *     l = lo + (i / 20.0) * (c - lo),  h = hi - (j / 20.0) * (hi - c)
+ *                                                        (each end clipped toward c)
+ *     s = (h - l) / 15
+ *     s_b = bf16(fp32(s)), m_b = bf16(fp32(l))            (round to nearest even, twice)
+ *     q_k = 0 if s_b == 0, else min(15, max(0, rint((v_k - m_b) / s_b)))
+ *     e   = sum over k ascending of ((q_k * s_b + m_b) - v_k)^2
+ *   keep the first candidate with the smallest e.
+ *
+ * Every step is one IEEE fp64 operation in the order written (no fused
+ * multiply-add), so an fp64 implementation that follows the same steps makes
+ * the same choices bit for bit.
+ */
+
+static uint16_t bf16_of_f32(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;      /* round to nearest, ties to even */
+    return (uint16_t)u;
+}
+
+static double f64_of_bf16_bits(uint16_t b)
+{
+    double v = 0.0;
+    bf16_decode(b, &v);
+    return v;
+}
+
+/* One group: v[128] -> codes q[128], scale/minimum bits; returns the error. */
+static double quantize_group(const double *v, int ncand, uint8_t *q, uint16_t *sb, uint16_t *mb)
+{
+    double lo = v[0], hi = v[0];
+    for (int k = 1; k < 128; ++k) {
+        if (v[k] < lo) lo = v[k];
+        if (v[k] > hi) hi = v[k];
+    }
+    const double c = (lo + hi) * 0.5;
+    double best = INFINITY;
+    uint8_t qc[128];
+    for (int ij = 0; ij < ncand * ncand; ++ij) {
+        const double bl = (double)(ij / ncand) / 20.0;
+        const double bh = (double)(ij % ncand) / 20.0;
+        const double l = lo + bl * (c - lo);
+        const double h = hi - bh * (hi - c);
+        const double sv = (h - l) / 15.0;
+        const uint16_t s16 = bf16_of_f32((float)sv);
+        const uint16_t m16 = bf16_of_f32((float)l);
+        const double sd = f64_of_bf16_bits(s16);
+        const double md = f64_of_bf16_bits(m16);
+        double e = 0.0;
+        for (int k = 0; k < 128; ++k) {
+            double code = 0.0;
+            if (sd != 0.0) {
+#if ORACLE_PLANT == 9
+                code = floor((v[k] - md) / sd);               /* planted: truncation */
+#elif ORACLE_PLANT == 10
+                code = rint((v[k] - md) / (sd * 15.0 / 16.0)); /* planted: 16 steps */
+#else
+                code = rint((v[k] - md) / sd);
+#endif
+                if (code < 0.0) code = 0.0;
+#if ORACLE_PLANT == 8
+                if (code > 14.0) code = 14.0;                 /* planted: top code lost */
+#else
+                if (code > 15.0) code = 15.0;
+#endif
+            }
+            qc[k] = (uint8_t)code;
+            const double r = (code * sd + md) - v[k];
+            e = e + r * r;
+        }
+        if (e < best) {
+            best = e;
+            memcpy(q, qc, 128);
+            *sb = s16;
+            *mb = m16;
+        }
+    }
+    return best;
+}
+
+/* Quantize w [N][K] bf16 (K a multiple of 128) into W [N][K/8] (code k of
+ * column n in nibble k % 8 of word k / 8, low nibble first), scale and
+ * minimum [N][K/128] bf16; err [N][K/128] (may be NULL) gets each group's
+ * squared error.  ncand in 1..16 (ncand * ncand candidates per group). */
+int q4o_quantize(const uint16_t *w, long K, long N, int ncand, uint32_t *W, uint16_t *S,
+                 uint16_t *Mn, double *err, int nthreads)
+{
+    if (!w || !W || !S || !Mn || K <= 0 || K % 128 || N <= 0 || ncand < 1 || ncand > 16)
+        return ORC_EINVAL;
+    const long G = K / 128;
+    int status = ORC_OK;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+#else
+    (void)nthreads;
+#endif
+    for (long gi = 0; gi < N * G; ++gi) {
+        const long n = gi / G, g = gi % G;
+        double v[128];
+        uint8_t q[128];
+        uint16_t sb = 0, mb = 0;
+        int bad = 0;
+        for (int k = 0; k < 128; ++k)
+            if (bf16_decode(w[n * K + g * 128 + k], &v[k]) != ORC_OK) bad = 1;
+        if (bad) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            status = ORC_ENONFINITE;
+            continue;
+        }
+        const double e = quantize_group(v, ncand, q, &sb, &mb);
+        for (int j = 0; j < 16; ++j) {
+            uint32_t word = 0;
+            for (int i = 0; i < 8; ++i) word |= (uint32_t)q[8 * j + i] << (4 * i);
+            W[n * (K / 8) + g * 16 + j] = word;
+        }
+        S[n * G + g] = sb;
+        Mn[n * G + g] = mb;
+        if (err) err[n * G + g] = e;
+    }
+    return status;
 }
 
 /* Threads the OpenMP runtime would use by default (for reporting). */

@@ -1,6 +1,7 @@
 """Each planted mistake in the oracle (a dropped or sign-flipped minimum, the
 wrong nibble order, the wrong group size, a transposed scale read, a dropped
-term of the sum, a wrong activation row) must trip at least one pin.  The
+term of the sum, a wrong activation row; in the quantizer a lost top code,
+truncation for rounding, 16 steps for 15) must trip at least one pin.  The
 mutants are separate builds of the same C source; CPU only."""
 import os
 import shutil
@@ -9,11 +10,13 @@ import pytest
 
 import oracle
 import oracle_pins
+import quant_pins
 from oracle.build import build_oracle
 
 PLANTS = {1: "minimum dropped", 2: "minimum subtracted", 3: "high nibble first",
           4: "groups of 64", 5: "scale read transposed", 6: "last k dropped",
-          7: "every row reads x row 0"}
+          7: "every row reads x row 0", 8: "quantizer loses code 15", 9: "quantizer truncates",
+          10: "quantizer uses 16 steps"}
 
 
 @pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
@@ -23,7 +26,7 @@ def test_planted_mistake_is_caught(tmp_path, plant):
     mutant = oracle.Oracle(lib)
     assert mutant.plant == plant
     caught = []
-    for pin in oracle_pins.ALL_PINS:
+    for pin in oracle_pins.ALL_PINS + quant_pins.ALL_QPINS:
         try:
             pin(mutant)
         except (AssertionError, oracle.OracleError):
