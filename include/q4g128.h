@@ -57,6 +57,7 @@ extern "C" {
 #define Q4G128_ABI_VERSION 1
 #define Q4G128_GROUP 128
 #define Q4G128_MAX_M 8
+#define Q4G128_QUANT_MAX_CAND 16
 
 typedef enum {
     Q4G128_OK = 0,
@@ -131,6 +132,31 @@ q4g128_status q4g128_gemm_streamk(const void *x, int M, int K,
  * README, weight format paragraph. */
 q4g128_status q4g128_dequant(const uint32_t *W, const void *scale, const void *min,
                              int K, int N, float *w_out, void *stream);
+
+/* Quantize bf16 weights into the format above.  w is bf16 [N][K] (row n
+ * holds the K weights of output column n, K a multiple of 128); the outputs
+ * W [N][K/8], scale and min [N][K/128] are the layouts the product reads,
+ * and err [N][K/128] fp64 (may be NULL) receives each group's squared
+ * dequantisation error sum_k (q*s + m - w)^2.
+ *
+ * Per group the codes come from a search over clipped ranges scored by
+ * squared error (Token Rush README, quantization section: a per-group range
+ * search that clips a few outliers so the rest get a finer grid).  With
+ * lo, hi the group's extremes and c their midpoint, candidate (i, j),
+ * 0 <= i, j < ncand, taken in the order i*ncand + j, uses the range
+ * [lo + (i/20)(c - lo), hi - (j/20)(hi - c)], scale s = (range width)/15 and
+ * minimum = the range's low end, each rounded fp64 -> fp32 -> bf16 (nearest
+ * even), codes clamp(rint((w - min)/s), 0, 15) (all 0 if s rounds to 0); the
+ * first candidate with the smallest error wins.  ncand = 1 is plain
+ * round-to-nearest over the full range.  All arithmetic is fp64 with no
+ * fused multiply-adds, so the result is deterministic and bit-reproducible.
+ *
+ * Requirements beyond the common ones: 1 <= ncand <= 16; w and W 16-byte
+ * aligned, scale and min 2-byte aligned, err 8-byte aligned.  A group that
+ * holds a NaN or an infinity gets codes 0, scale 0, min 0 and err NaN (the
+ * call itself succeeds: check err when the input may hold such values). */
+q4g128_status q4g128_quantize(const void *w, int K, int N, int ncand, uint32_t *W, void *scale, void *min,
+                              double *err, void *stream);
 
 /* Static text for a status code. */
 const char *q4g128_status_string(q4g128_status s);

@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.q4g128_streamk_workspace_bytes.restype = sz
         L.q4g128_dequant.argtypes = [vp, vp, vp, ci, ci, vp, vp]
         L.q4g128_dequant.restype = ci
+        L.q4g128_quantize.argtypes = [vp, ci, ci, ci, vp, vp, vp, vp, vp]
+        L.q4g128_quantize.restype = ci
         L.q4g128_splitk_workspace_bytes.argtypes = [ci, ci, ci]
         L.q4g128_splitk_workspace_bytes.restype = sz
         L.q4g128_splitk_default_splits.argtypes = [ci, ci]
@@ -226,7 +228,38 @@ def q4g128_dequant(W, scale, min, out=None, stream=None) -> torch.Tensor:
     return out
 
 
-__all__ = ["q4g128_gemm", "q4g128_gemm_splitk", "q4g128_gemm_streamk", "q4g128_streamk_workspace",
+def q4g128_quantize(w, ncand: int = 9, W=None, scale=None, min=None, err=None, stream=None):
+    """bf16 weights w [N][K] -> (W [N][K/8] int32, scale [N][K/128] int16
+    bf16 bits, min [N][K/128] int16 bf16 bits, err [N][K/128] float64): the
+    per-group range search over ncand x ncand clipped ranges (ncand = 1 is
+    round-to-nearest).  A group holding a NaN or infinity comes back with
+    err NaN and zero codes, scale and min."""
+    w = _dev(w, "w", _HALF)
+    N, K = w.shape
+    if K % GROUP:
+        raise ValueError(f"K={K} must be a multiple of {GROUP}")
+    G = K // GROUP
+    dev = w.device
+
+    def out(t, name, shape, dtypes, dtype):
+        if t is None:
+            return torch.empty(shape, dtype=dtype, device=dev)
+        t = _dev(t, name, dtypes)
+        if tuple(t.shape) != shape or t.device != dev:
+            raise ValueError(f"{name} must be {shape} on {dev}")
+        return t
+
+    W = out(W, "W", (N, K // 8), _WORD, torch.int32)
+    scale = out(scale, "scale", (N, G), _HALF, torch.int16)
+    min = out(min, "min", (N, G), _HALF, torch.int16)
+    err = out(err, "err", (N, G), (torch.float64,), torch.float64)
+    st = lib().q4g128_quantize(w.data_ptr(), K, N, int(ncand), W.data_ptr(), scale.data_ptr(), min.data_ptr(),
+                               err.data_ptr(), _stream(stream, dev))
+    _check(st, "q4g128_quantize")
+    return W, scale, min, err
+
+
+__all__ = ["q4g128_gemm", "q4g128_quantize", "q4g128_gemm_splitk", "q4g128_gemm_streamk", "q4g128_streamk_workspace",
            "q4g128_streamk_workspace_bytes", "q4g128_dequant", "q4g128_splitk_workspace_bytes",
            "q4g128_splitk_default_splits", "q4g128_status_string", "q4g128_last_error",
            "q4g128_abi_version", "Q4G128Error", "lib", "LIB_PATH"]

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libq4g128.so")
 SOURCES = [os.path.join(CSRC, "q4g128_kernels.hip"), os.path.join(CSRC, "q4g128_streamk.hip"),
-           os.path.join(CSRC, "q4g128_api.cpp")]
+           os.path.join(CSRC, "q4g128_quant.hip"), os.path.join(CSRC, "q4g128_api.cpp")]
 ARCH = "gfx950"
 
 

@@ -280,4 +280,24 @@ q4g128_status q4g128_dequant(const uint32_t *W, const void *scale, const void *m
     return Q4G128_OK;
 }
 
+q4g128_status q4g128_quantize(const void *w, int K, int N, int ncand, uint32_t *W, void *scale, void *min,
+                              double *err, void *stream)
+{
+    if (!shape_ok(1, K, N) || !w || !W || !scale || !min || ncand < 1 || ncand > Q4G128_QUANT_MAX_CAND)
+        return Q4G128_EINVAL;
+    if (!aligned(w, 16) || !aligned(W, 16) || !aligned(scale, 2) || !aligned(min, 2) || (err && !aligned(err, 8)))
+        return Q4G128_EINVAL;
+    const long ngroups = (long)N * (K / Q4G128_GROUP);
+    const int gpw = q4g128::quantize_groups_per_block(ncand);
+    if ((ngroups + gpw - 1) / gpw > 0x7FFFFFFFL) return Q4G128_EINVAL;
+    hipError_t e = q4g128::launch_quantize(static_cast<const uint16_t *>(w), ngroups, ncand, W,
+                                           static_cast<uint16_t *>(scale), static_cast<uint16_t *>(min), err,
+                                           static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        set_error("quantize launch", e);
+        return Q4G128_EHIP;
+    }
+    return Q4G128_OK;
+}
+
 }  // extern "C"

@@ -121,4 +121,10 @@ hipError_t launch_splitk_sum(const float *P, int S, size_t MN, float *y, hipStre
 hipError_t launch_dequant(const uint32_t *W, const uint16_t *scale, const uint16_t *mn, int K, int N,
                           float *w, hipStream_t stream);
 
+// Quantizer (q4g128_quant.hip): groups staged per workgroup for `ncand`, and
+// the launch over `ngroups` consecutive 128-weight groups of w.
+int quantize_groups_per_block(int ncand);
+hipError_t launch_quantize(const uint16_t *w, long ngroups, int ncand, uint32_t *W, uint16_t *S, uint16_t *Mn,
+                           double *err, hipStream_t stream);
+
 }  // namespace q4g128

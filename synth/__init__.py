@@ -75,6 +75,19 @@ def draw_weights(rng: np.random.Generator, K: int, N: int) -> Weights:
     return Weights(W, scale, mn)
 
 
+def draw_dense_weights(rng: np.random.Generator, N: int, K: int, sigma: float = 0.02,
+                       outlier_frac: float = 1e-3, outlier_gain: float = 25.0) -> np.ndarray:
+    """Unquantized weights as bf16 bits [N][K] (row n = the K weights of
+    output column n): N(0, sigma^2), with round(outlier_frac * N * K) entries
+    chosen uniformly without replacement multiplied by outlier_gain."""
+    w = rng.standard_normal((N, K)) * sigma
+    n_out = int(round(outlier_frac * N * K))
+    if n_out:
+        idx = rng.choice(N * K, size=n_out, replace=False)
+        w.reshape(-1)[idx] *= outlier_gain
+    return to_bf16_bits(w)
+
+
 def draw_x(rng: np.random.Generator, M: int, K: int, outlier_frac: float = 0.0,
            outlier_gain: float = 20.0) -> np.ndarray:
     x = rng.standard_normal((M, K))

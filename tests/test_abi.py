@@ -136,3 +136,17 @@ def test_streamk_rejects(L):
     assert f(*ok, FAKE, need - 4, None) == q.Q4G128_EWORKSPACE
     assert f(FAKE, 1, 2048, FAKE, FAKE + 2, FAKE, 16, FAKE, FAKE, need, None) == q.Q4G128_EINVAL   # scale not 16-aligned
     assert f(FAKE, 9, 2048, FAKE, FAKE, FAKE, 16, FAKE, FAKE, need, None) == q.Q4G128_EINVAL
+
+
+def test_quantize_rejects(L):
+    f = L.q4g128_quantize
+    ok = dict(w=FAKE, K=256, N=4, ncand=9, W=FAKE, s=FAKE, m=FAKE, e=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["w"], a["K"], a["N"], a["ncand"], a["W"], a["s"], a["m"], a["e"], None)
+
+    for kw in (dict(w=None), dict(W=None), dict(s=None), dict(m=None), dict(K=200), dict(K=0), dict(N=0),
+               dict(ncand=0), dict(ncand=17), dict(w=FAKE + 2), dict(W=FAKE + 4), dict(s=FAKE + 1),
+               dict(e=FAKE + 4)):
+        assert call(**kw) == q.Q4G128_EINVAL, kw
