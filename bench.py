@@ -11,11 +11,14 @@ timed region.  Each step reads a different copy of the weights, cycling over
 Reported: algorithmic bytes per step / time as GB/s (value), the same at M=7
 (speculative verify) and the verify/decode time ratio, the down projection
 (split-K) and the full synthetic decode-step stream (257 launches, 12.7 GB)
-as extra fields, the dominant kernel's
+as extra fields, the quantizer producing the format (the gate/up matrix from
+bf16, 9 x 9 range search, fp64) as an extra field with its own fp64 ALU
+roofline, the dominant kernel's
 roofline (HIP-event kernel durations; bytes from the format: K*N/2 codes +
 4*N*K/128 scale/min + 2*M*K x + 4*M*N y), and the fp64 CPU oracle's rate on
-the host as a baseline.  A result that fails parity against the oracle is not
-reported (value null).
+the host as a baseline.  The oracle runs only in the CPU leg (cpu_baseline),
+after the GPU timing; it also computes the parity references, and a result
+that fails parity against them is not reported (value null).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -49,6 +52,7 @@ if ROOT not in sys.path:
 import synth  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
+PEAK_FP64_TFLOPS = 78.6         # MI355X fp64 vector peak
 ROTATE_BYTES = 1.2e9            # > 4x the 256 MB last-level cache
 METRIC = "achieved HBM GB/s (% of MI355X peak) for int4-g128 GEMV at M=1 and M=7"
 KERNEL = "gemv_q4g128"          # the dominant (only) kernel of a decode step
@@ -68,6 +72,7 @@ def parse():
     p.add_argument("--no-stream", action="store_true", help="skip the 12.7 GB decode-step stream")
     p.add_argument("--no-verify", action="store_true", help="skip the M=7 verify step (profiling decode alone)")
     p.add_argument("--no-down", action="store_true", help="skip the down projection")
+    p.add_argument("--no-quantize", action="store_true", help="skip the quantizer measurement")
     p.add_argument("--stream-only", action="store_true",
                    help="run only the decode-step stream (for a kernel trace of it) and print its fields")
     p.add_argument("--pmc-workload", action="store_true",
@@ -231,29 +236,102 @@ def graph_stream(torch, rc, seq, B, reps):
             "replay_equals_eager": bool(same)}
 
 
-def cpu_baseline(case, budget_s):
+QUANT_SHAPE = (34816, 5120)     # the gate/up matrix, [N][K] bf16 before quantization
+QUANT_NCAND = 9                  # 9 x 9 clipped ranges per group
+QUANT_SAMPLE_COLS = 64
+QUANT_FLOPS_PER_TRY = 8          # per weight and candidate: sub, div, rint, mul, add, sub, mul, add
+
+
+def measure_quantize(torch, q, reps=5, warmup=2):
+    """The quantizer on the gate/up matrix: bf16 weights [34816][5120] drawn
+    N(0, 0.02^2) with 0.1% of entries x25, into codes, scale and minimum with
+    the 9 x 9 range search.  Returns the timing and, for the parity gate, the
+    sampled columns' bf16 input and GPU outputs."""
+    N, K = QUANT_SHAPE
+    G = K // synth.GROUP
+    w = synth.draw_dense_weights(synth.rng_for(61), N, K)
+    dev = torch.device("cuda:0")
+    wd = torch.from_numpy(w.view(np.int16)).to(dev)
+    W = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    s = torch.empty((N, G), dtype=torch.int16, device=dev)
+    m = torch.empty((N, G), dtype=torch.int16, device=dev)
+    e = torch.empty((N, G), dtype=torch.float64, device=dev)
+    L = q.lib()
+    stream = torch.cuda.current_stream()
+    args = (wd.data_ptr(), K, N, QUANT_NCAND, W.data_ptr(), s.data_ptr(), m.data_ptr(), e.data_ptr(),
+            stream.cuda_stream)
+    for _ in range(warmup):
+        if L.q4g128_quantize(*args) != 0:
+            raise RuntimeError("quantize launch failed: " + q.q4g128_last_error())
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(reps):
+        L.q4g128_quantize(*args)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    t = t0.elapsed_time(t1) * 1e-3 / reps
+    cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(62).choice(N, QUANT_SAMPLE_COLS - 2,
+                                                                                   replace=False)]))
+    ci = torch.from_numpy(cols).to(dev)
+    gpu = tuple(a.index_select(0, ci).cpu().numpy() for a in (W, s, m, e))
+    flops = N * G * QUANT_NCAND ** 2 * synth.GROUP * QUANT_FLOPS_PER_TRY
+    info = {"workload": f"quantize the gate/up matrix, bf16 [N={N}][K={K}], {QUANT_NCAND}x{QUANT_NCAND} "
+                        f"range search per 128-group",
+            "ms_per_matrix": round(t * 1e3, 4), "groups_per_s": round(N * G / t, 1),
+            "input_GBps": round(2 * N * K / t / 1e9, 2),
+            "roofline": {"bound": "alu", "achieved": round(flops / t / 1e12, 3), "peak": PEAK_FP64_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(flops / t / 1e12 / PEAK_FP64_TFLOPS, 4),
+                         "traffic": None, "kernel": "quantize_q4g128",
+                         "flops_per_launch": flops,
+                         "counting": "fp64, 8 per weight per candidate, a divide counted as one"}}
+    del wd, W, s, m, e
+    torch.cuda.empty_cache()
+    return info, (np.ascontiguousarray(w[cols]), gpu)
+
+
+def cpu_baseline(dec_case, budget_s, y_dec, ver_case=None, y_ver=None, quant=None):
+    """The CPU leg, the only part of the benchmark that runs the fp64 oracle:
+    it times the oracle on the decode workload (when budget_s > 0) and
+    computes the references the parity gate compares the GPU results with
+    (decode and verify products within tolerance; the quantizer's sampled
+    columns bit for bit).  Returns (baseline or None, {check: pass?})."""
     import oracle
     orc = oracle.load()
-    wt = case.weights
+    wt = dec_case.weights
+    y, a = orc.gemm(dec_case.x, wt.W, wt.scale, wt.mn)
+    checks = {"decode_M1": bool(oracle.within_tolerance(y_dec, y, a).all())}
+    if y_ver is not None:
+        yv, av = orc.gemm(ver_case.x, ver_case.weights.W, ver_case.weights.scale, ver_case.weights.mn)
+        checks["verify_M7"] = bool(oracle.within_tolerance(y_ver, yv, av).all())
+    if quant is not None:
+        w_cols, gpu = quant
+        ref = orc.quantize(w_cols, QUANT_NCAND)
+        checks["quantize"] = all(np.array_equal(np.ascontiguousarray(g).view(np.uint8),
+                                                np.ascontiguousarray(r).view(np.uint8)) for g, r in zip(gpu, ref))
+    if budget_s <= 0:
+        return None, checks
     t0 = time.perf_counter()
-    y, a = orc.gemm(case.x, wt.W, wt.scale, wt.mn)
+    orc.gemm(dec_case.x, wt.W, wt.scale, wt.mn)
     reps = 1
     while time.perf_counter() - t0 < budget_s and reps < 1000:
-        orc.gemm(case.x, wt.W, wt.scale, wt.mn)
+        orc.gemm(dec_case.x, wt.W, wt.scale, wt.mn)
         reps += 1
     dt = (time.perf_counter() - t0) / reps
-    B = synth.algorithmic_bytes(case.M, case.K, case.N)
+    B = synth.algorithmic_bytes(dec_case.M, dec_case.K, dec_case.N)
     # One thread, on a column sample of the same input (a bounded time).
-    cols = np.arange(0, case.N, 16, dtype=np.int64)
+    cols = np.arange(0, dec_case.N, 16, dtype=np.int64)
     t1 = time.perf_counter()
-    orc.gemm(case.x, wt.W, wt.scale, wt.mn, cols=cols, nthreads=1)
-    dt1 = (time.perf_counter() - t1) * case.N / cols.size
+    orc.gemm(dec_case.x, wt.W, wt.scale, wt.mn, cols=cols, nthreads=1)
+    dt1 = (time.perf_counter() - t1) * dec_case.N / cols.size
+    case = dec_case
     return {"value": round(B / dt / 1e9, 4), "unit": "GB/s", "cores": orc.max_threads(), "kind": "oracle",
             "sample": f"{reps} full fp64 oracle calls on the same M={case.M} K={case.K} N={case.N} "
                       f"input ({dt * 1e3:.1f} ms per call, {reps * dt:.1f} s in all)",
             "one_thread": {"value": round(B / dt1 / 1e9, 4), "unit": "GB/s",
                            "sample": f"every 16th column ({cols.size} of {case.N}) on 1 thread, scaled to all N"}}, \
-        (y, a)
+        checks
 
 
 # ---- HBM traffic from counters ------------------------------------------------
@@ -425,20 +503,8 @@ def main():
     y_dec = raw.y_of(dec_calls).cpu().numpy()
     y_ver = raw.y_of(ver_calls).cpu().numpy() if ver_calls else None
 
-    cpu = None
-    import oracle
-    if not args.no_cpu_baseline:
-        cpu, (yr, ar) = cpu_baseline(dec_case, args.cpu_seconds)
-    else:
-        yr, ar = oracle.load().gemm(dec_case.x, dec_case.weights.W, dec_case.weights.scale, dec_case.weights.mn)
-    ok_dec = bool(oracle.within_tolerance(y_dec, yr, ar).all())
-    ok_ver = None
-    if ver_calls:
-        yv, av = oracle.load().gemm(ver_case.x, ver_case.weights.W, ver_case.weights.scale, ver_case.weights.mn)
-        ok_ver = bool(oracle.within_tolerance(y_ver, yv, av).all())
-
-    # Bring the GPU out of its idle clocks (the oracle just kept it idle for
-    # seconds) before anything is timed: ~0.5 s of decode launches.
+    # Bring the GPU out of its idle clocks (setting up the inputs kept it idle
+    # for seconds) before anything is timed: ~0.5 s of decode launches.
     t_end = time.perf_counter() + 0.5
     while time.perf_counter() < t_end:
         for c in dec_calls:
@@ -455,12 +521,26 @@ def main():
         n_ver = max(1, args.steps // len(ver_calls)) * len(ver_calls)
         wall_v = timed_calls(torch, ver_calls, n_ver // len(ver_calls), max(1, args.warmup // len(ver_calls)))
         t_ver = wall_v * 1e-3 / n_ver
-        verify = {"GBps": round(B_ver / t_ver / 1e9, 1) if ok_ver else None, "us_per_call": round(t_ver * 1e6, 3),
-                  "bytes_per_call": B_ver,
-                  "time_ratio_vs_M1": round(t_ver / t_dec, 4) if ok_ver and ok_dec else None}
+        verify = {"GBps": round(B_ver / t_ver / 1e9, 1), "us_per_call": round(t_ver * 1e6, 3),
+                  "bytes_per_call": B_ver, "time_ratio_vs_M1": round(t_ver / t_dec, 4)}
     traffic = traffic_from_summary()
     down = None if args.no_down else measure_down(torch, q, args.steps, args.warmup)
     stream_step = measure_stream(torch, q) if not args.no_stream else None
+    quant, quant_out = (None, None) if args.no_quantize else measure_quantize(torch, q)
+
+    # The CPU leg last: oracle baseline and the parity references.
+    cpu, checks = cpu_baseline(dec_case, 0.0 if args.no_cpu_baseline else args.cpu_seconds, y_dec,
+                               ver_case, y_ver, quant_out)
+    ok_dec, ok_ver = checks["decode_M1"], checks.get("verify_M7")
+    if verify is not None:
+        if not ok_ver:
+            verify["GBps"] = None
+        if not (ok_ver and ok_dec):
+            verify["time_ratio_vs_M1"] = None
+    if quant is not None:
+        quant["parity"] = "pass" if checks["quantize"] else "FAIL"
+        if not checks["quantize"]:
+            quant["roofline"]["achieved"] = quant["roofline"]["frac"] = None
 
     line = {
         "metric": METRIC,
@@ -484,6 +564,7 @@ def main():
         "verify_M7": verify,
         "down_M1": down,
         "decode_step_stream": stream_step,
+        "quantize": quant,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": round(traffic) if traffic is not None else None,
