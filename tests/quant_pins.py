@@ -6,6 +6,7 @@ the quantizer disagrees with the fact:
   * a group lying exactly on a grid of 16 bf16 levels is recovered exactly,
     by round-to-nearest and by the range search (its first candidate already
     has zero error);
+  * a group worked by hand (codes, scale, minimum and error in closed form);
   * a constant group gets code 0, scale 0 and the constant as minimum;
   * every code is the nearest of the 16 levels of its group's scale and
     minimum, or 0 / 15 for weights below / above the levels;
@@ -41,6 +42,24 @@ def qpin_grid_exact(orc):
         assert np.array_equal(orc.codes(W), q), ncand
         assert np.all(_values(S) == 2.0 ** -6) and np.all(_values(Mn) == -2.0 ** -3), ncand
         assert np.all(err == 0.0), ncand
+
+
+def qpin_worked_rtn(orc):
+    """Worked by hand: v_0 = 0, v_1 = 15/16 and, for k >= 2, v_k = j/16 + 1/64
+    (k even) or j/16 - 1/64 (k odd) with j = 1 + k mod 14, all exact in bf16.
+    The range is [0, 15/16], so round-to-nearest has scale 1/16 and minimum
+    0; (v_k - 0)/(1/16) = j +- 1/4 rounds to code j; v_0, v_1 get codes 0 and
+    15 exactly, and every other weight is off by 1/64: error 126/4096."""
+    k = np.arange(128)
+    j = 1 + k % 14
+    v = j / 16.0 + np.where(k % 2 == 0, 1.0, -1.0) / 64.0
+    v[0], v[1] = 0.0, 15.0 / 16.0
+    q = j.copy()
+    q[0], q[1] = 0, 15
+    W, S, Mn, err = orc.quantize(_bits(v[None, :]), 1)
+    assert np.array_equal(orc.codes(W)[0], q)
+    assert _values(S)[0, 0] == 1.0 / 16.0 and _values(Mn)[0, 0] == 0.0
+    assert err[0, 0] == 126.0 / 4096.0
 
 
 def qpin_constant_group(orc):
@@ -105,5 +124,5 @@ def qpin_search_beats_round_to_nearest(orc):
     assert orc.codes(Wg)[0, 127] == 15 and _values(Mg)[0, 0] + 15 * _values(Sg)[0, 0] < 1.3
 
 
-ALL_QPINS = [qpin_grid_exact, qpin_constant_group, qpin_nearest_level, qpin_error_is_dequant_error,
+ALL_QPINS = [qpin_worked_rtn, qpin_grid_exact, qpin_constant_group, qpin_nearest_level, qpin_error_is_dequant_error,
              qpin_search_beats_round_to_nearest]
