@@ -16,8 +16,10 @@ format paragraph and bandwidth paragraph; bw24 article, exactness paragraph):
     a[m][n]  = sum over k of |x[m][k] * w[n][k]|                       (tolerance scale)
     w32      = w rounded once to fp32 (nearest, ties to even)
 
-and the quantizer that produces the format from bf16 weights (Token Rush
-README, quantization section; the steps are in q4g128_oracle.c).
+the quantizer that produces the format from bf16 weights (Token Rush README,
+quantization section; the steps are in q4g128_oracle.c), and the epilogues
+after the product (Token Rush README, steps table rows 3 and 8-9): SwiGLU on
+a fused gate/up product and a residual add + RMSNorm.
 
 bf16 tensors are passed as their uint16 bit patterns.
 """
@@ -60,8 +62,10 @@ class Oracle:
         L.q4o_gemm_cols.argtypes = [vp, lg, lg, vp, vp, vp, lg, vp, lg, vp, vp, ci]
         L.q4o_gemm.argtypes = [vp, lg, lg, vp, vp, vp, lg, vp, vp, ci]
         L.q4o_quantize.argtypes = [vp, lg, lg, ci, vp, vp, vp, vp, ci]
+        L.q4o_swiglu.argtypes = [vp, lg, lg, vp]
+        L.q4o_residual_rmsnorm.argtypes = [vp, vp, vp, ctypes.c_double, lg, lg, vp, vp]
         for f in ("q4o_codes", "q4o_dequant_f64", "q4o_dequant_f32", "q4o_gemm_cols",
-                  "q4o_gemm", "q4o_quantize", "q4o_abi_version", "q4o_plant", "q4o_max_threads"):
+                  "q4o_gemm", "q4o_quantize", "q4o_swiglu", "q4o_residual_rmsnorm", "q4o_abi_version", "q4o_plant", "q4o_max_threads"):
             getattr(L, f).restype = ci
         self.plant = L.q4o_plant()
 
@@ -137,6 +141,28 @@ class Oracle:
         self._check(self.lib.q4o_quantize(_ptr(w), K, N, int(ncand), _ptr(W), _ptr(S), _ptr(Mn), _ptr(err),
                                           int(nthreads)), "quantize")
         return W, S, Mn, err
+
+    def swiglu(self, y):
+        """fp64 y [M][2I] (gate columns first, then up) -> act [M][I] = silu(g) * u."""
+        y = np.ascontiguousarray(y, dtype=np.float64)
+        M, N = y.shape
+        act = np.empty((M, N // 2), dtype=np.float64)
+        self._check(self.lib.q4o_swiglu(_ptr(y), M, N, _ptr(act)), "swiglu")
+        return act
+
+    def residual_rmsnorm(self, y, r, gamma, eps: float):
+        """fp64 y, r [M][N], gamma [N] bf16 bits -> (h = r + y, out = h / sqrt(mean(h^2) + eps) * gamma)."""
+        y = np.ascontiguousarray(y, dtype=np.float64)
+        r = np.ascontiguousarray(r, dtype=np.float64)
+        gamma = np.ascontiguousarray(gamma, dtype=np.uint16)
+        M, N = y.shape
+        if r.shape != (M, N) or gamma.shape != (N,):
+            raise OracleError(f"residual {r.shape} / gamma {gamma.shape} do not match y {y.shape}")
+        h = np.empty((M, N), dtype=np.float64)
+        out = np.empty((M, N), dtype=np.float64)
+        self._check(self.lib.q4o_residual_rmsnorm(_ptr(y), _ptr(r), _ptr(gamma), float(eps), M, N, _ptr(h),
+                                                  _ptr(out)), "residual_rmsnorm")
+        return h, out
 
     def max_threads(self) -> int:
         return int(self.lib.q4o_max_threads())

@@ -402,6 +402,76 @@ int q4o_quantize(const uint16_t *w, long K, long N, int ncand, uint32_t *W, uint
 }
 
 /* Threads the OpenMP runtime would use by default (for reporting). */
+/* ---- epilogues after the product ---------------------------------------------
+ *
+ * Token Rush README, steps table: the projections are fused side by side
+ * along N (row 3), and split-K partial sums are added inside the following
+ * norm (rows 8-9).  The pages name neither the activation nor the norm's
+ * formula; the readings taken are those of the gated MLP and the RMSNorm of
+ * the model family both pages run:
+ *
+ *   SwiGLU on a fused gate/up product y [M][N], N = 2I, gate = columns
+ *   0..I-1, up = columns I..2I-1:
+ *       act[m][i] = silu(g) * u,  silu(g) = g / (1 + exp(-g)),
+ *       g = y[m][i], u = y[m][I + i];
+ *
+ *   residual add + RMSNorm of a product y [M][N] with residual r [M][N],
+ *   bf16 gain gamma [N] and eps:
+ *       h[m][n]   = r[m][n] + y[m][n]
+ *       ms[m]     = (sum over n ascending of h[m][n]^2) / N
+ *       out[m][n] = h[m][n] / sqrt(ms[m] + eps) * gamma[n].
+ *
+ * Both in fp64, on fp64 inputs (the oracle's own product), one row at a time.
+ */
+int q4o_swiglu(const double *y, long M, long N, double *act)
+{
+    if (!y || !act || M <= 0 || N <= 0 || N % 2) return ORC_EINVAL;
+    const long I = N / 2;
+    for (long m = 0; m < M; ++m)
+        for (long i = 0; i < I; ++i) {
+#if ORACLE_PLANT == 12
+            const double g = y[m * N + I + i], u = y[m * N + i];   /* planted: halves swapped */
+#else
+            const double g = y[m * N + i], u = y[m * N + I + i];
+#endif
+#if ORACLE_PLANT == 11
+            act[m * I + i] = g / (1.0 + exp(g)) * u;              /* planted: wrong sign in exp */
+#else
+            act[m * I + i] = g / (1.0 + exp(-g)) * u;
+#endif
+        }
+    return ORC_OK;
+}
+
+int q4o_residual_rmsnorm(const double *y, const double *r, const uint16_t *gamma, double eps, long M, long N,
+                         double *h, double *out)
+{
+    if (!y || !r || !gamma || !h || !out || M <= 0 || N <= 0 || !(eps >= 0.0)) return ORC_EINVAL;
+    for (long m = 0; m < M; ++m) {
+        double ss = 0.0;
+        for (long n = 0; n < N; ++n) {
+            h[m * N + n] = r[m * N + n] + y[m * N + n];
+            ss += h[m * N + n] * h[m * N + n];
+        }
+#if ORACLE_PLANT == 13
+        const double ms = ss;                                    /* planted: sum, not mean */
+#else
+        const double ms = ss / (double)N;
+#endif
+#if ORACLE_PLANT == 14
+        const double inv = 1.0 / sqrt(ms);                       /* planted: eps dropped */
+#else
+        const double inv = 1.0 / sqrt(ms + eps);
+#endif
+        for (long n = 0; n < N; ++n) {
+            double gm;
+            if (bf16_decode(gamma[n], &gm) != ORC_OK) return ORC_ENONFINITE;
+            out[m * N + n] = h[m * N + n] * inv * gm;
+        }
+    }
+    return ORC_OK;
+}
+
 int q4o_max_threads(void)
 {
 #ifdef _OPENMP
