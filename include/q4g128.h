@@ -126,6 +126,63 @@ q4g128_status q4g128_gemm_streamk(const void *x, int M, int K,
                                   int N, float *y, void *workspace, size_t workspace_bytes,
                                   void *stream);
 
+/* Bytes of workspace q4g128_gemm_swiglu needs for (M, K, N):
+ * splits * M * N * 4 with splits = q4g128_splitk_default_splits(K, N) (the
+ * partial sums of the shapes the fused launch cannot take).  Returns 0 for
+ * invalid arguments (N must be even). */
+size_t q4g128_swiglu_workspace_bytes(int M, int K, int N);
+
+/* The product on a fused gate/up matrix followed by the SwiGLU activation:
+ * N = 2I, output columns 0..I-1 of W are the gate projection and I..2I-1
+ * the up projection (Token Rush README, steps table row 3: projections fused
+ * side by side along N), and
+ *
+ *     act[m][i] = bf16( silu(g) * u ),  silu(g) = g / (1 + exp(-g)),
+ *     g = y[m][i], u = y[m][I + i]   (y the fp32 product q4g128_gemm gives),
+ *
+ * in fp32, rounded once to bf16 (nearest even), act bf16 [M][I] 2-byte
+ * aligned.  The activation is the gated MLP of the model family the pages
+ * run; the pages do not spell it out.  When the shape allows (K a multiple
+ * of 1024, scale and min 16-byte aligned, x small enough for the staging
+ * and the LDS), one launch computes each
+ * gate tile and its up tile on the same compute unit and applies the
+ * activation before anything is stored; otherwise the product's split-K
+ * partial sums go to the workspace and a second launch sums them (ascending
+ * split order) and applies it.  Both give the same bits, rows are
+ * bit-identical across M, and y itself is never written.  The workspace
+ * (q4g128_swiglu_workspace_bytes) is required either way and must not be
+ * shared by calls in flight. */
+q4g128_status q4g128_gemm_swiglu(const void *x, int M, int K,
+                                 const uint32_t *W, const void *scale, const void *min,
+                                 int N, void *act, float *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/* The product followed by a residual add and RMSNorm, with the split-K
+ * partial sums added inside the norm (Token Rush README, steps table rows
+ * 8-9: a split-K GEMV whose partials are summed in the norm):
+ *
+ *     h[m][n]     = residual[m][n] + y[m][n]                    (fp32)
+ *     x_out[m][n] = bf16( h[m][n] * inv[m] * gamma[n] ),
+ *     inv[m]      = 1 / sqrt( (sum over n of h[m][n]^2) / N + eps )
+ *
+ * y is the product with K cut into `splits` ranges exactly as in
+ * q4g128_gemm_splitk (splits == 1: not cut), its partials summed in
+ * ascending split order, so h equals fp32(residual + y_splitk) bit for bit.
+ * The sum of squares is taken in a fixed order (per thread of a
+ * 1024-thread workgroup per row, then a fixed tree), the square root and
+ * division correctly rounded.  residual and h fp32 [M][N] (h may be the
+ * residual itself, updated in place; 4-byte aligned); gamma bf16 [N];
+ * x_out bf16 [M][N] (the next product's input; 2-byte aligned); eps >= 0.
+ * The RMSNorm formula is the usual one of the model family the pages run;
+ * the pages do not spell it out.  Workspace: at least
+ * q4g128_splitk_workspace_bytes(M, N, splits) bytes, for splits == 1 too.
+ * Rows are bit-identical across M; results deterministic. */
+q4g128_status q4g128_gemm_rmsnorm(const void *x, int M, int K,
+                                  const uint32_t *W, const void *scale, const void *min,
+                                  int N, const float *residual, const void *gamma, float eps,
+                                  float *h, void *x_out, int splits,
+                                  float *workspace, size_t workspace_bytes, void *stream);
+
 /* Decoded weights w_out[n][k] = fp32(q*s + m), rounded once (fma), laid out
  * fp32 [N][K].  Uses the same device unpacking as the product; it exists so
  * tests can compare the unpack and dequant bit for bit.  Passage: Token Rush

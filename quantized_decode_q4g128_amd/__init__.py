@@ -55,6 +55,13 @@ def lib() -> ctypes.CDLL:
         L.q4g128_streamk_workspace_bytes.restype = sz
         L.q4g128_dequant.argtypes = [vp, vp, vp, ci, ci, vp, vp]
         L.q4g128_dequant.restype = ci
+        L.q4g128_swiglu_workspace_bytes.argtypes = [ci, ci, ci]
+        L.q4g128_swiglu_workspace_bytes.restype = sz
+        L.q4g128_gemm_swiglu.argtypes = [vp, ci, ci, vp, vp, vp, ci, vp, vp, sz, vp]
+        L.q4g128_gemm_swiglu.restype = ci
+        L.q4g128_gemm_rmsnorm.argtypes = [vp, ci, ci, vp, vp, vp, ci, vp, vp, ctypes.c_float, vp, vp, ci, vp, sz,
+                                          vp]
+        L.q4g128_gemm_rmsnorm.restype = ci
         L.q4g128_quantize.argtypes = [vp, ci, ci, ci, vp, vp, vp, vp, vp]
         L.q4g128_quantize.restype = ci
         L.q4g128_splitk_workspace_bytes.argtypes = [ci, ci, ci]
@@ -228,6 +235,69 @@ def q4g128_dequant(W, scale, min, out=None, stream=None) -> torch.Tensor:
     return out
 
 
+def q4g128_swiglu_workspace_bytes(M: int, K: int, N: int) -> int:
+    return int(lib().q4g128_swiglu_workspace_bytes(int(M), int(K), int(N)))
+
+
+def _half_out(t, name, shape, device):
+    if t is None:
+        return torch.empty(shape, dtype=torch.bfloat16, device=device)
+    t = _dev(t, name, _HALF)
+    if tuple(t.shape) != shape or t.device != device:
+        raise ValueError(f"{name} must be {shape} on {device}")
+    return t
+
+
+def _workspace(ws, need, device):
+    if ws is None:
+        ws = torch.empty((max(need, 4) // 4,), dtype=torch.float32, device=device)
+    ws = _dev(ws, "workspace", (torch.float32,), ndim=ws.dim())
+    if ws.device != device:
+        raise ValueError("workspace must be on the operands' device")
+    return ws
+
+
+def q4g128_gemm_swiglu(x, W, scale, min, act=None, workspace=None, stream=None) -> torch.Tensor:
+    """act [M][N/2] bf16 = silu(gate) * up of the fused gate/up product
+    (gate = output columns 0..N/2-1, up = the rest)."""
+    x, W, scale, min, M, K, N = _operands(x, W, scale, min)
+    if N % 2:
+        raise ValueError(f"N={N} must be even (gate and up halves)")
+    act = _half_out(act, "act", (M, N // 2), x.device)
+    workspace = _workspace(workspace, q4g128_swiglu_workspace_bytes(M, K, N), x.device)
+    st = lib().q4g128_gemm_swiglu(x.data_ptr(), M, K, W.data_ptr(), scale.data_ptr(), min.data_ptr(), N,
+                                  act.data_ptr(), workspace.data_ptr(), workspace.numel() * 4,
+                                  _stream(stream, x.device))
+    _check(st, "q4g128_gemm_swiglu")
+    return act
+
+
+def q4g128_gemm_rmsnorm(x, W, scale, min, residual, gamma, eps: float = 1e-6, splits=None, h=None, x_out=None,
+                        workspace=None, stream=None):
+    """(h, x_out): h = residual + x . dequant(W) (fp32 [M][N]; pass h=residual
+    to update it in place), x_out = bf16(h / sqrt(mean(h^2) + eps) * gamma),
+    the split-K partials (default split count) summed inside the norm."""
+    x, W, scale, min, M, K, N = _operands(x, W, scale, min)
+    residual = _dev(residual, "residual", (torch.float32,))
+    gamma = _dev(gamma, "gamma", _HALF, ndim=1)
+    if tuple(residual.shape) != (M, N) or tuple(gamma.shape) != (N,):
+        raise ValueError(f"residual must be [M][N] = {(M, N)} and gamma [N]")
+    if residual.device != x.device or gamma.device != x.device:
+        raise ValueError("all operands must be on the same device")
+    h = _out(h, M, N, x.device)
+    x_out = _half_out(x_out, "x_out", (M, N), x.device)
+    if splits is None:
+        splits = q4g128_splitk_default_splits(K, N)
+    need = q4g128_splitk_workspace_bytes(M, N, splits) if splits >= 1 else 0
+    workspace = _workspace(workspace, need, x.device)
+    st = lib().q4g128_gemm_rmsnorm(x.data_ptr(), M, K, W.data_ptr(), scale.data_ptr(), min.data_ptr(), N,
+                                   residual.data_ptr(), gamma.data_ptr(), float(eps), h.data_ptr(), x_out.data_ptr(),
+                                   int(splits), workspace.data_ptr(), workspace.numel() * 4,
+                                   _stream(stream, x.device))
+    _check(st, "q4g128_gemm_rmsnorm")
+    return h, x_out
+
+
 def q4g128_quantize(w, ncand: int = 9, W=None, scale=None, min=None, err=None, stream=None):
     """bf16 weights w [N][K] -> (W [N][K/8] int32, scale [N][K/128] int16
     bf16 bits, min [N][K/128] int16 bf16 bits, err [N][K/128] float64): the
@@ -259,7 +329,8 @@ def q4g128_quantize(w, ncand: int = 9, W=None, scale=None, min=None, err=None, s
     return W, scale, min, err
 
 
-__all__ = ["q4g128_gemm", "q4g128_quantize", "q4g128_gemm_splitk", "q4g128_gemm_streamk", "q4g128_streamk_workspace",
+__all__ = ["q4g128_gemm", "q4g128_quantize", "q4g128_gemm_swiglu", "q4g128_swiglu_workspace_bytes",
+           "q4g128_gemm_rmsnorm", "q4g128_gemm_splitk", "q4g128_gemm_streamk", "q4g128_streamk_workspace",
            "q4g128_streamk_workspace_bytes", "q4g128_dequant", "q4g128_splitk_workspace_bytes",
            "q4g128_splitk_default_splits", "q4g128_status_string", "q4g128_last_error",
            "q4g128_abi_version", "Q4G128Error", "lib", "LIB_PATH"]

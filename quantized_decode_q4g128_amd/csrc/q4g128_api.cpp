@@ -90,17 +90,17 @@ int bal_parts(int K, int N, int gx)
 }
 
 // Whether x for M rows over all of K fits the balanced kernel's staging and LDS.
-bool bal_fits(int M, int K, int N, int gx, int P)
+bool bal_fits(int M, int K, int N, int gx, int P, bool act)
 {
     using namespace q4g128;
     const int ng = K / 128;
     if ((long)M * ng * 16 > (long)kBalThreads * kBalStage) return false;       // x staging registers
     const int part = P > 1 ? 2 * ((ng / 2 + P - 1) / P) : ng;                    // longest part, groups
     if (16 * ((part + 7) / 8) > 64 * kBalSmRounds) return false;                 // scale/min pieces per lane
-    return bal_plan(M, K, N, 1, gx, P).lds <= kBalMaxLds;
+    return bal_plan(M, K, N, 1, gx, P, act).lds <= kBalMaxLds;
 }
 
-BalChoice plan_bal(int M, int K, int N, int S, const void *scale, const void *min)
+BalChoice plan_bal(int M, int K, int N, int S, const void *scale, const void *min, bool act = false)
 {
     BalChoice no = {0, 1};
     // One K split only: with several, fewer workgroups per split leave some
@@ -115,7 +115,7 @@ BalChoice plan_bal(int M, int K, int N, int S, const void *scale, const void *mi
     const int P = bal_parts(K, N, gx);
     // With P > 1 the sums differ in rounding from the per-tile kernel's, so a
     // shape takes this path for every M or for none: x is checked at M = 8.
-    if (!bal_fits(P > 1 ? Q4G128_MAX_M : M, K, N, gx, P)) return no;
+    if (!bal_fits(P > 1 ? Q4G128_MAX_M : M, K, N, gx, P, act)) return no;
     BalChoice c = {gx, P};
     return c;
 }
@@ -138,6 +138,44 @@ q4g128_status run_gemv(const void *x, int M, int K, const uint32_t *W, const voi
                              : q4g128::launch_gemv(a, plan_tiles_per_wave(K, N), stream);
     if (e != hipSuccess) {
         set_error("gemv launch", e);
+        return Q4G128_EHIP;
+    }
+    return Q4G128_OK;
+}
+
+// The fused gate/up product with bf16 silu(gate) * up written to act: one
+// launch of the balanced kernel when the shape allows it, else the product's
+// partial sums into the workspace and sum_swiglu over them.  The per-column
+// sums are the plain product's in both cases, so both give the same bits.
+q4g128_status run_swiglu(const void *x, int M, int K, const uint32_t *W, const void *scale, const void *min,
+                         int N, uint16_t *act, float *ws, hipStream_t stream)
+{
+    const BalChoice bc = plan_bal(M, K, N, 1, scale, min, true);
+    if (bc.gx > 0) {
+        q4g128::GemvArgs a;
+        a.x = static_cast<const uint16_t *>(x);
+        a.M = M;
+        a.K = K;
+        a.W = W;
+        a.scale = static_cast<const uint16_t *>(scale);
+        a.mn = static_cast<const uint16_t *>(min);
+        a.N = N;
+        a.out = nullptr;
+        a.S = 1;
+        a.act = act;
+        hipError_t e = q4g128::launch_gemv_bal(a, bc.gx, bc.P, stream);
+        if (e != hipSuccess) {
+            set_error("gemv+swiglu launch", e);
+            return Q4G128_EHIP;
+        }
+        return Q4G128_OK;
+    }
+    const int S = q4g128_splitk_default_splits(K, N);
+    q4g128_status rc = run_gemv(x, M, K, W, scale, min, N, ws, S, stream);
+    if (rc != Q4G128_OK) return rc;
+    hipError_t e = q4g128::launch_sum_swiglu(ws, S, M, N, act, stream);
+    if (e != hipSuccess) {
+        set_error("swiglu launch", e);
         return Q4G128_EHIP;
     }
     return Q4G128_OK;
@@ -295,6 +333,50 @@ q4g128_status q4g128_quantize(const void *w, int K, int N, int ncand, uint32_t *
                                            static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
         set_error("quantize launch", e);
+        return Q4G128_EHIP;
+    }
+    return Q4G128_OK;
+}
+
+size_t q4g128_swiglu_workspace_bytes(int M, int K, int N)
+{
+    if (M < 1 || M > Q4G128_MAX_M || N < 2 || N % 2) return 0;
+    const int S = q4g128_splitk_default_splits(K, N);
+    if (S < 1) return 0;
+    return (size_t)S * (size_t)M * (size_t)N * sizeof(float);
+}
+
+q4g128_status q4g128_gemm_swiglu(const void *x, int M, int K, const uint32_t *W, const void *scale, const void *min,
+                                 int N, void *act, float *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!shape_ok(M, K, N) || N % 2 || !act || !aligned(act, 2)) return Q4G128_EINVAL;
+    if (!x || !W || !scale || !min || !aligned(x, 16) || !aligned(W, 16) || !aligned(scale, 2) || !aligned(min, 2))
+        return Q4G128_EINVAL;
+    if (!workspace || !aligned(workspace, 4)) return Q4G128_EINVAL;
+    if (workspace_bytes < q4g128_swiglu_workspace_bytes(M, K, N)) return Q4G128_EWORKSPACE;
+    return run_swiglu(x, M, K, W, scale, min, N, static_cast<uint16_t *>(act), workspace,
+                      static_cast<hipStream_t>(stream));
+}
+
+q4g128_status q4g128_gemm_rmsnorm(const void *x, int M, int K, const uint32_t *W, const void *scale, const void *min,
+                                  int N, const float *residual, const void *gamma, float eps, float *h, void *x_out,
+                                  int splits, float *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!shape_ok(M, K, N) || !operands_ok(x, W, scale, min, h)) return Q4G128_EINVAL;
+    if (!residual || !gamma || !x_out || !aligned(residual, 4) || !aligned(gamma, 2) || !aligned(x_out, 2))
+        return Q4G128_EINVAL;
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return Q4G128_EINVAL;
+    if (splits < 1 || splits > max_splits(K) || splits > kMaxSplits) return Q4G128_EINVAL;
+    if (!workspace || !aligned(workspace, 4)) return Q4G128_EINVAL;
+    if (workspace_bytes < q4g128_splitk_workspace_bytes(M, N, splits)) return Q4G128_EWORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    q4g128_status rc = run_gemv(x, M, K, W, scale, min, N, workspace, splits, st);
+    if (rc != Q4G128_OK) return rc;
+    hipError_t e = q4g128::launch_sum_residual_rmsnorm(workspace, splits, M, N, residual,
+                                                       static_cast<const uint16_t *>(gamma), eps, h,
+                                                       static_cast<uint16_t *>(x_out), st);
+    if (e != hipSuccess) {
+        set_error("rmsnorm launch", e);
         return Q4G128_EHIP;
     }
     return Q4G128_OK;

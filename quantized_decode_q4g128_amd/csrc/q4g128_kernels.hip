@@ -397,16 +397,35 @@ struct BalTile : Tile<1, true, RING, SML, PAD> {
     }
 };
 
+// SwiGLU of a fused gate/up pair, rounded to bf16 (nearest even).  The
+// fused product's gate and up halves are its columns n and I + n (Token Rush
+// README, steps table row 3: projections fused side by side); the activation
+// is the gated MLP's silu(gate) * up.  Shared by every path that applies it,
+// so they give the same bits for the same fp32 gate and up values.
+__device__ __forceinline__ uint16_t swiglu_bf16(float g, float u)
+{
+    const float a = g / (1.0f + expf(-g)) * u;
+    const uint32_t b = __float_as_uint(a);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;        // NaN stays NaN
+    return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
 // PARTS: a workgroup with few tiles cuts each tile's K range into P parts
 // (one wave each, boundaries at even groups); the parts' fp32 sums go to LDS
 // and, after a barrier, are added in part order, so the result depends on
 // (K, N, P) only.  P comes from (K, N) and the CU count, never from M.
-template <int RING, bool SML, bool PARTS>
+// ACT: N = 2I is a fused gate/up product.  The workgroup owns pair-columns
+// [n0, n1) of I, cut in units of 4 (the same bytes per CU as the plain cut),
+// and computes gate tile k (columns n0 + 16k ..) and up tile k (I + n0 + 16k
+// ..) as separate units; their sums meet in LDS and bf16 silu(gate) * up is
+// written to act [M][I].  The per-column sums are those of the plain product.
+template <int RING, bool SML, bool PARTS, bool ACT>
 __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ mn, int N,
-    float *__restrict__ out, int S, int nblp, int P, int nps)
+    float *__restrict__ out, uint16_t *__restrict__ act, int S, int nblp, int P, int nps)
 {
+    constexpr bool SLOTS = PARTS || ACT;                   // unit sums go through LDS
     extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
 
     const int tid = threadIdx.x;
@@ -424,12 +443,16 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     // mix of larger and smaller shares.
     const int c = (gx % 8 == 0) ? (int)(blockIdx.x % 8) * (gx / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
     // Columns [n0, n1), cut in units of 8 so every CU streams the same bytes to
-    // within 8 columns (N = 34816 on 256 CUs: 136 each, 8 tiles of 16 + 1 of 8).
-    const int N8 = (N + 7) >> 3;
-    const int n0 = (int)((long)c * N8 / gx) * 8;
-    const int n1 = min((int)((long)(c + 1) * N8 / gx) * 8, N);
-    const int nchunk = (n1 - n0 + 15) >> 4;               // tiles of up to 16 columns
-    const int nunit = PARTS ? nchunk * P : nchunk;        // (tile, part) units
+    // within 8 columns (N = 34816 on 256 CUs: 136 each, 8 tiles of 16 + 1 of 8);
+    // ACT: pair-columns of I = N/2 in units of 4 (68 pairs each).
+    const int NC = ACT ? (N >> 1) : N;
+    const int CU = ACT ? 4 : 8;
+    const int NU = (NC + CU - 1) / CU;
+    const int n0 = (int)((long)c * NU / gx) * CU;
+    const int n1 = min((int)((long)(c + 1) * NU / gx) * CU, NC);
+    const int nchunk = (n1 - n0 + 15) >> 4;               // tiles of up to 16 columns (ACT: pairs of tiles)
+    const int ntile = ACT ? 2 * nchunk : nchunk;          // ACT: tile t = 2k + half (gate 0, up 1)
+    const int nunit = PARTS ? ntile * P : ntile;          // (tile, part) units
     const bool active = wave < nunit;                     // wave-uniform
 
     BalTile<RING, SML, PARTS> B;
@@ -453,10 +476,13 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     // behind megabytes of weight requests from all CUs, and the barrier waits
     // for the slowest wave's x.
     // A unit's column base and group range.
-    auto unit = [&](int u, int &cb, int &cs, int &ce) {
-        const int k = PARTS ? u / P : u;
-        const int p = PARTS ? u - k * P : 0;
+    auto unit = [&](int u, int &cb, int &cw, int &cs, int &ce) {
+        const int t = PARTS ? u / P : u;
+        const int p = PARTS ? u - t * P : 0;
+        const int k = ACT ? (t >> 1) : t;
         cb = n0 + 16 * k;
+        cw = min(16, n1 - cb);
+        if (ACT) cb += (t & 1) * NC;
         cs = PARTS ? gs + 2 * ((p * (ng >> 1)) / P) : gs;
         ce = PARTS ? gs + 2 * (((p + 1) * (ng >> 1)) / P) : ge;
     };
@@ -464,33 +490,58 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     xst.load(x, M, K, gs, ge);
     xst.store(xs, M, gs, ge);
     lds_barrier();
-    if (!PARTS && !active) return;
+    if (!SLOTS && !active) return;
 
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(out + (size_t)split * (size_t)M * (size_t)N, (uint32_t)(M * N * 4));
     if (active) {
         u32x4 sr[kBalSmRounds], mr[kBalSmRounds];
         for (int u = wave; u < nunit; u += kBalWaves) {   // this wave's units
-            int cb, cs, ce;
-            unit(u, cb, cs, ce);
+            int cb, cw, cs, ce;
+            unit(u, cb, cw, cs, ce);
             B.gs = cs;
             B.ge = ce;
             B.nblk = (ce - cs + 7) >> 3;
             B.smg0 = cs;
-            B.setup(W, scale, mn, cb, min(16, n1 - cb));
+            B.setup(W, scale, mn, cb, cw);
             if (SML) B.sm_load(sr, mr, lane);             // before the codes: waiting for them leaves the codes in flight
             B.prime(cs, ce);
             if (SML) B.sm_store(sr, mr, lane);            // the wave's own LDS area; its LDS ops stay in order
             if (SML) B.fetch_sm(0, cs);                   // (!SML: the prime loaded it)
             B.run(xs, gs, ng, cs, ce);
-            if (!PARTS) {
+            if (!SLOTS) {
                 B.store(ry, N, cb);
-            } else if (lane < 32) {                       // rows 0..7 of the part's 16 columns
+            } else if (lane < 32) {                       // rows 0..7 of the unit's 16 columns
                 *reinterpret_cast<f32x4 *>(slots + u * 128 + lane * 4) =
                     f32x4{B.acc[0][0], B.acc[0][1], B.acc[0][2], B.acc[0][3]};
             }
         }
     }
-    if (PARTS) {
+    if (ACT) {
+        lds_barrier();                                    // every wave, with or without a unit
+        // Pair-tile k: gate sums in units (2k)P .. (2k)P + P-1, up in (2k+1)P ..,
+        // parts added in order; lane i + 16h holds rows 4h..4h+3 of column i.
+        for (int k = wave; k < nchunk; k += kBalWaves) {
+            const int pb = n0 + 16 * k;
+            const int cw = min(16, n1 - pb);
+            const int li = lane & 31;
+            const float *sg = slots + (2 * k) * P * 128 + li * 4;
+            const float *su = slots + (2 * k + 1) * P * 128 + li * 4;
+            f32x4 g = *reinterpret_cast<const f32x4 *>(sg);
+            f32x4 v = *reinterpret_cast<const f32x4 *>(su);
+            for (int p = 1; p < P; ++p) {
+                g += *reinterpret_cast<const f32x4 *>(sg + p * 128);
+                v += *reinterpret_cast<const f32x4 *>(su + p * 128);
+            }
+            const int i = lane & 15, h = (lane >> 4) & 1;
+            if (lane < 32 && i < cw) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 4 * h + r;
+                    if (row < M) act[(size_t)row * NC + pb + i] = swiglu_bf16(g[r], v[r]);
+                }
+            }
+        }
+    } else if (PARTS) {
         lds_barrier();                                    // every wave, with or without a unit
         for (int k = wave; k < nchunk; k += kBalWaves) {
             const int cb = n0 + 16 * k;
@@ -513,6 +564,85 @@ __global__ __launch_bounds__(256) void splitk_sum(const float *__restrict__ P, i
     float v = P[e];
     for (int s = 1; s < S; ++s) v += P[(size_t)s * MN + e];
     y[e] = v;
+}
+
+// act[m][i] = swiglu_bf16(sum_s P[s][m][i], sum_s P[s][m][I + i]), N = 2I,
+// partials added in ascending s (as splitk_sum adds them).
+__global__ __launch_bounds__(256) void sum_swiglu(const float *__restrict__ P, int S, int M, int N,
+                                                  uint16_t *__restrict__ act)
+{
+    const int I = N >> 1;
+    const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= (size_t)M * I) return;
+    const size_t m = e / I, i = e - m * I;
+    const size_t MN = (size_t)M * N, eg = m * N + i, eu = eg + I;
+    float g = P[eg], u = P[eu];
+    for (int s = 1; s < S; ++s) {
+        g += P[(size_t)s * MN + eg];
+        u += P[(size_t)s * MN + eu];
+    }
+    act[e] = swiglu_bf16(g, u);
+}
+
+// Residual add + RMSNorm with the split-K partial sums added inside the norm
+// (Token Rush README, steps table rows 8-9).  One workgroup of 1024 threads
+// per row m: thread t takes n = t, t + 1024, ...; y = sum_s P[s] in ascending
+// s, h = r + y (written to h, which may be r itself), ss = sum of h*h (each
+// thread's terms in order by fmaf, then a butterfly within the wave, then the
+// 16 wave sums in order), inv = 1 / sqrt(ss / N + eps) (correctly rounded),
+// x_out = bf16((h * inv) * gamma).  PT > 0: the thread's h values stay in
+// registers (N <= 1024 PT); PT == 0: they are read back from h.
+constexpr int kNormThreads = 1024;
+
+__device__ __forceinline__ uint16_t bf16_rne(float a)
+{
+    const uint32_t b = __float_as_uint(a);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+    return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+template <int PT>
+__global__ __launch_bounds__(kNormThreads) void sum_residual_rmsnorm(const float *__restrict__ P, int S, int M,
+                                                                     int N, const float *r,
+                                                                     const uint16_t *__restrict__ gamma, float eps,
+                                                                     float *h, uint16_t *__restrict__ xo)
+{
+    __shared__ float wsum[kNormThreads / 64];
+    const int m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const size_t MN = (size_t)M * N;
+    const size_t row = (size_t)m * N;
+    constexpr int R = PT > 0 ? PT : 1;
+    float hv[R];
+    float ss = 0.0f;
+    const int passes = PT > 0 ? PT : (N + kNormThreads - 1) / kNormThreads;
+    for (int j = 0; j < passes; ++j) {
+        const int n = tid + j * kNormThreads;
+        float v = 0.0f;
+        if (n < N) {
+            const size_t e = row + n;
+            float t = P[e];
+            for (int s = 1; s < S; ++s) t += P[(size_t)s * MN + e];
+            v = r[e] + t;
+            h[e] = v;
+        }
+        if (PT > 0) hv[PT > 0 ? j : 0] = v;
+        ss = fmaf(v, v, ss);
+    }
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+    __syncthreads();
+    float tot = wsum[0];
+    for (int w = 1; w < kNormThreads / 64; ++w) tot += wsum[w];
+    const float inv = 1.0f / sqrtf(tot / (float)N + eps);
+    for (int j = 0; j < passes; ++j) {
+        const int n = tid + j * kNormThreads;
+        if (n < N) {
+            const float v = PT > 0 ? hv[PT > 0 ? j : 0] : h[row + n];
+            const float gm = __uint_as_float((uint32_t)gamma[n] << 16);
+            xo[row + n] = bf16_rne((v * inv) * gm);
+        }
+    }
 }
 
 // One thread per packed word: eight weights fp32(q*s + mn), one rounding each.
@@ -597,47 +727,78 @@ hipError_t launch_gemv(const GemvArgs &a, int tpw, hipStream_t stream)
     return hipGetLastError();
 }
 
-BalPlan bal_plan(int M, int K, int N, int S, int gx, int P)
+BalPlan bal_plan(int M, int K, int N, int S, int gx, int P, bool act)
 {
     BalPlan bp;
     const int nb = K / 1024;
     const int ngmax = (nb + S - 1) / S * 8;
-    const int N8 = (N + 7) / 8;
-    const int tiles = ((N8 + gx - 1) / gx * 8 + 15) / 16;      // most tiles of one workgroup
+    int tiles;                                                  // most tiles of one workgroup
+    if (act) {
+        const int NU = (N / 2 + 3) / 4;
+        tiles = 2 * (((NU + gx - 1) / gx * 4 + 15) / 16);
+    } else {
+        const int N8 = (N + 7) / 8;
+        tiles = ((N8 + gx - 1) / gx * 8 + 15) / 16;
+    }
     const int units = tiles * P;
     const int nw = units < kBalWaves ? units : kBalWaves;
     const int pg = P > 1 ? 2 * (((ngmax / 2) + P - 1) / P) : ngmax;   // longest part, in groups
     bp.nblp = ((pg + 7) / 8) | 1;
-    bp.nps = P > 1 ? units : 0;
+    bp.nps = (P > 1 || act) ? units : 0;
     bp.lds = (size_t)M * ngmax * 256 + (size_t)ngmax * 32 + (size_t)bp.nps * 512 +
              (size_t)(kBalSml ? nw : 0) * 2 * 16 * bp.nblp * 16;
     if (bp.lds < kBalOwnCu) bp.lds = kBalOwnCu;
     return bp;
 }
 
-template <bool PARTS>
+template <bool PARTS, bool ACT>
 static hipError_t launch_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)
 {
     static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing, kBalSml, PARTS>),
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
-    BalPlan bp = bal_plan(a.M, a.K, a.N, a.S, gx, P);
-    hipLaunchKernelGGL((gemv_q4g128_bal<kBalRing, kBalSml, PARTS>), dim3((unsigned)gx, (unsigned)a.S, 1),
-                       dim3(kBalThreads, 1, 1), bp.lds, stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.S,
-                       bp.nblp, P, bp.nps);
+    BalPlan bp = bal_plan(a.M, a.K, a.N, a.S, gx, P, ACT);
+    hipLaunchKernelGGL((gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT>), dim3((unsigned)gx, (unsigned)a.S, 1),
+                       dim3(kBalThreads, 1, 1), bp.lds, stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out,
+                       a.act, a.S, bp.nblp, P, bp.nps);
     return hipGetLastError();
 }
 
 hipError_t launch_gemv_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)
 {
-    return P > 1 ? launch_bal<true>(a, gx, P, stream) : launch_bal<false>(a, gx, 1, stream);
+    if (a.act) return P > 1 ? launch_bal<true, true>(a, gx, P, stream) : launch_bal<false, true>(a, gx, 1, stream);
+    return P > 1 ? launch_bal<true, false>(a, gx, P, stream) : launch_bal<false, false>(a, gx, 1, stream);
 }
 
 hipError_t launch_splitk_sum(const float *P, int S, size_t MN, float *y, hipStream_t stream)
 {
     dim3 grid((unsigned)((MN + 255) / 256), 1, 1);
     hipLaunchKernelGGL(splitk_sum, grid, dim3(256, 1, 1), 0, stream, P, S, MN, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_sum_swiglu(const float *P, int S, int M, int N, uint16_t *act, hipStream_t stream)
+{
+    const size_t MI = (size_t)M * (size_t)(N / 2);
+    hipLaunchKernelGGL(sum_swiglu, dim3((unsigned)((MI + 255) / 256), 1, 1), dim3(256, 1, 1), 0, stream, P, S, M, N,
+                       act);
+    return hipGetLastError();
+}
+
+hipError_t launch_sum_residual_rmsnorm(const float *P, int S, int M, int N, const float *r, const uint16_t *gamma,
+                                       float eps, float *h, uint16_t *xo, hipStream_t stream)
+{
+    const dim3 grid((unsigned)M, 1, 1), block(kNormThreads, 1, 1);
+    const int pt = (N + kNormThreads - 1) / kNormThreads;
+    if (pt <= 2)
+        hipLaunchKernelGGL(sum_residual_rmsnorm<2>, grid, block, 0, stream, P, S, M, N, r, gamma, eps, h, xo);
+    else if (pt <= 8)
+        hipLaunchKernelGGL(sum_residual_rmsnorm<8>, grid, block, 0, stream, P, S, M, N, r, gamma, eps, h, xo);
+    else if (pt <= 16)
+        hipLaunchKernelGGL(sum_residual_rmsnorm<16>, grid, block, 0, stream, P, S, M, N, r, gamma, eps, h, xo);
+    else
+        hipLaunchKernelGGL(sum_residual_rmsnorm<0>, grid, block, 0, stream, P, S, M, N, r, gamma, eps, h, xo);
     return hipGetLastError();
 }
 

@@ -45,6 +45,9 @@ struct GemvArgs {
     float *out;              // S == 1: y [M][N]; S > 1: partials [S][M][N]
     int S;                   // K splits, 1..ceil(K/1024): split s covers 8-group
                              // blocks [s*nb/S, (s+1)*nb/S), nb = ceil(K/1024)
+    uint16_t *act = nullptr; // balanced kernel only: if set, N = 2I is a fused gate/up
+                             // product and bf16 silu(gate) * up [M][I] is written
+                             // here instead of y (out unused)
 };
 
 // x chunk (in 128-groups, a multiple of kRing) staged in LDS for M rows.
@@ -81,7 +84,7 @@ struct BalPlan {
     int nblp;       // 8-group blocks per column row of a wave's scale/min area (odd)
     int nps;        // part-sum slots (P > 1)
 };
-BalPlan bal_plan(int M, int K, int N, int S, int gx, int P);
+BalPlan bal_plan(int M, int K, int N, int S, int gx, int P, bool act = false);
 // y (S == 1) or partials [S][M][N] (S > 1) with gx workgroups per split.
 // Requires K % 1024 == 0, 16-byte aligned scale/min, and the plan checks of
 // plan_bal (x and LDS fit).
@@ -120,6 +123,13 @@ hipError_t launch_gemv(const GemvArgs &a, int tpw, hipStream_t stream);
 hipError_t launch_splitk_sum(const float *P, int S, size_t MN, float *y, hipStream_t stream);
 hipError_t launch_dequant(const uint32_t *W, const uint16_t *scale, const uint16_t *mn, int K, int N,
                           float *w, hipStream_t stream);
+
+// Epilogues over partial sums P [S][M][N] (summed in ascending s first):
+// act [M][N/2] = bf16(silu(gate) * up) of the gate/up halves; and
+// h = r + y, x_out = bf16(h / sqrt(mean(h^2) + eps) * gamma) per row (h may be r).
+hipError_t launch_sum_swiglu(const float *P, int S, int M, int N, uint16_t *act, hipStream_t stream);
+hipError_t launch_sum_residual_rmsnorm(const float *P, int S, int M, int N, const float *r, const uint16_t *gamma,
+                                       float eps, float *h, uint16_t *xo, hipStream_t stream);
 
 // Quantizer (q4g128_quant.hip): groups staged per workgroup for `ncand`, and
 // the launch over `ngroups` consecutive 128-weight groups of w.

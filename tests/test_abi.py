@@ -150,3 +150,27 @@ def test_quantize_rejects(L):
                dict(ncand=0), dict(ncand=17), dict(w=FAKE + 2), dict(W=FAKE + 4), dict(s=FAKE + 1),
                dict(e=FAKE + 4)):
         assert call(**kw) == q.Q4G128_EINVAL, kw
+
+
+def test_epilogue_rejects(L):
+    f = L.q4g128_gemm_swiglu
+    need = q.q4g128_swiglu_workspace_bytes(1, 1024, 64)
+    assert need == 64 * 4
+    assert q.q4g128_swiglu_workspace_bytes(1, 1024, 63) == 0                      # odd N
+    ok = [FAKE, 1, 1024, FAKE, FAKE, FAKE]
+    assert f(*ok, 63, FAKE, FAKE, need, None) == q.Q4G128_EINVAL                 # odd N
+    assert f(*ok, 64, None, FAKE, need, None) == q.Q4G128_EINVAL                 # no act
+    assert f(*ok, 64, FAKE + 1, FAKE, need, None) == q.Q4G128_EINVAL             # act misaligned
+    assert f(*ok, 64, FAKE, None, need, None) == q.Q4G128_EINVAL                 # no workspace
+    assert f(*ok, 64, FAKE, FAKE, need - 4, None) == q.Q4G128_EWORKSPACE
+    g = L.q4g128_gemm_rmsnorm
+    base = [FAKE, 1, 1024, FAKE, FAKE, FAKE, 64]
+    wsb = q.q4g128_splitk_workspace_bytes(1, 64, 1)
+    assert g(*base, None, FAKE, 1e-6, FAKE, FAKE, 1, FAKE, wsb, None) == q.Q4G128_EINVAL    # no residual
+    assert g(*base, FAKE, None, 1e-6, FAKE, FAKE, 1, FAKE, wsb, None) == q.Q4G128_EINVAL    # no gamma
+    assert g(*base, FAKE, FAKE, -1.0, FAKE, FAKE, 1, FAKE, wsb, None) == q.Q4G128_EINVAL    # eps < 0
+    assert g(*base, FAKE, FAKE, float("nan"), FAKE, FAKE, 1, FAKE, wsb, None) == q.Q4G128_EINVAL
+    assert g(*base, FAKE, FAKE, 1e-6, FAKE, None, 1, FAKE, wsb, None) == q.Q4G128_EINVAL    # no x_out
+    assert g(*base, FAKE, FAKE, 1e-6, FAKE, FAKE, 0, FAKE, wsb, None) == q.Q4G128_EINVAL    # splits 0
+    assert g(*base, FAKE, FAKE, 1e-6, FAKE, FAKE, 2, FAKE, 10 ** 6, None) == q.Q4G128_EINVAL   # > ceil(K/1024)
+    assert g(*base, FAKE, FAKE, 1e-6, FAKE, FAKE, 1, FAKE, wsb - 4, None) == q.Q4G128_EWORKSPACE
