@@ -11,7 +11,9 @@ timed region.  Each step reads a different copy of the weights, cycling over
 Reported: algorithmic bytes per step / time as GB/s (value), the same at M=7
 (speculative verify) and the verify/decode time ratio, the down projection
 (split-K) and the full synthetic decode-step stream (257 launches, 12.7 GB)
-as extra fields, the quantizer producing the format (the gate/up matrix from
+as extra fields, the fused epilogues (gate/up + SwiGLU, down + residual-add
+RMSNorm) alone and chained through a 64-layer decode step, eager and as a
+HIP graph, the quantizer producing the format (the gate/up matrix from
 bf16, 9 x 9 range search, fp64) as an extra field with its own fp64 ALU
 roofline, the dominant kernel's
 roofline (HIP-event kernel durations; bytes from the format: K*N/2 codes +
@@ -73,6 +75,7 @@ def parse():
     p.add_argument("--no-verify", action="store_true", help="skip the M=7 verify step (profiling decode alone)")
     p.add_argument("--no-down", action="store_true", help="skip the down projection")
     p.add_argument("--no-quantize", action="store_true", help="skip the quantizer measurement")
+    p.add_argument("--no-epilogues", action="store_true", help="skip the fused-epilogue measurements")
     p.add_argument("--stream-only", action="store_true",
                    help="run only the decode-step stream (for a kernel trace of it) and print its fields")
     p.add_argument("--pmc-workload", action="store_true",
@@ -202,6 +205,181 @@ def measure_stream(torch, q, reps=5, warmup=2):
            "note": "wall time of back-to-back launches, gaps between kernels included"}
     out["graph"] = graph_stream(torch, rc, seq, B, reps)
     del rc
+    torch.cuda.empty_cache()
+    return out
+
+
+def dev_copies(torch, case, copies):
+    """Device copies of a case's weights: [(W, scale, min)] * copies."""
+    dev = torch.device("cuda:0")
+    wt = case.weights
+    W = torch.from_numpy(wt.W.view(np.int32)).to(dev)
+    s = torch.from_numpy(wt.scale.view(np.int16)).to(dev)
+    m = torch.from_numpy(wt.mn.view(np.int16)).to(dev)
+    return [(W, s, m)] + [(W.clone(), s.clone(), m.clone()) for _ in range(copies - 1)]
+
+
+def measure_epilogues(torch, q, steps, warmup):
+    """The fused epilogues on their decode shapes, each call on its own weight
+    copy: gate/up (M=1, K=5120, N=34816) with SwiGLU written as bf16, and down
+    (M=1, K=17408, N=5120, default split count) with the split-K partials
+    summed in the residual-add + RMSNorm."""
+    L = q.lib()
+    dev = torch.device("cuda:0")
+    out = {}
+    gu = synth.make_case("gateup")
+    B = synth.algorithmic_bytes(gu.M, gu.K, gu.N)
+    sets = dev_copies(torch, gu, max(2, math.ceil(ROTATE_BYTES / B)))
+    x = torch.from_numpy(gu.x.view(np.int16)).to(dev)
+    act = torch.empty((gu.M, gu.N // 2), dtype=torch.int16, device=dev)
+    wsb = q.q4g128_swiglu_workspace_bytes(gu.M, gu.K, gu.N)
+    ws = torch.empty(max(wsb, 4) // 4, dtype=torch.float32, device=dev)
+    calls = [lambda st, a=(x.data_ptr(), gu.M, gu.K, W.data_ptr(), sc.data_ptr(), mn.data_ptr(), gu.N,
+                           act.data_ptr(), ws.data_ptr(), wsb): L.q4g128_gemm_swiglu(*a, st) for W, sc, mn in sets]
+    reps = max(1, steps // len(calls))
+    t = timed_calls(torch, calls, reps, 1) * 1e-3 / (reps * len(calls))
+    Bo = B - 4 * gu.M * gu.N + 2 * gu.M * (gu.N // 2)           # y not written; bf16 act instead
+    out["gateup_swiglu_M1"] = {"us_per_call": round(t * 1e6, 3), "GBps": round(Bo / t / 1e9, 1),
+                               "bytes_per_call": Bo, "launches_per_call": 1}
+    del sets
+    dn = synth.make_case("down")
+    B = synth.algorithmic_bytes(dn.M, dn.K, dn.N)
+    sets = dev_copies(torch, dn, max(2, math.ceil(ROTATE_BYTES / B)))
+    x = torch.from_numpy(dn.x.view(np.int16)).to(dev)
+    rng = np.random.default_rng(63)
+    r = torch.from_numpy((rng.standard_normal((dn.M, dn.N)) * 0.5).astype(np.float32)).to(dev)
+    gamma = torch.from_numpy(synth.to_bf16_bits(1.0 + 0.1 * rng.standard_normal(dn.N)).view(np.int16)).to(dev)
+    h = torch.empty((dn.M, dn.N), dtype=torch.float32, device=dev)
+    xo = torch.empty((dn.M, dn.N), dtype=torch.int16, device=dev)
+    S = q.q4g128_splitk_default_splits(dn.K, dn.N)
+    wsb = q.q4g128_splitk_workspace_bytes(dn.M, dn.N, S)
+    ws = torch.empty(max(wsb, 4) // 4, dtype=torch.float32, device=dev)
+    calls = [lambda st, a=(x.data_ptr(), dn.M, dn.K, W.data_ptr(), sc.data_ptr(), mn.data_ptr(), dn.N, r.data_ptr(),
+                           gamma.data_ptr(), 1e-6, h.data_ptr(), xo.data_ptr(), S, ws.data_ptr(), wsb):
+             L.q4g128_gemm_rmsnorm(*a, st) for W, sc, mn in sets]
+    reps = max(1, steps // len(calls))
+    t = timed_calls(torch, calls, reps, 1) * 1e-3 / (reps * len(calls))
+    Bo = B + 4 * dn.M * dn.N + 2 * dn.N + 2 * dn.M * dn.N       # + residual in, gamma, bf16 x_out
+    out["down_rmsnorm_M1"] = {"us_per_call": round(t * 1e6, 3), "GBps": round(Bo / t / 1e9, 1),
+                              "bytes_per_call": Bo, "splits": S, "launches_per_call": 2}
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_chain(torch, q, reps=5):
+    """A decode step whose products feed each other as in a transformer layer
+    (attention itself out of scope): per layer, with h the fp32 residual
+    stream and x the bf16 normalised input,
+        qkv   = x . W_qkv                       (5120 -> 12288)
+        h    += a . W_o;  x' = RMSNorm(h)       (6144 -> 5120, a a fixed stand-in
+                                                 for the attention output)
+        act   = silu(gate) * up of x' . W_gu    (5120 -> 2 x 17408)
+        h    += act . W_down;  x = RMSNorm(h)   (17408 -> 5120, split-K partials
+                                                 summed in the norm)
+    64 layers, every layer on its own weight copies, then the 5120 -> 131072
+    output projection: 385 launches.  Timed eager and as one replayed HIP
+    graph; each replay starts from the same residual and must reproduce the
+    eager outputs bit for bit."""
+    L = q.lib()
+    dev = torch.device("cuda:0")
+    shapes = synth.stream_shapes()
+    cases = [synth.make_random(1, K, N, seed) for K, N, seed in shapes]
+    layers = synth.STREAM_LAYERS
+    w = [dev_copies(torch, cases[j], layers) for j in range(4)]
+    head = dev_copies(torch, cases[4], 1)[0]
+    rng = np.random.default_rng(64)
+    d = 5120
+    h0 = torch.from_numpy((rng.standard_normal((1, d)) * 0.5).astype(np.float32)).to(dev)
+    h = h0.clone()
+    x = torch.from_numpy(synth.to_bf16_bits(rng.standard_normal((1, d))).view(np.int16)).to(dev)
+    x0 = x.clone()
+    a = torch.from_numpy(synth.to_bf16_bits(rng.standard_normal((1, 6144))).view(np.int16)).to(dev)
+    xm = torch.empty((1, d), dtype=torch.int16, device=dev)
+    act = torch.empty((1, 17408), dtype=torch.int16, device=dev)
+    qkv = torch.empty((1, 12288), dtype=torch.float32, device=dev)
+    logits = torch.empty((1, 131072), dtype=torch.float32, device=dev)
+    g_o = torch.from_numpy(synth.to_bf16_bits(1.0 + 0.1 * rng.standard_normal(d)).view(np.int16)).to(dev)
+    g_d = torch.from_numpy(synth.to_bf16_bits(1.0 + 0.1 * rng.standard_normal(d)).view(np.int16)).to(dev)
+    S_o = q.q4g128_splitk_default_splits(6144, d)
+    S_d = q.q4g128_splitk_default_splits(17408, d)
+    wsb = max(q.q4g128_splitk_workspace_bytes(1, d, S_o), q.q4g128_splitk_workspace_bytes(1, d, S_d),
+              q.q4g128_swiglu_workspace_bytes(1, 5120, 34816))
+    ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
+    seq = []
+    for l in range(layers):
+        Wq, sq, mq = w[0][l]
+        Wo, so, mo = w[1][l]
+        Wg, sg, mg = w[2][l]
+        Wd, sd, md = w[3][l]
+        seq.append(lambda st, A=(x.data_ptr(), 1, 5120, Wq.data_ptr(), sq.data_ptr(), mq.data_ptr(), 12288,
+                                 qkv.data_ptr()): L.q4g128_gemm(*A, st))
+        seq.append(lambda st, A=(a.data_ptr(), 1, 6144, Wo.data_ptr(), so.data_ptr(), mo.data_ptr(), d, h.data_ptr(),
+                                 g_o.data_ptr(), 1e-6, h.data_ptr(), xm.data_ptr(), S_o, ws.data_ptr(), wsb):
+                   L.q4g128_gemm_rmsnorm(*A, st))
+        seq.append(lambda st, A=(xm.data_ptr(), 1, 5120, Wg.data_ptr(), sg.data_ptr(), mg.data_ptr(), 34816,
+                                 act.data_ptr(), ws.data_ptr(), wsb): L.q4g128_gemm_swiglu(*A, st))
+        seq.append(lambda st, A=(act.data_ptr(), 1, 17408, Wd.data_ptr(), sd.data_ptr(), md.data_ptr(), d,
+                                 h.data_ptr(), g_d.data_ptr(), 1e-6, h.data_ptr(), x.data_ptr(), S_d, ws.data_ptr(),
+                                 wsb): L.q4g128_gemm_rmsnorm(*A, st))
+    Wh, sh, mh = head
+    seq.append(lambda st, A=(x.data_ptr(), 1, 5120, Wh.data_ptr(), sh.data_ptr(), mh.data_ptr(), 131072,
+                             logits.data_ptr()): L.q4g128_gemm(*A, st))
+    B = layers * sum(synth.algorithmic_bytes(1, K, N) for K, N, _ in shapes[:4]) + \
+        synth.algorithmic_bytes(1, *shapes[4][:2])
+    stream = torch.cuda.current_stream()
+
+    def reset():
+        h.copy_(h0)
+        x.copy_(x0)
+
+    def run_eager():
+        st = torch.cuda.current_stream().cuda_stream      # the capture stream inside torch.cuda.graph
+        for c in seq:
+            if c(st) != 0:
+                raise RuntimeError("chain launch failed: " + q.q4g128_last_error())
+
+    reset()
+    run_eager()
+    torch.cuda.synchronize()
+    ref = (logits.clone(), h.clone())
+    finite = bool(torch.isfinite(logits).all() and torch.isfinite(h).all())
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    ms = 0.0
+    for _ in range(reps):
+        reset()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        run_eager()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms += t0.elapsed_time(t1)
+    t_eager = ms * 1e-3 / reps
+    g = torch.cuda.CUDAGraph()
+    reset()
+    with torch.cuda.graph(g):
+        run_eager()
+    same = True
+    ms = 0.0
+    for _ in range(reps):
+        reset()
+        logits.fill_(float("nan"))
+        torch.cuda.synchronize()
+        t0.record(stream)
+        g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms += t0.elapsed_time(t1)
+        same = same and torch.equal(logits, ref[0]) and torch.equal(h, ref[1])
+    t_graph = ms * 1e-3 / reps
+    out = {"launches_per_step": len(seq) + 2 * layers, "bytes_per_step": B,
+           "ms_per_step": round(t_eager * 1e3, 4), "GBps_wall": round(B / t_eager / 1e9, 1),
+           "graph": {"ms_per_step": round(t_graph * 1e3, 4), "GBps_wall": round(B / t_graph / 1e9, 1),
+                     "replay_equals_eager": bool(same)},
+           "outputs_finite": finite,
+           "note": "products chained through the fused epilogues; weight bytes as the plain stream"}
+    del w, head, g
     torch.cuda.empty_cache()
     return out
 
@@ -526,6 +704,8 @@ def main():
     traffic = traffic_from_summary()
     down = None if args.no_down else measure_down(torch, q, args.steps, args.warmup)
     stream_step = measure_stream(torch, q) if not args.no_stream else None
+    epilogues = None if args.no_epilogues else measure_epilogues(torch, q, args.steps, args.warmup)
+    chain = measure_chain(torch, q) if not (args.no_stream or args.no_epilogues) else None
     quant, quant_out = (None, None) if args.no_quantize else measure_quantize(torch, q)
 
     # The CPU leg last: oracle baseline and the parity references.
@@ -564,6 +744,8 @@ def main():
         "verify_M7": verify,
         "down_M1": down,
         "decode_step_stream": stream_step,
+        "epilogues": epilogues,
+        "decode_step_chain": chain,
         "quantize": quant,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),

@@ -108,6 +108,8 @@ BalChoice plan_bal(int M, int K, int N, int S, const void *scale, const void *mi
     if (S != 1) return no;
     if (K % 1024 != 0 || !aligned(scale, 16) || !aligned(min, 16)) return no;
     if ((long)M * N * 4 >= (1L << 31)) return no;
+    // ACT tiles address gate and up columns N/2 apart through one descriptor.
+    if (act && ((long)N / 2 + 8) * (K / 2) >= (1L << 31)) return no;
     const int ncu = device_cus();
     if (ncu < 1) return no;
     const int N8 = (N + 7) / 8;

@@ -312,6 +312,19 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
     }
 }
 
+// SwiGLU of a fused gate/up pair, rounded to bf16 (nearest even).  The
+// fused product's gate and up halves are its columns n and I + n (Token Rush
+// README, steps table row 3: projections fused side by side); the activation
+// is the gated MLP's silu(gate) * up.  Shared by every path that applies it,
+// so they give the same bits for the same fp32 gate and up values.
+__device__ __forceinline__ uint16_t swiglu_bf16(float g, float u)
+{
+    const float a = g / (1.0f + expf(-g)) * u;
+    const uint32_t b = __float_as_uint(a);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;        // NaN stays NaN
+    return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
 // ---- balanced kernel: one workgroup per compute unit ---------------------------
 //
 // A stream only reaches full rate when every compute unit moves about the
@@ -326,23 +339,38 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
 // per-column instructions are those of gemv_q4g128, so results are the same
 // bits.  Needs K/128 a multiple of 8 and 16-byte aligned scale/min.
 
-template <int RING, bool SML, bool PAD>
+template <int RING, bool SML, bool PAD, bool ACT = false>
 struct BalTile : Tile<1, true, RING, SML, PAD> {
     typedef Tile<1, true, RING, SML, PAD> Base;
-    int la, lb, nblk, ncols;
+    int la, lb, nblk, ncols, wact, NC;
 
-    // Descriptors and lane offsets for the tile of `width` (1..16) columns
-    // from cbase; lanes past the width read its last column.
+    // Column of W that tile column c (0..15) reads, relative to the tile's
+    // base: plain, c itself (clamped to the tile's width); ACT, a tile holds
+    // `wact` <= 8 gate/up pairs: columns 0..7 the gate columns base + c and
+    // 8..15 the up columns NC + base + c - 8, each half clamped to its width.
+    __device__ __forceinline__ int colmap(int c) const
+    {
+        if (ACT) return c < 8 ? min(c, wact - 1) : NC + min(c - 8, wact - 1);
+        return min(c, ncols - 1);
+    }
+
+    // Descriptors and lane offsets for the tile of `width` columns (ACT:
+    // pairs, 1..8; else 1..16) from cbase; lanes past the width read its last
+    // column.
     __device__ __forceinline__ void setup(const uint32_t *W, const uint16_t *scale, const uint16_t *mn, int cbase_,
-                                          int width)
+                                          int width, int nc)
     {
         const int cbase = __builtin_amdgcn_readfirstlane(cbase_);
-        ncols = __builtin_amdgcn_readfirstlane(width);
-        this->rw = make_rsrc(W + (size_t)cbase * this->K8, (uint32_t)((size_t)ncols * this->K8 * 4));
-        this->rs = make_rsrc(scale + (size_t)cbase * this->G, (uint32_t)(ncols * this->G * 2));
-        this->rm = make_rsrc(mn + (size_t)cbase * this->G, (uint32_t)(ncols * this->G * 2));
-        this->vw[0] = (uint32_t)((size_t)min(la, ncols - 1) * this->K8 * 4 + 16 * lb);
-        this->vs[0] = (uint32_t)(min(la, ncols - 1) * this->G * 2);   // !SML: per-block loads, quad order
+        const int w = __builtin_amdgcn_readfirstlane(width);
+        NC = nc;
+        wact = w;
+        ncols = ACT ? 16 : w;                              // tile columns staged and computed
+        const size_t span = ACT ? (size_t)NC + w : (size_t)w;   // columns the descriptors cover
+        this->rw = make_rsrc(W + (size_t)cbase * this->K8, (uint32_t)(span * this->K8 * 4));
+        this->rs = make_rsrc(scale + (size_t)cbase * this->G, (uint32_t)(span * this->G * 2));
+        this->rm = make_rsrc(mn + (size_t)cbase * this->G, (uint32_t)(span * this->G * 2));
+        this->vw[0] = (uint32_t)((size_t)colmap(la) * this->K8 * 4 + 16 * lb);
+        this->vs[0] = (uint32_t)((size_t)colmap(la) * this->G * 2);   // !SML: per-block loads, quad order
 #pragma unroll
         for (int r = 0; r < 4; ++r) this->acc[0][r] = 0.0f;
     }
@@ -357,7 +385,7 @@ struct BalTile : Tile<1, true, RING, SML, PAD> {
             if (64 * r < pieces) {                         // wave-uniform
                 const int q = min(lane + 64 * r, pieces - 1);
                 const int col = q / nblk, b = q - col * nblk;
-                const uint32_t off = (uint32_t)(col * this->G + this->gs + 8 * b) * 2;
+                const uint32_t off = (uint32_t)(((size_t)colmap(col) * this->G + this->gs + 8 * b) * 2);
                 sr[r] = __builtin_amdgcn_raw_buffer_load_b128(this->rs, off, 0, 0);
                 mr[r] = __builtin_amdgcn_raw_buffer_load_b128(this->rm, off, 0, 0);
             }
@@ -395,37 +423,41 @@ struct BalTile : Tile<1, true, RING, SML, PAD> {
             }
         }
     }
-};
 
-// SwiGLU of a fused gate/up pair, rounded to bf16 (nearest even).  The
-// fused product's gate and up halves are its columns n and I + n (Token Rush
-// README, steps table row 3: projections fused side by side); the activation
-// is the gated MLP's silu(gate) * up.  Shared by every path that applies it,
-// so they give the same bits for the same fp32 gate and up values.
-__device__ __forceinline__ uint16_t swiglu_bf16(float g, float u)
-{
-    const float a = g / (1.0f + expf(-g)) * u;
-    const uint32_t b = __float_as_uint(a);
-    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;        // NaN stays NaN
-    return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
-}
+    // ACT: tile column i < 8 holds gate column base + i and column i + 8 the
+    // matching up column; lane i + 16h takes the up sums from lane i + 8 + 16h
+    // and writes rows 4h..4h+3 of act [M][NC].
+    __device__ __forceinline__ void store_act(uint16_t *act, int cbase) const
+    {
+        float u[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u[r] = __shfl_down(this->acc[0][r], 8);
+        if (this->i < wact) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * this->h + r;
+                if (row < this->M) act[(size_t)row * NC + cbase + this->i] = swiglu_bf16(this->acc[0][r], u[r]);
+            }
+        }
+    }
+};
 
 // PARTS: a workgroup with few tiles cuts each tile's K range into P parts
 // (one wave each, boundaries at even groups); the parts' fp32 sums go to LDS
 // and, after a barrier, are added in part order, so the result depends on
 // (K, N, P) only.  P comes from (K, N) and the CU count, never from M.
 // ACT: N = 2I is a fused gate/up product.  The workgroup owns pair-columns
-// [n0, n1) of I, cut in units of 4 (the same bytes per CU as the plain cut),
-// and computes gate tile k (columns n0 + 16k ..) and up tile k (I + n0 + 16k
-// ..) as separate units; their sums meet in LDS and bf16 silu(gate) * up is
-// written to act [M][I].  The per-column sums are those of the plain product.
+// [n0, n1) of I, cut in units of 4 (the same bytes per CU as the plain cut);
+// a tile holds 8 pairs, gate columns in its first 8 MFMA columns and the
+// matching up columns in the last 8, so a pair meets in one wave's
+// registers and bf16 silu(gate) * up goes straight to act [M][I].  The
+// per-column sums are those of the plain product.
 template <int RING, bool SML, bool PARTS, bool ACT>
 __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ mn, int N,
     float *__restrict__ out, uint16_t *__restrict__ act, int S, int nblp, int P, int nps)
 {
-    constexpr bool SLOTS = PARTS || ACT;                   // unit sums go through LDS
     extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
 
     const int tid = threadIdx.x;
@@ -450,12 +482,12 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     const int NU = (NC + CU - 1) / CU;
     const int n0 = (int)((long)c * NU / gx) * CU;
     const int n1 = min((int)((long)(c + 1) * NU / gx) * CU, NC);
-    const int nchunk = (n1 - n0 + 15) >> 4;               // tiles of up to 16 columns (ACT: pairs of tiles)
-    const int ntile = ACT ? 2 * nchunk : nchunk;          // ACT: tile t = 2k + half (gate 0, up 1)
-    const int nunit = PARTS ? ntile * P : ntile;          // (tile, part) units
+    const int TW = ACT ? 8 : 16;                          // columns (ACT: pairs) per tile
+    const int nchunk = (n1 - n0 + TW - 1) / TW;
+    const int nunit = PARTS ? nchunk * P : nchunk;        // (tile, part) units
     const bool active = wave < nunit;                     // wave-uniform
 
-    BalTile<RING, SML, PARTS> B;
+    BalTile<RING, SML, PARTS, ACT> B;
     B.i = lane & 15;
     B.h = lane >> 4;
     B.la = lane >> 2;
@@ -466,6 +498,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     B.G = G;
     B.K8 = (size_t)(K >> 3);
     B.nbl = nblp;
+    B.NC = NC;
     // LDS: x [M][ng*128] bf16, row sums [ng][8] fp32, nps part slots of 128
     // fp32 (PARTS), then one scale/minimum area of 2*16*nblp*8 bf16 per wave.
     float *slots = reinterpret_cast<float *>(xs + M * ng * 128 + ng * 16);
@@ -477,12 +510,10 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     // for the slowest wave's x.
     // A unit's column base and group range.
     auto unit = [&](int u, int &cb, int &cw, int &cs, int &ce) {
-        const int t = PARTS ? u / P : u;
-        const int p = PARTS ? u - t * P : 0;
-        const int k = ACT ? (t >> 1) : t;
-        cb = n0 + 16 * k;
-        cw = min(16, n1 - cb);
-        if (ACT) cb += (t & 1) * NC;
+        const int k = PARTS ? u / P : u;
+        const int p = PARTS ? u - k * P : 0;
+        cb = n0 + TW * k;
+        cw = min(TW, n1 - cb);
         cs = PARTS ? gs + 2 * ((p * (ng >> 1)) / P) : gs;
         ce = PARTS ? gs + 2 * (((p + 1) * (ng >> 1)) / P) : ge;
     };
@@ -490,7 +521,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     xst.load(x, M, K, gs, ge);
     xst.store(xs, M, gs, ge);
     lds_barrier();
-    if (!SLOTS && !active) return;
+    if (!PARTS && !active) return;
 
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(out + (size_t)split * (size_t)M * (size_t)N, (uint32_t)(M * N * 4));
     if (active) {
@@ -502,56 +533,67 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
             B.ge = ce;
             B.nblk = (ce - cs + 7) >> 3;
             B.smg0 = cs;
-            B.setup(W, scale, mn, cb, cw);
+            B.setup(W, scale, mn, cb, cw, NC);
             if (SML) B.sm_load(sr, mr, lane);             // before the codes: waiting for them leaves the codes in flight
             B.prime(cs, ce);
             if (SML) B.sm_store(sr, mr, lane);            // the wave's own LDS area; its LDS ops stay in order
             if (SML) B.fetch_sm(0, cs);                   // (!SML: the prime loaded it)
             B.run(xs, gs, ng, cs, ce);
-            if (!SLOTS) {
-                B.store(ry, N, cb);
+            if (!PARTS) {
+                if (ACT) B.store_act(act, cb);
+                else B.store(ry, N, cb);
             } else if (lane < 32) {                       // rows 0..7 of the unit's 16 columns
                 *reinterpret_cast<f32x4 *>(slots + u * 128 + lane * 4) =
                     f32x4{B.acc[0][0], B.acc[0][1], B.acc[0][2], B.acc[0][3]};
             }
         }
     }
-    if (ACT) {
-        lds_barrier();                                    // every wave, with or without a unit
-        // Pair-tile k: gate sums in units (2k)P .. (2k)P + P-1, up in (2k+1)P ..,
-        // parts added in order; lane i + 16h holds rows 4h..4h+3 of column i.
-        for (int k = wave; k < nchunk; k += kBalWaves) {
-            const int pb = n0 + 16 * k;
-            const int cw = min(16, n1 - pb);
-            const int li = lane & 31;
-            const float *sg = slots + (2 * k) * P * 128 + li * 4;
-            const float *su = slots + (2 * k + 1) * P * 128 + li * 4;
-            f32x4 g = *reinterpret_cast<const f32x4 *>(sg);
-            f32x4 v = *reinterpret_cast<const f32x4 *>(su);
-            for (int p = 1; p < P; ++p) {
-                g += *reinterpret_cast<const f32x4 *>(sg + p * 128);
-                v += *reinterpret_cast<const f32x4 *>(su + p * 128);
-            }
-            const int i = lane & 15, h = (lane >> 4) & 1;
-            if (lane < 32 && i < cw) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 4 * h + r;
-                    if (row < M) act[(size_t)row * NC + pb + i] = swiglu_bf16(g[r], v[r]);
-                }
-            }
-        }
-    } else if (PARTS) {
+    if (PARTS) {
         lds_barrier();                                    // every wave, with or without a unit
         for (int k = wave; k < nchunk; k += kBalWaves) {
-            const int cb = n0 + 16 * k;
+            const int cb = n0 + TW * k;
             f32x4 v = *reinterpret_cast<const f32x4 *>(slots + (k * P) * 128 + (lane & 31) * 4);
             for (int p = 1; p < P; ++p) v += *reinterpret_cast<const f32x4 *>(slots + (k * P + p) * 128 + (lane & 31) * 4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) B.acc[0][r] = v[r];
-            B.ncols = min(16, n1 - cb);
-            if (lane < 32) B.store(ry, N, cb);
+            if (ACT) {                                    // all lanes: the pair exchange is a shuffle
+                B.wact = min(TW, n1 - cb);
+                B.store_act(act, cb);
+            } else {
+                B.ncols = min(16, n1 - cb);
+                if (lane < 32) B.store(ry, N, cb);
+            }
         }
+    }
+}
+
+// Partial sums of R elements e[j] (valid where ok[j]) over S splits,
+// t[j] = P[0][e] + P[1][e] + ... + P[S-1][e] in ascending s.  The loads of up
+// to kSumBatch splits are all issued before any is added, so a thread waits
+// for ceil(S / kSumBatch) memory round trips, not S.
+#ifndef Q4G128_SUM_BATCH
+#define Q4G128_SUM_BATCH 4
+#endif
+constexpr int kSumBatch = Q4G128_SUM_BATCH;
+
+template <int R>
+__device__ __forceinline__ void sum_partials(const float *__restrict__ P, int S, size_t MN, const size_t (&e)[R],
+                                             const bool (&ok)[R], float (&t)[R])
+{
+#pragma unroll
+    for (int j = 0; j < R; ++j) t[j] = 0.0f;
+    for (int s0 = 0; s0 < S; s0 += kSumBatch) {
+        float v[kSumBatch][R];
+#pragma unroll
+        for (int q = 0; q < kSumBatch; ++q)
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+                v[q][j] = (s0 + q < S && ok[j]) ? P[(size_t)(s0 + q) * MN + e[j]] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < kSumBatch; ++q)
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+                if (s0 + q < S) t[j] = (s0 + q == 0) ? v[q][j] : t[j] + v[q][j];
     }
 }
 
@@ -559,11 +601,12 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
 __global__ __launch_bounds__(256) void splitk_sum(const float *__restrict__ P, int S, size_t MN,
                                                   float *__restrict__ y)
 {
-    const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= MN) return;
-    float v = P[e];
-    for (int s = 1; s < S; ++s) v += P[(size_t)s * MN + e];
-    y[e] = v;
+    const size_t e0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t e[1] = {e0};
+    const bool ok[1] = {e0 < MN};
+    float t[1];
+    sum_partials<1>(P, S, MN, e, ok, t);
+    if (ok[0]) y[e0] = t[0];
 }
 
 // act[m][i] = swiglu_bf16(sum_s P[s][m][i], sum_s P[s][m][I + i]), N = 2I,
@@ -575,13 +618,12 @@ __global__ __launch_bounds__(256) void sum_swiglu(const float *__restrict__ P, i
     const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= (size_t)M * I) return;
     const size_t m = e / I, i = e - m * I;
-    const size_t MN = (size_t)M * N, eg = m * N + i, eu = eg + I;
-    float g = P[eg], u = P[eu];
-    for (int s = 1; s < S; ++s) {
-        g += P[(size_t)s * MN + eg];
-        u += P[(size_t)s * MN + eu];
-    }
-    act[e] = swiglu_bf16(g, u);
+    const size_t MN = (size_t)M * N, eg = m * N + i;
+    const size_t ee[2] = {eg, eg + I};
+    const bool ok[2] = {true, true};
+    float t[2];
+    sum_partials<2>(P, S, MN, ee, ok, t);
+    act[e] = swiglu_bf16(t[0], t[1]);
 }
 
 // Residual add + RMSNorm with the split-K partial sums added inside the norm
@@ -592,7 +634,10 @@ __global__ __launch_bounds__(256) void sum_swiglu(const float *__restrict__ P, i
 // 16 wave sums in order), inv = 1 / sqrt(ss / N + eps) (correctly rounded),
 // x_out = bf16((h * inv) * gamma).  PT > 0: the thread's h values stay in
 // registers (N <= 1024 PT); PT == 0: they are read back from h.
-constexpr int kNormThreads = 1024;
+#ifndef Q4G128_NORM_THREADS
+#define Q4G128_NORM_THREADS 1024
+#endif
+constexpr int kNormThreads = Q4G128_NORM_THREADS;
 
 __device__ __forceinline__ uint16_t bf16_rne(float a)
 {
@@ -616,18 +661,50 @@ __global__ __launch_bounds__(kNormThreads) void sum_residual_rmsnorm(const float
     float hv[R];
     float ss = 0.0f;
     const int passes = PT > 0 ? PT : (N + kNormThreads - 1) / kNormThreads;
-    for (int j = 0; j < passes; ++j) {
-        const int n = tid + j * kNormThreads;
-        float v = 0.0f;
-        if (n < N) {
-            const size_t e = row + n;
-            float t = P[e];
-            for (int s = 1; s < S; ++s) t += P[(size_t)s * MN + e];
-            v = r[e] + t;
-            h[e] = v;
+    if (PT > 0) {
+        // Every load first (r and h may be the same array, so a store to h
+        // would otherwise hold back the next element's loads), then h.
+        float rv[R];
+        size_t e[R];
+        bool ok[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int n = tid + j * kNormThreads;
+            e[j] = row + n;
+            ok[j] = n < N;
+            rv[j] = ok[j] ? r[e[j]] : 0.0f;
         }
-        if (PT > 0) hv[PT > 0 ? j : 0] = v;
-        ss = fmaf(v, v, ss);
+        sum_partials<R>(P, S, MN, e, ok, hv);
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int n = tid + j * kNormThreads;
+            const float v = rv[j] + hv[j];
+            if (n < N) h[row + n] = v;
+            hv[j] = v;
+            ss = fmaf(v, v, ss);
+        }
+    } else {
+        // Wide rows: the same steps on chunks of 8 of the thread's elements
+        // (loads of a chunk batched), h read back afterwards.
+        for (int j0 = 0; j0 < passes; j0 += 8) {
+            size_t e[8];
+            bool ok[8];
+            float t[8], rv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int n = tid + (j0 + j) * kNormThreads;
+                e[j] = row + n;
+                ok[j] = j0 + j < passes && n < N;
+                rv[j] = ok[j] ? r[e[j]] : 0.0f;
+            }
+            sum_partials<8>(P, S, MN, e, ok, t);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float v = rv[j] + t[j];
+                if (ok[j]) h[e[j]] = v;
+                ss = fmaf(ok[j] ? v : 0.0f, ok[j] ? v : 0.0f, ss);
+            }
+        }
     }
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
     if ((tid & 63) == 0) wsum[tid >> 6] = ss;
@@ -638,7 +715,7 @@ __global__ __launch_bounds__(kNormThreads) void sum_residual_rmsnorm(const float
     for (int j = 0; j < passes; ++j) {
         const int n = tid + j * kNormThreads;
         if (n < N) {
-            const float v = PT > 0 ? hv[PT > 0 ? j : 0] : h[row + n];
+            const float v = PT > 0 ? hv[PT > 0 ? j : 0] : h[row + n];   // PT == 0: this thread's own h
             const float gm = __uint_as_float((uint32_t)gamma[n] << 16);
             xo[row + n] = bf16_rne((v * inv) * gm);
         }
@@ -735,7 +812,7 @@ BalPlan bal_plan(int M, int K, int N, int S, int gx, int P, bool act)
     int tiles;                                                  // most tiles of one workgroup
     if (act) {
         const int NU = (N / 2 + 3) / 4;
-        tiles = 2 * (((NU + gx - 1) / gx * 4 + 15) / 16);
+        tiles = ((NU + gx - 1) / gx * 4 + 7) / 8;               // tiles of 8 gate/up pairs
     } else {
         const int N8 = (N + 7) / 8;
         tiles = ((N8 + gx - 1) / gx * 8 + 15) / 16;
@@ -744,7 +821,7 @@ BalPlan bal_plan(int M, int K, int N, int S, int gx, int P, bool act)
     const int nw = units < kBalWaves ? units : kBalWaves;
     const int pg = P > 1 ? 2 * (((ngmax / 2) + P - 1) / P) : ngmax;   // longest part, in groups
     bp.nblp = ((pg + 7) / 8) | 1;
-    bp.nps = (P > 1 || act) ? units : 0;
+    bp.nps = P > 1 ? units : 0;
     bp.lds = (size_t)M * ngmax * 256 + (size_t)ngmax * 32 + (size_t)bp.nps * 512 +
              (size_t)(kBalSml ? nw : 0) * 2 * 16 * bp.nblp * 16;
     if (bp.lds < kBalOwnCu) bp.lds = kBalOwnCu;
@@ -786,6 +863,9 @@ hipError_t launch_sum_swiglu(const float *P, int S, int M, int N, uint16_t *act,
     return hipGetLastError();
 }
 
+// 16 elements per thread in registers only while the batched loads fit too.
+constexpr bool kNormPt16 = kSumBatch * 16 <= 64;
+
 hipError_t launch_sum_residual_rmsnorm(const float *P, int S, int M, int N, const float *r, const uint16_t *gamma,
                                        float eps, float *h, uint16_t *xo, hipStream_t stream)
 {
@@ -795,8 +875,9 @@ hipError_t launch_sum_residual_rmsnorm(const float *P, int S, int M, int N, cons
         hipLaunchKernelGGL(sum_residual_rmsnorm<2>, grid, block, 0, stream, P, S, M, N, r, gamma, eps, h, xo);
     else if (pt <= 8)
         hipLaunchKernelGGL(sum_residual_rmsnorm<8>, grid, block, 0, stream, P, S, M, N, r, gamma, eps, h, xo);
-    else if (pt <= 16)
-        hipLaunchKernelGGL(sum_residual_rmsnorm<16>, grid, block, 0, stream, P, S, M, N, r, gamma, eps, h, xo);
+    else if (pt <= 16 && kNormPt16)
+        hipLaunchKernelGGL(sum_residual_rmsnorm<kNormPt16 ? 16 : 8>, grid, block, 0, stream, P, S, M, N, r, gamma, eps, h,
+                           xo);
     else
         hipLaunchKernelGGL(sum_residual_rmsnorm<0>, grid, block, 0, stream, P, S, M, N, r, gamma, eps, h, xo);
     return hipGetLastError();
