@@ -18,7 +18,9 @@ bf16, 9 x 9 range search, fp64) as an extra field with its own fp64 ALU
 roofline, the dominant kernel's
 roofline (HIP-event kernel durations; bytes from the format: K*N/2 codes +
 4*N*K/128 scale/min + 2*M*K x + 4*M*N y), and the fp64 CPU oracle's rate on
-the host as a baseline.  The oracle runs only in the CPU leg (cpu_baseline),
+the host as a baseline, and beside the roofline what a pure read of the same
+codes reaches on this GPU in the product's access pattern and contiguously
+(libq4g128_probe.so).  The oracle runs only in the CPU leg (cpu_baseline),
 after the GPU timing; it also computes the parity references, and a result
 that fails parity against them is not reported (value null).
 
@@ -76,6 +78,7 @@ def parse():
     p.add_argument("--no-down", action="store_true", help="skip the down projection")
     p.add_argument("--no-quantize", action="store_true", help="skip the quantizer measurement")
     p.add_argument("--no-epilogues", action="store_true", help="skip the fused-epilogue measurements")
+    p.add_argument("--no-read-ceiling", action="store_true", help="skip the pure-read probes")
     p.add_argument("--stream-only", action="store_true",
                    help="run only the decode-step stream (for a kernel trace of it) and print its fields")
     p.add_argument("--pmc-workload", action="store_true",
@@ -469,6 +472,46 @@ def measure_quantize(torch, q, reps=5, warmup=2):
     return info, (np.ascontiguousarray(w[cols]), gpu)
 
 
+PROBE_LINEAR_WAVES = 1024
+
+
+def measure_read_ceiling(torch, case, reps=20):
+    """What HBM delivers on this GPU to a pure read of the gate/up codes
+    (K*N/2 bytes, no arithmetic): in the product's access pattern (a wave per
+    16-row tile, 64 contiguous bytes per row per step) and read contiguously
+    (1 KB per wave per step, 1024 waves).  Each launch reads its own copy of
+    the codes, as the timed product does."""
+    import ctypes
+    from quantized_decode_q4g128_amd.build import PROBE_PATH
+    if not os.path.exists(PROBE_PATH):
+        return None
+    P = ctypes.CDLL(PROBE_PATH)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    P.q4g128_probe_sink_words.argtypes = [ci, ci, ci]
+    P.q4g128_probe_sink_words.restype = ctypes.c_size_t
+    P.q4g128_probe_tile_read.argtypes = [vp, ci, ci, vp, vp]
+    P.q4g128_probe_linear_read.argtypes = [vp, ci, ci, ci, vp, vp]
+    dev = torch.device("cuda:0")
+    K, N = case.K, case.N
+    B = K * N // 2
+    W = torch.from_numpy(case.weights.W.view(np.int32)).to(dev)
+    copies = [W] + [W.clone() for _ in range(max(2, math.ceil(ROTATE_BYTES / B)) - 1)]
+    sink = torch.empty(P.q4g128_probe_sink_words(K, N, PROBE_LINEAR_WAVES), dtype=torch.int32, device=dev)
+    tile = [lambda st, w=w: P.q4g128_probe_tile_read(w.data_ptr(), K, N, sink.data_ptr(), st) for w in copies]
+    lin = [lambda st, w=w: P.q4g128_probe_linear_read(w.data_ptr(), K, N, PROBE_LINEAR_WAVES, sink.data_ptr(), st)
+           for w in copies]
+    out = {"bytes_per_launch": B}
+    for name, calls in (("tile_pattern", tile), ("linear", lin)):
+        passes = max(1, reps * 13 // len(calls))
+        t = timed_calls(torch, calls, passes, 2) * 1e-3 / (passes * len(calls))
+        out[name] = {"us_per_launch": round(t * 1e6, 3), "GBps": round(B / t / 1e9, 1)}
+    out["note"] = ("pure reads of the gate/up codes: tile_pattern = one wave per 16 rows, 64 B per row per "
+                   "step, 4 steps in flight; linear = 1 KB per wave per step, 1024 waves, 8 in flight")
+    del copies
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(dec_case, budget_s, y_dec, ver_case=None, y_ver=None, quant=None):
     """The CPU leg, the only part of the benchmark that runs the fp64 oracle:
     it times the oracle on the decode workload (when budget_s > 0) and
@@ -702,6 +745,7 @@ def main():
         verify = {"GBps": round(B_ver / t_ver / 1e9, 1), "us_per_call": round(t_ver * 1e6, 3),
                   "bytes_per_call": B_ver, "time_ratio_vs_M1": round(t_ver / t_dec, 4)}
     traffic = traffic_from_summary()
+    ceiling = None if args.no_read_ceiling else measure_read_ceiling(torch, dec_case)
     down = None if args.no_down else measure_down(torch, q, args.steps, args.warmup)
     stream_step = measure_stream(torch, q) if not args.no_stream else None
     epilogues = None if args.no_epilogues else measure_epilogues(torch, q, args.steps, args.warmup)
@@ -751,7 +795,10 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": round(traffic) if traffic is not None else None,
                      "kernel": KERNEL, "us_per_launch": round(t_dec * 1e6, 3),
-                     "algorithmic_bytes_per_launch": B_dec},
+                     "algorithmic_bytes_per_launch": B_dec,
+                     "frac_of_read_ceiling": (round(achieved / ceiling["tile_pattern"]["GBps"], 4)
+                                              if ceiling else None)},
+        "read_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

@@ -16,6 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libq4g128.so")
+PROBE_PATH = os.path.join(PKG, "libq4g128_probe.so")      # read-bandwidth probes, loaded by bench.py only
+PROBE_SOURCE = os.path.join(CSRC, "q4g128_probe.hip")
 SOURCES = [os.path.join(CSRC, "q4g128_kernels.hip"), os.path.join(CSRC, "q4g128_streamk.hip"),
            os.path.join(CSRC, "q4g128_quant.hip"), os.path.join(CSRC, "q4g128_api.cpp")]
 ARCH = "gfx950"
@@ -69,5 +71,17 @@ def build_library(out: str = LIB_PATH, extra_flags=(), quiet: bool = True) -> st
     return out
 
 
+def build_probe(out: str = PROBE_PATH) -> str:
+    """Compile the benchmark's read-bandwidth probes (a library of their own)."""
+    tmp = out + ".tmp"
+    cmd = [hipcc()] + compile_flags() + ["-shared", PROBE_SOURCE, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build_library(quiet=False))
+    print(build_probe())
