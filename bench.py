@@ -477,8 +477,9 @@ PROBE_LINEAR_WAVES = 1024
 
 def measure_read_ceiling(torch, case, reps=20):
     """What HBM delivers on this GPU to a pure read of the gate/up codes
-    (K*N/2 bytes, no arithmetic): in the product's access pattern (a wave per
-    16-row tile, 64 contiguous bytes per row per step) and read contiguously
+    (K*N/2 bytes, no arithmetic): in the product's access pattern and work
+    split (one 12-wave workgroup per CU owning an equal share of the rows,
+    tiles of 16 rows, 64 contiguous bytes per row per step) and read contiguously
     (1 KB per wave per step, 1024 waves).  Each launch reads its own copy of
     the codes, as the timed product does."""
     import ctypes
@@ -505,8 +506,9 @@ def measure_read_ceiling(torch, case, reps=20):
         passes = max(1, reps * 13 // len(calls))
         t = timed_calls(torch, calls, passes, 2) * 1e-3 / (passes * len(calls))
         out[name] = {"us_per_launch": round(t * 1e6, 3), "GBps": round(B / t / 1e9, 1)}
-    out["note"] = ("pure reads of the gate/up codes: tile_pattern = one wave per 16 rows, 64 B per row per "
-                   "step, 4 steps in flight; linear = 1 KB per wave per step, 1024 waves, 8 in flight")
+    out["note"] = ("pure reads of the gate/up codes: tile_pattern = the product's work split (12-wave "
+                   "workgroup per CU, 16-row tiles, 64 B per row per step, 4 steps in flight); linear = 1 KB "
+                   "per wave per step, 1024 waves, 8 in flight")
     del copies
     torch.cuda.empty_cache()
     return out

@@ -4,11 +4,14 @@
 // They read a code matrix W [N][K/8] uint32 and nothing else, so their
 // rates are what HBM delivers for a given access pattern on this GPU:
 //
-//   probe_tile_read    the product's pattern: one wave per tile of 16
-//                      consecutive rows n; per step each lane quad reads 64
-//                      contiguous bytes (one 128-weight group) of one row,
-//                      16 rows per wave instruction; 4 groups in flight per
-//                      wave; 4 waves per workgroup;
+//   probe_tile_read    the product's pattern and work split: one
+//                      12-wave workgroup per compute unit owning an equal
+//                      share of the rows (cut in units of 8, workgroups
+//                      numbered XCD by XCD), tiles of 16 consecutive rows,
+//                      one tile per wave at a time; per step each lane quad
+//                      reads 64 contiguous bytes (one 128-weight group) of
+//                      one row, 16 rows per wave instruction, 4 groups in
+//                      flight per wave;
 //   probe_linear_read  the same bytes read contiguously: each wave owns an
 //                      equal span of the buffer and reads 1 KB per step
 //                      (16 bytes per lane); 8 steps in flight per wave.
@@ -31,34 +34,51 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t b
 constexpr int kTileRing = 4;
 constexpr int kLinRing = 8;
 
-__global__ __launch_bounds__(256) void probe_tile_read(const uint32_t *__restrict__ W, int K, int N,
-                                                       uint32_t *__restrict__ sink)
+constexpr int kTileWaves = 12;
+constexpr int kOwnCuLds = 81 * 1024;
+
+__global__ __launch_bounds__(64 * kTileWaves) void probe_tile_read(const uint32_t *__restrict__ W, int K, int N,
+                                                                   uint32_t *__restrict__ sink)
 {
     const int lane = threadIdx.x & 63;
-    const int wave = (int)((blockIdx.x * blockDim.x + threadIdx.x) >> 6);
-    const int tiles = (N + 15) / 16;
-    if (wave >= tiles) return;                       // wave-uniform
+    const int wave = threadIdx.x >> 6;
+    const int gx = gridDim.x;
+    const int c = (gx % 8 == 0) ? (int)(blockIdx.x % 8) * (gx / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    const int N8 = (N + 7) >> 3;
+    const int n0 = (int)((long)c * N8 / gx) * 8;
+    const int n1 = min((int)((long)(c + 1) * N8 / gx) * 8, N);
+    const int ntile = (n1 - n0 + 15) >> 4;
     const int G = K / 128;
     const uint32_t rowb = (uint32_t)(K / 2);         // bytes per row
-    const int row = min(wave * 16 + (lane >> 2), N - 1);
     const __amdgpu_buffer_rsrc_t r = rsrc(W, (uint32_t)((size_t)N * rowb));
-    const uint32_t base = (uint32_t)row * rowb + 16 * (lane & 3);
     uint32_t acc = 0;
-    u32x4 ring[kTileRing];
+    for (int t = wave; t < ntile; t += kTileWaves) {
+        const int row = min(n0 + 16 * t + (lane >> 2), n1 - 1);
+        const uint32_t base = (uint32_t)row * rowb + 16 * (lane & 3);
+        u32x4 ring[kTileRing];
 #pragma unroll
-    for (int u = 0; u < kTileRing; ++u)
-        ring[u] = __builtin_amdgcn_raw_buffer_load_b128(r, base + 64 * (uint32_t)min(u, G - 1), 0, 0);
-    for (int g = 0; g < G; g += kTileRing) {
+        for (int u = 0; u < kTileRing; ++u)
+            ring[u] = __builtin_amdgcn_raw_buffer_load_b128(r, base + 64 * (uint32_t)min(u, G - 1), 0, 0);
+        for (int g = 0; g < G; g += kTileRing) {
 #pragma unroll
-        for (int u = 0; u < kTileRing; ++u) {
-            acc ^= ring[u].x ^ ring[u].y ^ ring[u].z ^ ring[u].w;
-            const int gn = min(g + u + kTileRing, G - 1);
-            ring[u] = __builtin_amdgcn_raw_buffer_load_b128(r, base + 64 * (uint32_t)gn, 0, 0);
+            for (int u = 0; u < kTileRing; ++u) {
+                acc ^= ring[u].x ^ ring[u].y ^ ring[u].z ^ ring[u].w;
+                const int gn = min(g + u + kTileRing, G - 1);
+                ring[u] = __builtin_amdgcn_raw_buffer_load_b128(r, base + 64 * (uint32_t)gn, 0, 0);
+            }
         }
-    }
 #pragma unroll
-    for (int u = 0; u < kTileRing; ++u) acc ^= ring[u].x ^ ring[u].y ^ ring[u].z ^ ring[u].w;
-    sink[(size_t)wave * 64 + lane] = acc;
+        for (int u = 0; u < kTileRing; ++u) acc ^= ring[u].x ^ ring[u].y ^ ring[u].z ^ ring[u].w;
+    }
+    sink[((size_t)blockIdx.x * kTileWaves + wave) * 64 + lane] = acc;
+}
+
+int compute_units()
+{
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    return ncu;
 }
 
 __global__ __launch_bounds__(256) void probe_linear_read(const uint32_t *__restrict__ W, size_t bytes, int waves,
@@ -95,11 +115,14 @@ __global__ __launch_bounds__(256) void probe_linear_read(const uint32_t *__restr
 
 extern "C" {
 
-// Sink words the probes write: 64 per wave.
+// Sink words the probes write: 64 per wave (the tile probe: 12 waves on
+// each of at most 1024 compute units).
 size_t q4g128_probe_sink_words(int K, int N, int linear_waves)
 {
-    const size_t tiles = ((size_t)N + 15) / 16;
-    const size_t w = tiles > (size_t)linear_waves ? tiles : (size_t)linear_waves;
+    (void)K;
+    (void)N;
+    const size_t w = (size_t)1024 * kTileWaves > (size_t)linear_waves ? (size_t)1024 * kTileWaves
+                                                                        : (size_t)linear_waves;
     return w * 64;
 }
 
@@ -109,8 +132,16 @@ int q4g128_probe_tile_read(const uint32_t *W, int K, int N, uint32_t *sink, void
 {
     if (!W || !sink || K <= 0 || K % 128 || N <= 0 || (size_t)N * (size_t)(K / 2) >= (1ull << 32))
         return (int)hipErrorInvalidValue;
-    const int tiles = (N + 15) / 16;
-    hipLaunchKernelGGL(probe_tile_read, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0,
+    const int ncu = compute_units();
+    if (ncu < 1 || ncu > 1024) return (int)hipErrorInvalidDevice;
+    const int N8 = (N + 7) / 8;
+    const int gx = ncu < N8 ? ncu : N8;
+    // The product's LDS request (over half the CU's 160 KB) keeps two
+    // workgroups off one CU; the probe asks for the same.
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&probe_tile_read),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kOwnCuLds);
+    if (attr != hipSuccess) return (int)attr;
+    hipLaunchKernelGGL(probe_tile_read, dim3((unsigned)gx), dim3(64 * kTileWaves), kOwnCuLds,
                        static_cast<hipStream_t>(stream), W, K, N, sink);
     return (int)hipGetLastError();
 }
