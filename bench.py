@@ -170,6 +170,22 @@ def timed_calls(torch, seq, reps, warmup):
     return t0.elapsed_time(t1)
 
 
+def measure_wide_verify(torch, q, raw, t_dec, steps, warmup):
+    """Verify steps wider than the 7-row one on the gate/up shape: M = 9 (a
+    draft of 8 tokens plus the next) and M = 16 (the MFMA tile's rows), each
+    timed like M = 7 and given as a ratio to the M = 1 call."""
+    out = {}
+    for M in (9, 16):
+        case = synth.make_random(M, 5120, 34816, 80 + M)
+        B = synth.algorithmic_bytes(M, case.K, case.N)
+        calls, _ = raw.prepare(case, max(2, math.ceil(ROTATE_BYTES / B)), splits=1)
+        n = max(1, steps // len(calls)) * len(calls)
+        t = timed_calls(torch, calls, n // len(calls), max(1, warmup // len(calls))) * 1e-3 / n
+        out[f"M{M}"] = {"us_per_call": round(t * 1e6, 3), "GBps": round(B / t / 1e9, 1), "bytes_per_call": B,
+                        "time_ratio_vs_M1": round(t / t_dec, 4)}
+    return out
+
+
 def measure_down(torch, q, steps, warmup):
     """Decode down projection (M=1, K=17408, N=5120; split-K with the default
     split count, partial sums reduced in split order)."""
@@ -746,6 +762,7 @@ def main():
         t_ver = wall_v * 1e-3 / n_ver
         verify = {"GBps": round(B_ver / t_ver / 1e9, 1), "us_per_call": round(t_ver * 1e6, 3),
                   "bytes_per_call": B_ver, "time_ratio_vs_M1": round(t_ver / t_dec, 4)}
+    wider = None if args.no_verify else measure_wide_verify(torch, q, raw, t_dec, args.steps, args.warmup)
     traffic = traffic_from_summary()
     ceiling = None if args.no_read_ceiling else measure_read_ceiling(torch, dec_case)
     down = None if args.no_down else measure_down(torch, q, args.steps, args.warmup)
@@ -788,6 +805,7 @@ def main():
         "parity": {"decode_M1": "pass" if ok_dec else "FAIL",
                    "verify_M7": None if ok_ver is None else ("pass" if ok_ver else "FAIL")},
         "verify_M7": verify,
+        "verify_wider": wider,
         "down_M1": down,
         "decode_step_stream": stream_step,
         "epilogues": epilogues,

@@ -1,11 +1,13 @@
 /*
  * q4g128.h -- C ABI of libq4g128.so: the int4-g128 weight-streaming product
  *
- *     y[M][N] = x[M][K] . dequant(W)[K][N],   1 <= M <= 8
+ *     y[M][N] = x[M][K] . dequant(W)[K][N],   1 <= M <= 16
  *
- * on AMD Instinct MI355X (gfx950).  M = 1 is a plain decode step; M = 2..8 is
- * a speculative verify step that checks M draft tokens in one pass (Token
- * Rush README, steps table rows 13-14 and 28).  Decode is bound by streaming
+ * on AMD Instinct MI355X (gfx950).  M = 1 is a plain decode step; M = 2..16
+ * is a speculative verify step that checks a draft of M - 1 tokens plus the
+ * next one in one pass (Token Rush README, steps table rows 13-14 and 28:
+ * verifying 7 draft tokens; bw24 article, feature list: draft depths up to
+ * 8, i.e. 9 rows).  Decode is bound by streaming
  * the weights (Token Rush README, bandwidth paragraph), so the library reads
  * every weight byte once per call, for all M rows together.
  *
@@ -31,7 +33,7 @@
  * Conventions for every call below:
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
  *     work on it and return without synchronising.
- *   - Argument errors return Q4G128_EINVAL (null pointer, M outside [1, 8],
+ *   - Argument errors return Q4G128_EINVAL (null pointer, M outside [1, 16],
  *     K <= 0, K > 2^24 or K % 128 != 0, N <= 0 or N > 2^28, splits > 65535,
  *     x or W or w_out not 16-byte aligned,
  *     scale or min not 2-byte aligned, y or workspace not 4-byte aligned,
@@ -56,7 +58,7 @@ extern "C" {
 
 #define Q4G128_ABI_VERSION 1
 #define Q4G128_GROUP 128
-#define Q4G128_MAX_M 8
+#define Q4G128_MAX_M 16
 #define Q4G128_QUANT_MAX_CAND 16
 
 typedef enum {
@@ -79,9 +81,10 @@ q4g128_status q4g128_gemm(const void *x, int M, int K,
  * partial sums P[s][m][n]).  Returns 0 for invalid arguments. */
 size_t q4g128_splitk_workspace_bytes(int M, int N, int splits);
 
-/* Split count the library recommends for a (K, N) shape: a pure function of
- * K and N only (never of M, so rows stay bit-identical across M).  1 means
- * "do not split"; returns 0 for invalid K or N. */
+/* Split count the library recommends for a (K, N) shape: a function of K, N
+ * and the current device's compute-unit count only (never of M, so rows
+ * stay bit-identical across M).  1 means "do not split"; returns 0 for
+ * invalid K or N. */
 int q4g128_splitk_default_splits(int K, int N);
 
 /* The product with K cut into `splits` contiguous ranges of whole blocks of
@@ -114,7 +117,7 @@ size_t q4g128_streamk_workspace_bytes(int K, int N);
  * paragraph (decode is bound by streaming the weights: every CU must stream
  * its share at full rate) and steps table rows 8-9 (partial sums over K).
  *
- * Requirements beyond the common ones: K % 1024 == 0; scale and min 16-byte
+ * Requirements beyond the common ones: M <= 8; K % 1024 == 0; scale and min 16-byte
  * aligned; workspace 256-byte aligned, at least
  * q4g128_streamk_workspace_bytes(K, N) bytes, ZERO-FILLED before its first
  * use.  Every call leaves the counters it used at zero again, so a workspace

@@ -5,7 +5,7 @@ Argument marshalling only.  Every step of the product runs in the library's
 HIP kernels; PyTorch supplies device memory and the stream.  The functions
 carry the C ABI's names (include/q4g128.h) and take torch tensors:
 
-    x      [M][K]    bf16 (or int16/uint16 holding bf16 bit patterns), 1 <= M <= 8
+    x      [M][K]    bf16 (or int16/uint16 holding bf16 bit patterns), 1 <= M <= 16
     W      [N][K/8]  int32/uint32 packed codes, low nibble first
     scale  [N][K/128] bf16 (or 16-bit bit patterns)
     min    [N][K/128] bf16 (or 16-bit bit patterns)
@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_PKG, "libq4g128.so")
 
 Q4G128_OK, Q4G128_EINVAL, Q4G128_EWORKSPACE, Q4G128_EHIP = 0, 1, 2, 3
 GROUP = 128
-MAX_M = 8
+MAX_M = 16
 
 _lib = None
 

@@ -116,7 +116,7 @@ BalChoice plan_bal(int M, int K, int N, int S, const void *scale, const void *mi
     const int gx = ncu < N8 ? ncu : N8;
     const int P = bal_parts(K, N, gx);
     // With P > 1 the sums differ in rounding from the per-tile kernel's, so a
-    // shape takes this path for every M or for none: x is checked at M = 8.
+    // shape takes this path for every M or for none: x is checked at M = 16.
     if (!bal_fits(P > 1 ? Q4G128_MAX_M : M, K, N, gx, P, act)) return no;
     BalChoice c = {gx, P};
     return c;
@@ -220,9 +220,17 @@ size_t q4g128_splitk_workspace_bytes(int M, int N, int splits)
 int q4g128_splitk_default_splits(int K, int N)
 {
     if (K <= 0 || K % Q4G128_GROUP != 0 || N <= 0 || K > kMaxK || N > kMaxN) return 0;
-    // The balanced kernel spreads any N over every CU without K splits when
-    // x for 8 rows of all of K fits its LDS.
-    if (K % 1024 == 0 && 8L * (K / 128) * 16 <= (long)q4g128::kBalThreads * q4g128::kBalStage) return 1;
+    // No K splits where the balanced kernel spreads the shape over every CU:
+    // with whole tiles when x for one row fits it (wider M falls back to the
+    // per-tile kernel, which then has enough tiles), and with K parts only if
+    // x for 16 rows fits (such shapes take it for every M or not at all).
+    const int ncu = device_cus();
+    if (K % 1024 == 0 && ncu > 0) {
+        const int N8 = (N + 7) / 8;
+        const int gx = ncu < N8 ? ncu : N8;
+        const int P = bal_parts(K, N, gx);
+        if (bal_fits(P > 1 ? Q4G128_MAX_M : 1, K, N, gx, P, false)) return 1;
+    }
     const long nb = max_splits(K);
     const long tpw = plan_tiles_per_wave(K, N);
     const long waves = ((long)N + 16 * tpw - 1) / (16 * tpw);
@@ -274,6 +282,7 @@ q4g128_status q4g128_gemm_streamk(const void *x, int M, int K, const uint32_t *W
                                   void *stream)
 {
     if (!shape_ok(M, K, N) || !operands_ok(x, W, scale, min, y)) return Q4G128_EINVAL;
+    if (M > q4g128::kSkMaxM) return Q4G128_EINVAL;
     if (K % 1024 != 0 || !aligned(scale, 16) || !aligned(min, 16)) return Q4G128_EINVAL;
     if (!workspace || !aligned(workspace, 256)) return Q4G128_EINVAL;
     if (workspace_bytes < streamk_ws_bytes(N)) return Q4G128_EWORKSPACE;

@@ -4,7 +4,8 @@
 //
 // Decode streams every weight byte once per step (Token Rush README,
 // bandwidth paragraph); an M-row verify step does the same with M activation
-// rows (steps table rows 13-14, 28).  One kernel serves every M in 1..8.
+// rows (steps table rows 13-14, 28).  One kernel serves every M in 1..16
+// (the MFMA's 16 rows).
 //
 // Per 128-group the sum is factored as
 //   sum_k x*(q*s + mn) = s * sum_k x*(128 + q) + (mn - 128*s) * sum_k x
@@ -117,7 +118,7 @@ struct Tile {
         u32x4 a[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u32x4 *>(gp + aoff[t]);
-        const f32x4 xsum = *reinterpret_cast<const f32x4 *>(xrow + lg * 8);
+        const f32x4 xsum = *reinterpret_cast<const f32x4 *>(xrow + lg * kXsRows);
         // Take the ring slot out (the gather reads it), then refill it at once
         // so RING groups stay in flight; the scheduling barrier keeps the
         // compiler from sinking the refill below the arithmetic.
@@ -177,7 +178,7 @@ struct Tile {
         const int ng = ce - cs;
         const int arow = min(i, M - 1);          // rows >= M read a real row; never stored
         const uint16_t *rbase = xs + arow * xng * 128;
-        const float *xrow = reinterpret_cast<const float *>(xs + M * xng * 128) + 4 * (h & 1);
+        const float *xrow = reinterpret_cast<const float *>(xs + M * xng * 128) + 4 * h;
         const int lg0 = cs - xg0;                // LDS group index of cs
         int aoff[4];
 #pragma unroll
@@ -224,7 +225,8 @@ struct Tile {
 // accumulate the same groups in the same order with the same instructions, so
 // they give identical bits.
 // A chunk of 16 groups of x for 8 rows must fit the staging registers.
-static_assert(kStageMax * 64 * kWavesSmall >= 8 * 16 * 16, "x staging cannot hold one 16-group chunk at M = 8");
+static_assert(kStageMax * 64 * kWavesSmall >= kSmallM * 16 * 16, "x staging cannot hold one 16-group chunk");
+static_assert(kStageMax * 64 * kWavesLarge >= kMaxM * 16 * 16, "x staging cannot hold one 16-group chunk at M = 16");
 
 template <int TPW, bool CHUNKED, bool VSM, int RING, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
@@ -499,10 +501,10 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     B.K8 = (size_t)(K >> 3);
     B.nbl = nblp;
     B.NC = NC;
-    // LDS: x [M][ng*128] bf16, row sums [ng][8] fp32, nps part slots of 128
+    // LDS: x [M][ng*128] bf16, row sums [ng][16] fp32, nps part slots of 256
     // fp32 (PARTS), then one scale/minimum area of 2*16*nblp*8 bf16 per wave.
-    float *slots = reinterpret_cast<float *>(xs + M * ng * 128 + ng * 16);
-    B.sml = xs + M * ng * 128 + ng * 16 + nps * 256 + wave * (2 * 16 * nblp * 8);
+    float *slots = reinterpret_cast<float *>(xs + M * ng * 128 + ng * kXsRows * 2);
+    B.sml = xs + M * ng * 128 + ng * kXsRows * 2 + nps * 512 + wave * (2 * 16 * nblp * 8);
 
     // x first, and alone: every wave's code and scale/minimum loads wait until
     // the workgroup's x is in LDS.  Issued together, its few kilobytes queue
@@ -542,8 +544,8 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
             if (!PARTS) {
                 if (ACT) B.store_act(act, cb);
                 else B.store(ry, N, cb);
-            } else if (lane < 32) {                       // rows 0..7 of the unit's 16 columns
-                *reinterpret_cast<f32x4 *>(slots + u * 128 + lane * 4) =
+            } else {                                      // the unit's 16 columns x 16 rows
+                *reinterpret_cast<f32x4 *>(slots + u * 256 + lane * 4) =
                     f32x4{B.acc[0][0], B.acc[0][1], B.acc[0][2], B.acc[0][3]};
             }
         }
@@ -552,8 +554,8 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
         lds_barrier();                                    // every wave, with or without a unit
         for (int k = wave; k < nchunk; k += kBalWaves) {
             const int cb = n0 + TW * k;
-            f32x4 v = *reinterpret_cast<const f32x4 *>(slots + (k * P) * 128 + (lane & 31) * 4);
-            for (int p = 1; p < P; ++p) v += *reinterpret_cast<const f32x4 *>(slots + (k * P + p) * 128 + (lane & 31) * 4);
+            f32x4 v = *reinterpret_cast<const f32x4 *>(slots + (k * P) * 256 + lane * 4);
+            for (int p = 1; p < P; ++p) v += *reinterpret_cast<const f32x4 *>(slots + (k * P + p) * 256 + lane * 4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) B.acc[0][r] = v[r];
             if (ACT) {                                    // all lanes: the pair exchange is a shuffle
@@ -561,7 +563,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
                 B.store_act(act, cb);
             } else {
                 B.ncols = min(16, n1 - cb);
-                if (lane < 32) B.store(ry, N, cb);
+                B.store(ry, N, cb);
             }
         }
     }
@@ -768,7 +770,13 @@ int chunk_groups(int M)
 template <int TPW, bool CHUNKED, bool VSM, int WAVES>
 static void launch_one(const GemvArgs &a, dim3 grid, int cg, hipStream_t stream)
 {
-    const size_t lds = (size_t)a.M * (size_t)cg * 128 * 2 + (size_t)cg * 8 * 4;
+    // x for up to 16 rows of a chunk can pass 64 KiB (66.5 KiB at M = 16):
+    // allow the kernel the CU's whole LDS once.
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_q4g128<TPW, CHUNKED, VSM, kRingDepth, WAVES>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBalMaxLds);
+    (void)attr;                                  // a failure shows up as the launch's error
+    const size_t lds = (size_t)a.M * (size_t)cg * 128 * 2 + (size_t)cg * kXsRows * 4;
     hipLaunchKernelGGL((gemv_q4g128<TPW, CHUNKED, VSM, kRingDepth, WAVES>), grid, dim3(64 * WAVES, 1, 1), lds,
                        stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.S, cg);
 }
@@ -822,7 +830,7 @@ BalPlan bal_plan(int M, int K, int N, int S, int gx, int P, bool act)
     const int pg = P > 1 ? 2 * (((ngmax / 2) + P - 1) / P) : ngmax;   // longest part, in groups
     bp.nblp = ((pg + 7) / 8) | 1;
     bp.nps = P > 1 ? units : 0;
-    bp.lds = (size_t)M * ngmax * 256 + (size_t)ngmax * 32 + (size_t)bp.nps * 512 +
+    bp.lds = (size_t)M * ngmax * 256 + (size_t)ngmax * kXsRows * 4 + (size_t)bp.nps * 1024 +
              (size_t)(kBalSml ? nw : 0) * 2 * 16 * bp.nblp * 16;
     if (bp.lds < kBalOwnCu) bp.lds = kBalOwnCu;
     return bp;

@@ -24,7 +24,8 @@ namespace q4g128 {
 #define Q4G128_STAGE 16
 #endif
 
-constexpr int kMaxM = 8;
+constexpr int kMaxM = 16;                  // rows of one MFMA tile
+constexpr int kSkMaxM = 8;                 // the stream-K kernel keeps 8 rows
 // Waves per workgroup (they share one LDS copy of x): few for small M, where
 // x is small and finer workgroups spread more evenly over the CUs; more for
 // large M, whose x would not fit in LDS once per small workgroup.
@@ -67,7 +68,7 @@ constexpr int kBalRing = Q4G128_BAL_RING;   // groups of codes in flight per wav
 #endif
 constexpr bool kBalSml = Q4G128_BAL_SML;    // scales/minimums staged in LDS per tile (else loaded per block)
 constexpr int kBalThreads = 64 * kBalWaves;
-constexpr int kBalStage = 8;                // x pieces per thread: M * ng * 16 <= 6144 (M = 8 at K = 6144)
+constexpr int kBalStage = 8;                // x pieces per thread: M * ng * 16 <= 6144 (M = 8 at K = 6144, 9 at 5120)
 constexpr int kBalSmRounds = 2;             // scale/min pieces per lane: 16 * nblk <= 128, nblk <= 8
 constexpr size_t kBalOwnCu = 80 * 1024 + 1024;   // LDS request that keeps two workgroups off one CU
 constexpr int kBalMinTiles = 8;             // fewer tiles per workgroup: cut each tile's K into parts

@@ -23,10 +23,15 @@ __device__ __forceinline__ float bf16_at(const u32x4 &v, int j)
 }
 
 // x in LDS: row r of the staged range holds its 16-byte blocks (8 bf16 in
-// pair order) with block index b stored at b ^ (r & 7).  Lanes of one row
-// block read 8 different rows at the same block index; the XOR spreads them
-// over 8 different 16-byte bank groups, without padding rows.
-__device__ __forceinline__ int swz(int blk, int row) { return blk ^ (row & 7); }
+// pair order) with block index b stored at b ^ (r & 15) (the XOR stays
+// inside the group's 16 blocks).  The 16 lanes of one row block read up to
+// 16 different rows at the same block index; the XOR spreads them over 16
+// different 16-byte bank groups, without padding rows.
+__device__ __forceinline__ int swz(int blk, int row) { return blk ^ (row & 15); }
+
+// Row-sum slots per staged group: Xs[g][row], one per MFMA row (M <= 16);
+// rows >= M are never written and their results never stored.
+constexpr int kXsRows = 16;
 
 // Sum of a float over each row of 16 lanes, by a fixed tree; lane 15 of the
 // row ends with the total.
@@ -90,7 +95,7 @@ struct XStage {
                 part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, part, false);
                 part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, part, false);
                 const float tot = row16_sum(part);
-                if ((tid & 15) == 15 && pu < pieces) Xs[(blk >> 4) * 8 + row] = tot;
+                if ((tid & 15) == 15 && pu < pieces) Xs[(blk >> 4) * kXsRows + row] = tot;
             }
         }
     }

@@ -119,7 +119,7 @@ __device__ __forceinline__ void sk_block(SkWave &w, const uint16_t *rbase, const
         u32x4 a[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u32x4 *>(gp + aoff[t]);
-        const f32x4 xsum = *reinterpret_cast<const f32x4 *>(xrow + lg * 8);
+        const f32x4 xsum = *reinterpret_cast<const f32x4 *>(xrow + lg * kXsRows);
         u32x4 bq[4];
         bq[0] = unpack_biased(w.cb[q].x, uc);
         bq[1] = unpack_biased(w.cb[q].y, uc);
@@ -318,7 +318,7 @@ bool streamk_plan(int K, int N, int ncu, SkShape *p)
 size_t streamk_lds_bytes(const SkShape &p, int M)
 {
     const int nbmax = (p.nb + p.SK - 1) / p.SK;
-    const size_t need = (size_t)M * nbmax * 1024 * 2 + (size_t)nbmax * 8 * 8 * 4;
+    const size_t need = (size_t)M * nbmax * 1024 * 2 + (size_t)nbmax * 8 * kXsRows * 4;
     // More than half of the 160 KB LDS of a CU, so no two workgroups share one.
     const size_t own_cu = 80 * 1024 + 1024;
     return need > own_cu ? need : own_cu;

@@ -45,7 +45,7 @@ def test_version_and_status_strings(L):
 def test_workspace_bytes(L):
     assert q.q4g128_splitk_workspace_bytes(1, 5120, 7) == 7 * 5120 * 4
     assert q.q4g128_splitk_workspace_bytes(8, 34816, 2) == 2 * 8 * 34816 * 4
-    for bad in ((0, 10, 2), (9, 10, 2), (1, 0, 2), (1, 10, 0)):
+    for bad in ((0, 10, 2), (17, 10, 2), (1, 0, 2), (1, 10, 0)):
         assert q.q4g128_splitk_workspace_bytes(*bad) == 0
 
 
@@ -71,7 +71,7 @@ def call_gemm(L, x=FAKE, M=1, K=256, W=FAKE, s=FAKE, m=FAKE, N=16, y=FAKE):
 
 @pytest.mark.parametrize("kw", [
     dict(x=None), dict(W=None), dict(s=None), dict(m=None), dict(y=None),
-    dict(M=0), dict(M=9), dict(K=0), dict(K=100), dict(K=-128), dict(N=0),
+    dict(M=0), dict(M=17), dict(K=0), dict(K=100), dict(K=-128), dict(N=0),
     dict(x=FAKE + 8), dict(W=FAKE + 4), dict(s=FAKE + 1), dict(y=FAKE + 2),
 ])
 def test_gemm_rejects(L, kw):
@@ -135,7 +135,7 @@ def test_streamk_rejects(L):
     assert f(*ok, FAKE + 16, need, None) == q.Q4G128_EINVAL              # not 256-byte aligned
     assert f(*ok, FAKE, need - 4, None) == q.Q4G128_EWORKSPACE
     assert f(FAKE, 1, 2048, FAKE, FAKE + 2, FAKE, 16, FAKE, FAKE, need, None) == q.Q4G128_EINVAL   # scale not 16-aligned
-    assert f(FAKE, 9, 2048, FAKE, FAKE, FAKE, 16, FAKE, FAKE, need, None) == q.Q4G128_EINVAL
+    assert f(FAKE, 9, 2048, FAKE, FAKE, FAKE, 16, FAKE, FAKE, need, None) == q.Q4G128_EINVAL   # stream-K: M <= 8
 
 
 def test_quantize_rejects(L):

@@ -67,7 +67,8 @@ def misaligned(t: torch.Tensor) -> torch.Tensor:
 
 SWIGLU_CASES = [("gateup", None, None, None, None), ("verify", None, None, None, None),
                 (None, 3, 2048, 200, 81), (None, 1, 1024, 34, 82), (None, 2, 1024, 2, 83),
-                (None, 8, 640, 100, 84), (None, 5, 8192, 778, 85), (None, 1, 17408, 2 * 1000, 86)]
+                (None, 8, 640, 100, 84), (None, 5, 8192, 778, 85), (None, 1, 17408, 2 * 1000, 86),
+                (None, 9, 5120, 34816, 87), (None, 16, 2048, 2 * 1000, 88)]
 
 
 def swiglu_case(name, M, K, N, seed):
@@ -137,7 +138,8 @@ def rms_tolerance(y_ref, a_ref, r, gamma_bits, eps, out_ref):
 
 RMS_CASES = [("down", None, None, None, None, None), ("down", None, None, None, None, 1),
              (None, 3, 6144, 5120, 95, None), (None, 2, 1024, 1000, 96, None), (None, 1, 2048, 20000, 97, None),
-             (None, 8, 1024, 300, 98, None), (None, 1, 128, 1, 99, None)]
+             (None, 8, 1024, 300, 98, None), (None, 1, 128, 1, 99, None), (None, 16, 17408, 5120, 100, None),
+             (None, 9, 6144, 5120, 101, None)]
 
 
 def rms_case(name, M, K, N, seed):

@@ -4,7 +4,7 @@
 * one-hot activations select single weights (ties the product's unpack to
   the oracle's);
 * every workload within |y - y_ref| <= 1e-3 * sum|x*w| + 1e-6;
-* rows of an M-row call bit-identical to one-row calls, M = 1..8;
+* rows of an M-row call bit-identical to one-row calls, M = 1..16;
 * split-K deterministic run to run and across streams;
 * y(2x) = 2 y(x) exactly;
 * ragged and extreme shapes.
@@ -196,7 +196,7 @@ def test_invalid_arguments_are_rejected_before_launch():
         q.q4g128_gemm_splitk(x, W, s, m, splits=2)      # K=256 is one block of 1024 k
     assert e.value.status == q.Q4G128_EINVAL
     with pytest.raises(q.Q4G128Error) as e:
-        q.q4g128_gemm(dev_x(np.zeros((9, 256), np.uint16)), W, s, m)
+        q.q4g128_gemm(dev_x(np.zeros((17, 256), np.uint16)), W, s, m)
     assert e.value.status == q.Q4G128_EINVAL
     big = synth.make_random(1, 2048, 8, 6)
     ws = torch.empty(4, dtype=torch.float32, device=DEV)
@@ -220,6 +220,37 @@ def test_rows_bit_identical_across_kernel_choice(K, N):
     for M in range(1, 8):
         yM = host_f32(q.q4g128_gemm(x8[:M].contiguous(), W, s, m))
         assert np.array_equal(bits(yM), bits(y8[:M])), M
+
+
+# Verify wider than 8 rows (a draft of up to 15 tokens plus the next one):
+# rows of every M up to 16 equal the 16-row call's.  At K = 5120, N = 34816
+# the balanced kernel takes M <= 9 and the per-tile kernel M >= 10; at K =
+# 2048, N = 1001 the balanced kernel cuts K into parts for every M (x for 16
+# rows fits); 17408 -> 5120 runs split-K; 6144 -> 5120 the per-tile kernel.
+@pytest.mark.parametrize("K,N,split", [(5120, 34816, False), (2048, 1001, False), (17408, 5120, True),
+                                       (6144, 5120, False)])
+def test_rows_bit_identical_up_to_16_rows(K, N, split):
+    case = synth.make_random(16, K, N, 60 + K // 1024, outlier_frac=0.01)
+    W, s, m = dev_weights(case.weights)
+    x16 = dev_x(case.x)
+    f = q.q4g128_gemm_splitk if split else q.q4g128_gemm
+    y16 = host_f32(f(x16, W, s, m))
+    for M in (1, 2, 5, 8, 9, 10, 12, 15):
+        yM = host_f32(f(x16[:M].contiguous(), W, s, m))
+        assert np.array_equal(bits(yM), bits(y16[:M])), M
+
+
+@pytest.mark.parametrize("M,K,N", [(9, 5120, 34816), (16, 5120, 34816), (9, 17408, 5120), (16, 2048, 1001),
+                                   (13, 1024, 17), (16, 640, 100)])
+def test_wide_verify_within_tolerance(orc, M, K, N):
+    case = synth.make_random(M, K, N, 70 + M, outlier_frac=0.01)
+    wt = case.weights
+    y_ref, a_ref = orc.gemm(case.x, wt.W, wt.scale, wt.mn)
+    x = dev_x(case.x)
+    W, s, m = dev_weights(wt)
+    r1 = assert_within_tolerance(host_f32(q.q4g128_gemm(x, W, s, m)), y_ref, a_ref, f"M={M} K={K} N={N}")
+    r2 = assert_within_tolerance(host_f32(q.q4g128_gemm_splitk(x, W, s, m)), y_ref, a_ref, f"split M={M}")
+    print(f"M={M} K={K} N={N}: worst |err|/tol {r1:.2e} / split-K {r2:.2e}")
 
 
 # Column sharing of the balanced kernel: N not a multiple of 8, fewer than 8

@@ -100,6 +100,10 @@ def test_power_of_two_scaling_is_exact():
 
 
 def test_unsupported_and_invalid_arguments():
+    wide = synth.make_random(9, 1024, 16, 5)         # stream-K keeps M <= 8
+    with pytest.raises(q.Q4G128Error) as e:
+        q.q4g128_gemm_streamk(dev_x(wide.x), *dev_weights(wide.weights))
+    assert e.value.status == q.Q4G128_EINVAL
     case = synth.make_random(1, 640, 8, 5)           # K not a multiple of 1024
     with pytest.raises(ValueError):
         q.q4g128_gemm_streamk(dev_x(case.x), *dev_weights(case.weights))
