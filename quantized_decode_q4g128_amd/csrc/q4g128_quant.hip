@@ -25,7 +25,9 @@
 // consecutive 256-byte pieces of memory, group index n*G + g).  The first
 // thread of each group scans the candidates' errors in order, then writes
 // 16 code words, scale, minimum and the error.  The work is fp64 ALU bound
-// (a correctly rounded fp64 divide per code per candidate).
+// (per code per candidate: a subtract, a multiply by the reciprocal of the
+// scale and the rounding, with a correctly rounded divide only next to a
+// half-integer).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -71,11 +73,23 @@ __device__ Cand candidate(double lo, double hi, int bi, int bj)
     return r;
 }
 
-__device__ __forceinline__ double code_of(double v, double sd, double md)
+// clamp(rint((v - md) / sd), 0, 15), 0 if sd == 0, with the quotient
+// rounded exactly as a correctly rounded fp64 divide would give it.  The
+// quotient is first formed as (v - md) * rs with rs = fl(1 / sd): two
+// roundings, so it lies within 1.5 * 2^-52 |t| of the divided one, whose
+// own error is 2^-53 |t|.  rint of the two can differ only if a half-integer
+// lies within that distance; when the product is within 2^-50 |t| of one,
+// the divide itself decides.  (t - rint(t) is exact for |t| < 2^52; larger
+// quotients clamp to 0 or 15 either way.)
+__device__ __forceinline__ double code_of(double v, double sd, double md, double rs)
 {
 #pragma clang fp contract(off)
     if (sd == 0.0) return 0.0;
-    double q = __builtin_rint((v - md) / sd);
+    const double d = v - md;
+    const double t = d * rs;
+    double q = __builtin_rint(t);
+    const double near_half = __builtin_fabs(__builtin_fabs(t - q) - 0.5);
+    if (near_half <= 0x1p-50 * __builtin_fabs(t)) q = __builtin_rint(d / sd);
     q = q < 0.0 ? 0.0 : q;
     return q > 15.0 ? 15.0 : q;
 }
@@ -121,10 +135,11 @@ __global__ __launch_bounds__(kQThreads) void quantize_q4g128(const uint16_t *__r
         if (!bad) {
             cd = candidate(lo, hi, cand / ncand, cand % ncand);
             const double sd = f64_of_bf16(cd.s16), md = f64_of_bf16(cd.m16);
+            const double rs = sd != 0.0 ? 1.0 / sd : 0.0;
             e = 0.0;
             for (int k = 0; k < 128; ++k) {
                 const double x = f64_of_bf16(v[k]);
-                const double r = (code_of(x, sd, md) * sd + md) - x;
+                const double r = (code_of(x, sd, md, rs) * sd + md) - x;
                 e = e + r * r;
             }
         }
@@ -156,13 +171,14 @@ __global__ __launch_bounds__(kQThreads) void quantize_q4g128(const uint16_t *__r
     const uint32_t sm = sms[gl * nc2 + bi];
     const uint16_t s16 = (uint16_t)(sm & 0xFFFFu), m16 = (uint16_t)(sm >> 16);
     const double sd = f64_of_bf16(s16), md = f64_of_bf16(m16);
+    const double rs = sd != 0.0 ? 1.0 / sd : 0.0;
     for (int j = 0; j < 4; ++j) {
         uint32_t word[4];
         for (int t = 0; t < 4; ++t) {
             uint32_t wd = 0;
             for (int i = 0; i < 8; ++i) {
                 const int k = 32 * j + 8 * t + i;
-                wd |= (uint32_t)code_of(f64_of_bf16(v[k]), sd, md) << (4 * i);
+                wd |= (uint32_t)code_of(f64_of_bf16(v[k]), sd, md, rs) << (4 * i);
             }
             word[t] = wd;
         }

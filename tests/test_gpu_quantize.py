@@ -56,6 +56,10 @@ def special_groups():
     o = rng.standard_normal(128) * 0.01; o[9] = -3.0; o[77] = 2.0; rows.append(o)
     t = np.linspace(-1, 1, 128); rows.append(t)                       # evenly spread
     rows.append(np.where(np.arange(128) % 2 == 0, 1.0, -1.0))         # two values
+    h = (np.arange(128) % 31) * 2.0 ** -5                              # half steps of 1/16 over [0, 15/16]:
+    h[0], h[1] = 0.0, 15.0 / 16.0                                      # exact ties at every odd multiple
+    rows.append(h)
+    rows.append(-3.0 + h * 4.0)                                        # the same ties, shifted and scaled
     return synth.to_bf16_bits(np.concatenate(rows)[None, :])
 
 
