@@ -67,7 +67,13 @@ int device_cus()
 struct BalChoice {
     int gx;
     int P;
+    int rows;       // rows per launch: M, or kBalRowBlock for K-part shapes at M > kBalRowBlock
 };
+
+// K-part shapes stage x for at most this many rows per launch; wider calls
+// run as several launches over blocks of rows (each row's sums do not depend
+// on the other rows of its launch).
+constexpr int kBalRowBlock = 8;
 
 // Tiles of 16 columns a workgroup gets when N is shared out in units of 8.
 int bal_tiles(int N, int gx)
@@ -102,7 +108,7 @@ bool bal_fits(int M, int K, int N, int gx, int P, bool act)
 
 BalChoice plan_bal(int M, int K, int N, int S, const void *scale, const void *min, bool act = false)
 {
-    BalChoice no = {0, 1};
+    BalChoice no = {0, 1, M};
     // One K split only: with several, fewer workgroups per split leave some
     // CUs a larger share than the per-tile kernel does.
     if (S != 1) return no;
@@ -116,9 +122,10 @@ BalChoice plan_bal(int M, int K, int N, int S, const void *scale, const void *mi
     const int gx = ncu < N8 ? ncu : N8;
     const int P = bal_parts(K, N, gx);
     // With P > 1 the sums differ in rounding from the per-tile kernel's, so a
-    // shape takes this path for every M or for none: x is checked at M = 16.
-    if (!bal_fits(P > 1 ? Q4G128_MAX_M : M, K, N, gx, P, act)) return no;
-    BalChoice c = {gx, P};
+    // shape takes this path for every M or for none: x is checked for a block
+    // of kBalRowBlock rows, and wider calls go block by block.
+    if (!bal_fits(P > 1 ? kBalRowBlock : M, K, N, gx, P, act)) return no;
+    BalChoice c = {gx, P, P > 1 && M > kBalRowBlock ? kBalRowBlock : M};
     return c;
 }
 
@@ -136,8 +143,17 @@ q4g128_status run_gemv(const void *x, int M, int K, const uint32_t *W, const voi
     a.out = out;
     a.S = S;
     const BalChoice bc = plan_bal(M, K, N, S, scale, min);
-    hipError_t e = bc.gx > 0 ? q4g128::launch_gemv_bal(a, bc.gx, bc.P, stream)
-                             : q4g128::launch_gemv(a, plan_tiles_per_wave(K, N), stream);
+    hipError_t e = hipSuccess;
+    if (bc.gx > 0) {
+        for (int r0 = 0; r0 < M && e == hipSuccess; r0 += bc.rows) {      // S == 1: y rows are contiguous
+            a.x = static_cast<const uint16_t *>(x) + (size_t)r0 * K;
+            a.M = M - r0 < bc.rows ? M - r0 : bc.rows;
+            a.out = out + (size_t)r0 * N;
+            e = q4g128::launch_gemv_bal(a, bc.gx, bc.P, stream);
+        }
+    } else {
+        e = q4g128::launch_gemv(a, plan_tiles_per_wave(K, N), stream);
+    }
     if (e != hipSuccess) {
         set_error("gemv launch", e);
         return Q4G128_EHIP;
@@ -164,8 +180,13 @@ q4g128_status run_swiglu(const void *x, int M, int K, const uint32_t *W, const v
         a.N = N;
         a.out = nullptr;
         a.S = 1;
-        a.act = act;
-        hipError_t e = q4g128::launch_gemv_bal(a, bc.gx, bc.P, stream);
+        hipError_t e = hipSuccess;
+        for (int r0 = 0; r0 < M && e == hipSuccess; r0 += bc.rows) {
+            a.x = static_cast<const uint16_t *>(x) + (size_t)r0 * K;
+            a.M = M - r0 < bc.rows ? M - r0 : bc.rows;
+            a.act = act + (size_t)r0 * (N / 2);
+            e = q4g128::launch_gemv_bal(a, bc.gx, bc.P, stream);
+        }
         if (e != hipSuccess) {
             set_error("gemv+swiglu launch", e);
             return Q4G128_EHIP;
@@ -222,14 +243,15 @@ int q4g128_splitk_default_splits(int K, int N)
     if (K <= 0 || K % Q4G128_GROUP != 0 || N <= 0 || K > kMaxK || N > kMaxN) return 0;
     // No K splits where the balanced kernel spreads the shape over every CU:
     // with whole tiles when x for one row fits it (wider M falls back to the
-    // per-tile kernel, which then has enough tiles), and with K parts only if
-    // x for 16 rows fits (such shapes take it for every M or not at all).
+    // per-tile kernel, which then has enough tiles), and with K parts when x
+    // for a block of kBalRowBlock rows fits (such shapes take it for every M,
+    // block by block, or not at all).
     const int ncu = device_cus();
     if (K % 1024 == 0 && ncu > 0) {
         const int N8 = (N + 7) / 8;
         const int gx = ncu < N8 ? ncu : N8;
         const int P = bal_parts(K, N, gx);
-        if (bal_fits(P > 1 ? Q4G128_MAX_M : 1, K, N, gx, P, false)) return 1;
+        if (bal_fits(P > 1 ? kBalRowBlock : 1, K, N, gx, P, false)) return 1;
     }
     const long nb = max_splits(K);
     const long tpw = plan_tiles_per_wave(K, N);
