@@ -333,9 +333,10 @@ __device__ __forceinline__ uint16_t swiglu_bf16(float g, float u)
 // same number of bytes (Token Rush README, bandwidth paragraph: decode is
 // bound by streaming the weights).  Here the grid is gx workgroups per K split,
 // at most one per CU (the LDS request is sized so two never share a CU), and
-// workgroup c of a split owns the tiles [c*T/gx, (c+1)*T/gx): 8 or 9 tiles
-// each for the 2176 tiles of N = 34816 on 256 CUs.  Each of up to 16 waves
-// takes one tile at a time.  x is staged once per workgroup; each wave copies
+// workgroup c owns an equal share of the columns, dealt in units of 8 (136
+// for N = 34816 on 256 CUs), cut into the fewest tiles of at most 16 columns,
+// all of (nearly) equal width.  Each of 12 waves takes one tile at a time.
+// x is staged once per workgroup; each wave copies
 // its tile's scales and minimums into its own LDS area with 16-byte loads of
 // consecutive pieces, so the main loop streams nothing but codes.  The
 // per-column instructions are those of gemv_q4g128, so results are the same
@@ -477,15 +478,24 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     // mix of larger and smaller shares.
     const int c = (gx % 8 == 0) ? (int)(blockIdx.x % 8) * (gx / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
     // Columns [n0, n1), cut in units of 8 so every CU streams the same bytes to
-    // within 8 columns (N = 34816 on 256 CUs: 136 each, 8 tiles of 16 + 1 of 8);
+    // within 8 columns (N = 34816 on 256 CUs: 136 each, 9 tiles of 15-16);
     // ACT: pair-columns of I = N/2 in units of 4 (68 pairs each).
     const int NC = ACT ? (N >> 1) : N;
     const int CU = ACT ? 4 : 8;
     const int NU = (NC + CU - 1) / CU;
     const int n0 = (int)((long)c * NU / gx) * CU;
     const int n1 = min((int)((long)(c + 1) * NU / gx) * CU, NC);
-    const int TW = ACT ? 8 : 16;                          // columns (ACT: pairs) per tile
-    const int nchunk = (n1 - n0 + TW - 1) / TW;
+    // Tiles of at most TW columns (ACT: pairs), as few as that allows, of
+    // equal widths: tile k covers [n0 + k*width/nchunk, n0 + (k+1)*width/nchunk).
+    // (136 columns make 9 tiles of 15-16 columns rather than 8 of 16 and one
+    // of 8: every wave then streams the same bytes.)
+    const int TW = ACT ? 8 : 16;
+    const int width = n1 - n0;
+    const int nchunk = (width + TW - 1) / TW;
+    auto tile = [&](int k, int &cb, int &cw) {
+        cb = n0 + (k * width) / nchunk;
+        cw = n0 + ((k + 1) * width) / nchunk - cb;
+    };
     const int nunit = PARTS ? nchunk * P : nchunk;        // (tile, part) units
     const bool active = wave < nunit;                     // wave-uniform
 
@@ -514,8 +524,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     auto unit = [&](int u, int &cb, int &cw, int &cs, int &ce) {
         const int k = PARTS ? u / P : u;
         const int p = PARTS ? u - k * P : 0;
-        cb = n0 + TW * k;
-        cw = min(TW, n1 - cb);
+        tile(k, cb, cw);
         cs = PARTS ? gs + 2 * ((p * (ng >> 1)) / P) : gs;
         ce = PARTS ? gs + 2 * (((p + 1) * (ng >> 1)) / P) : ge;
     };
@@ -553,16 +562,17 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     if (PARTS) {
         lds_barrier();                                    // every wave, with or without a unit
         for (int k = wave; k < nchunk; k += kBalWaves) {
-            const int cb = n0 + TW * k;
+            int cb, cw;
+            tile(k, cb, cw);
             f32x4 v = *reinterpret_cast<const f32x4 *>(slots + (k * P) * 256 + lane * 4);
             for (int p = 1; p < P; ++p) v += *reinterpret_cast<const f32x4 *>(slots + (k * P + p) * 256 + lane * 4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) B.acc[0][r] = v[r];
             if (ACT) {                                    // all lanes: the pair exchange is a shuffle
-                B.wact = min(TW, n1 - cb);
+                B.wact = cw;
                 B.store_act(act, cb);
             } else {
-                B.ncols = min(16, n1 - cb);
+                B.ncols = cw;
                 B.store(ry, N, cb);
             }
         }
@@ -820,7 +830,7 @@ BalPlan bal_plan(int M, int K, int N, int S, int gx, int P, bool act)
     int tiles;                                                  // most tiles of one workgroup
     if (act) {
         const int NU = (N / 2 + 3) / 4;
-        tiles = ((NU + gx - 1) / gx * 4 + 7) / 8;               // tiles of 8 gate/up pairs
+        tiles = ((NU + gx - 1) / gx * 4 + 7) / 8;               // tiles of at most 8 gate/up pairs
     } else {
         const int N8 = (N + 7) / 8;
         tiles = ((N8 + gx - 1) / gx * 8 + 15) / 16;
