@@ -781,10 +781,10 @@ template <int TPW, bool CHUNKED, bool VSM, int WAVES>
 static void launch_one(const GemvArgs &a, dim3 grid, int cg, hipStream_t stream)
 {
     // x for up to 16 rows of a chunk can pass 64 KiB (66.5 KiB at M = 16):
-    // allow the kernel the CU's whole LDS once.
-    static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_q4g128<TPW, CHUNKED, VSM, kRingDepth, WAVES>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBalMaxLds);
+    // allow the kernel the CU's whole LDS.
+    static LdsFlags done;
+    const hipError_t attr = allow_dynamic_lds(
+        reinterpret_cast<const void *>(&gemv_q4g128<TPW, CHUNKED, VSM, kRingDepth, WAVES>), (int)kBalMaxLds, done);
     (void)attr;                                  // a failure shows up as the launch's error
     const size_t lds = (size_t)a.M * (size_t)cg * 128 * 2 + (size_t)cg * kXsRows * 4;
     hipLaunchKernelGGL((gemv_q4g128<TPW, CHUNKED, VSM, kRingDepth, WAVES>), grid, dim3(64 * WAVES, 1, 1), lds,
@@ -849,9 +849,9 @@ BalPlan bal_plan(int M, int K, int N, int S, int gx, int P, bool act)
 template <bool PARTS, bool ACT>
 static hipError_t launch_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)
 {
-    static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    static LdsFlags done;
+    const hipError_t attr = allow_dynamic_lds(
+        reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT>), (int)kBalMaxLds, done);
     if (attr != hipSuccess) return attr;
     BalPlan bp = bal_plan(a.M, a.K, a.N, a.S, gx, P, ACT);
     hipLaunchKernelGGL((gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT>), dim3((unsigned)gx, (unsigned)a.S, 1),

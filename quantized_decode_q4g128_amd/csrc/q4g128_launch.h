@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace q4g128 {
 
 #ifndef Q4G128_WAVES_SMALL
@@ -23,6 +25,23 @@ namespace q4g128 {
 #ifndef Q4G128_STAGE
 #define Q4G128_STAGE 16
 #endif
+
+// Dynamic LDS above 64 KiB has to be allowed per kernel and per device; each
+// call site keeps one flag per device so the attribute is set once on each.
+constexpr int kMaxDevices = 64;
+typedef std::atomic<bool> LdsFlags[kMaxDevices];
+
+inline hipError_t allow_dynamic_lds(const void *kernel, int bytes, LdsFlags &done)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool cached = dev >= 0 && dev < kMaxDevices;
+    if (cached && done[dev].load(std::memory_order_relaxed)) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && cached) done[dev].store(true, std::memory_order_relaxed);
+    return e;
+}
 
 constexpr int kMaxM = 16;                  // rows of one MFMA tile
 constexpr int kSkMaxM = 8;                 // the stream-K kernel keeps 8 rows

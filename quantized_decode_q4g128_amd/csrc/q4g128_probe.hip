@@ -138,9 +138,15 @@ int q4g128_probe_tile_read(const uint32_t *W, int K, int N, uint32_t *sink, void
     const int gx = ncu < N8 ? ncu : N8;
     // The product's LDS request (over half the CU's 160 KB) keeps two
     // workgroups off one CU; the probe asks for the same.
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&probe_tile_read),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kOwnCuLds);
-    if (attr != hipSuccess) return (int)attr;
+    static bool done[64];                        // per device: the attribute is set once on each
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return (int)hipErrorInvalidDevice;
+    if (!done[dev]) {
+        const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&probe_tile_read),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, kOwnCuLds);
+        if (attr != hipSuccess) return (int)attr;
+        done[dev] = true;
+    }
     hipLaunchKernelGGL(probe_tile_read, dim3((unsigned)gx), dim3(64 * kTileWaves), kOwnCuLds,
                        static_cast<hipStream_t>(stream), W, K, N, sink);
     return (int)hipGetLastError();
