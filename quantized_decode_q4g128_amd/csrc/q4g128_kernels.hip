@@ -224,7 +224,8 @@ struct Tile {
 // multiple of 16), each chunk staged, primed and drained on its own.  Both
 // accumulate the same groups in the same order with the same instructions, so
 // they give identical bits.
-// A chunk of 16 groups of x for 8 rows must fit the staging registers.
+// A chunk of 16 groups of x must fit the staging registers: for M <= kSmallM
+// rows with the small workgroups, for 16 rows with the large ones.
 static_assert(kStageMax * 64 * kWavesSmall >= kSmallM * 16 * 16, "x staging cannot hold one 16-group chunk");
 static_assert(kStageMax * 64 * kWavesLarge >= kMaxM * 16 * 16, "x staging cannot hold one 16-group chunk at M = 16");
 
