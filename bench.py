@@ -662,7 +662,7 @@ def trace_summarize(trace_dir, out, command):
     rows = {}
     with open(files[0]) as f:
         for r in csv.DictReader(f):
-            name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
             key = (name, int(r["LDS_Block_Size"]), int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]),
                    int(r["Workgroup_Size_X"]))
             rows.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
