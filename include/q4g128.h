@@ -87,6 +87,12 @@ size_t q4g128_splitk_workspace_bytes(int M, int N, int splits);
  * invalid K or N. */
 int q4g128_splitk_default_splits(int K, int N);
 
+/* K parts of q4g128_gemm's one-launch form for a (K, N) shape on the
+ * current device (1 if that form does not cut K): q4g128_gemm_splitk with
+ * this many splits gives the bits of q4g128_gemm, for every M.  A function
+ * of K, N and the compute-unit count; 0 for invalid K or N. */
+int q4g128_gemm_parts(int K, int N);
+
 /* The product with K cut into `splits` contiguous ranges of whole blocks of
  * 8 groups (1024 k): with nb = ceil(K/1024) blocks, split s covers blocks
  * [s*nb/splits, (s+1)*nb/splits), so 1 <= splits <= nb.  Each
@@ -130,9 +136,10 @@ q4g128_status q4g128_gemm_streamk(const void *x, int M, int K,
                                   void *stream);
 
 /* Bytes of workspace q4g128_gemm_swiglu needs for (M, K, N):
- * splits * M * N * 4 with splits = q4g128_splitk_default_splits(K, N) (the
- * partial sums of the shapes the fused launch cannot take).  Returns 0 for
- * invalid arguments (N must be even). */
+ * splits * M * N * 4, splits the larger of q4g128_splitk_default_splits(K, N)
+ * and the fused launch's K-part count (the partial sums of the calls the
+ * fused launch cannot take).  Returns 0 for invalid arguments (N must be
+ * even). */
 size_t q4g128_swiglu_workspace_bytes(int M, int K, int N);
 
 /* The product on a fused gate/up matrix followed by the SwiGLU activation:

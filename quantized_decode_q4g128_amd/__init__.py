@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.q4g128_quantize.restype = ci
         L.q4g128_splitk_workspace_bytes.argtypes = [ci, ci, ci]
         L.q4g128_splitk_workspace_bytes.restype = sz
+        L.q4g128_gemm_parts.argtypes = [ci, ci]
+        L.q4g128_gemm_parts.restype = ci
         L.q4g128_splitk_default_splits.argtypes = [ci, ci]
         L.q4g128_splitk_default_splits.restype = ci
         L.q4g128_status_string.argtypes = [ci]
@@ -96,6 +98,11 @@ def q4g128_splitk_workspace_bytes(M: int, N: int, splits: int) -> int:
 
 def q4g128_splitk_default_splits(K: int, N: int) -> int:
     return int(lib().q4g128_splitk_default_splits(int(K), int(N)))
+
+
+def q4g128_gemm_parts(K: int, N: int) -> int:
+    """Split count whose q4g128_gemm_splitk bits equal q4g128_gemm's (1: no cut)."""
+    return int(lib().q4g128_gemm_parts(int(K), int(N)))
 
 
 # ---- marshalling helpers -----------------------------------------------------
@@ -332,5 +339,5 @@ def q4g128_quantize(w, ncand: int = 9, W=None, scale=None, min=None, err=None, s
 __all__ = ["q4g128_gemm", "q4g128_quantize", "q4g128_gemm_swiglu", "q4g128_swiglu_workspace_bytes",
            "q4g128_gemm_rmsnorm", "q4g128_gemm_splitk", "q4g128_gemm_streamk", "q4g128_streamk_workspace",
            "q4g128_streamk_workspace_bytes", "q4g128_dequant", "q4g128_splitk_workspace_bytes",
-           "q4g128_splitk_default_splits", "q4g128_status_string", "q4g128_last_error",
+           "q4g128_splitk_default_splits", "q4g128_gemm_parts", "q4g128_status_string", "q4g128_last_error",
            "q4g128_abi_version", "Q4G128Error", "lib", "LIB_PATH"]

@@ -60,26 +60,31 @@ int device_cus()
     return ncu;
 }
 
-// Balanced plan for gemv_q4g128_bal: workgroups per K split (at most one per
-// CU) and K parts per tile, or gx = 0 when the shape needs the per-tile
-// kernel (K not a multiple of 1024, unaligned scale/min, several K splits,
-// x or LDS too large, huge y).
+// Balanced plan for gemv_q4g128_bal (one K split): workgroups (at most one
+// per CU) and K parts per tile, or gx = 0 when the shape needs the per-tile
+// kernel (K not a multiple of 1024, unaligned scale/min, x or LDS too large,
+// huge y).
 struct BalChoice {
     int gx;
     int P;
-    int rows;       // rows per launch: M, or kBalRowBlock for K-part shapes at M > kBalRowBlock
+    int rb;         // P > 1: rows one launch can hold (1..kBalRowBlock); P == 1: M
 };
 
-// K-part shapes stage x for at most this many rows per launch; wider calls
-// run as several launches over blocks of rows (each row's sums do not depend
-// on the other rows of its launch).
+// K-part shapes stage x for at most this many rows per launch.
 constexpr int kBalRowBlock = 8;
 
-// Tiles of 16 columns a workgroup gets when N is shared out in units of 8.
+// Workgroups for N columns (ACT: N/2 pairs) shared out in units of 4.
+int bal_gx(int N, bool act, int ncu)
+{
+    const int units = act ? (N / 2 + 3) / 4 : (N + 3) / 4;
+    return ncu < units ? ncu : units;
+}
+
+// Tiles of at most 16 columns a workgroup gets when N is shared out in units of 4.
 int bal_tiles(int N, int gx)
 {
-    const int N8 = (N + 7) / 8;
-    return ((N8 + gx - 1) / gx * 8 + 15) / 16;
+    const int N4 = (N + 3) / 4;
+    return ((N4 + gx - 1) / gx * 4 + 15) / 16;
 }
 
 // K parts per tile: 1 when a workgroup has enough tiles for its waves, else
@@ -101,36 +106,41 @@ bool bal_fits(int M, int K, int N, int gx, int P, bool act)
     using namespace q4g128;
     const int ng = K / 128;
     if ((long)M * ng * 16 > (long)kBalThreads * kBalStage) return false;       // x staging registers
-    const int part = P > 1 ? 2 * ((ng / 2 + P - 1) / P) : ng;                    // longest part, groups
+    const int part = P > 1 ? (ng / 8 + P - 1) / P * 8 : ng;                     // longest part, groups
     if (16 * ((part + 7) / 8) > 64 * kBalSmRounds) return false;                 // scale/min pieces per lane
     return bal_plan(M, K, N, 1, gx, P, act).lds <= kBalMaxLds;
 }
 
-BalChoice plan_bal(int M, int K, int N, int S, const void *scale, const void *min, bool act = false)
+// With P > 1 the balanced kernel's sums are those of the per-tile kernel with
+// P K splits and the split-order reduce (same block boundaries, same order),
+// so a shape can take either path for any M: one balanced launch when it
+// holds all M rows, else P splits.  With P == 1 both kernels compute every
+// column the same way, so the choice may depend on M freely.
+BalChoice plan_bal(int M, int K, int N, const void *scale, const void *min, bool act = false)
 {
-    BalChoice no = {0, 1, M};
-    // One K split only: with several, fewer workgroups per split leave some
-    // CUs a larger share than the per-tile kernel does.
-    if (S != 1) return no;
+    BalChoice no = {0, 1, 0};
     if (K % 1024 != 0 || !aligned(scale, 16) || !aligned(min, 16)) return no;
     if ((long)M * N * 4 >= (1L << 31)) return no;
     // ACT tiles address gate and up columns N/2 apart through one descriptor.
     if (act && ((long)N / 2 + 8) * (K / 2) >= (1L << 31)) return no;
     const int ncu = device_cus();
     if (ncu < 1) return no;
-    const int N8 = (N + 7) / 8;
-    const int gx = ncu < N8 ? ncu : N8;
-    const int P = bal_parts(K, N, gx);
-    // With P > 1 the sums differ in rounding from the per-tile kernel's, so a
-    // shape takes this path for every M or for none: x is checked for a block
-    // of kBalRowBlock rows, and wider calls go block by block.
-    if (!bal_fits(P > 1 ? kBalRowBlock : M, K, N, gx, P, act)) return no;
-    BalChoice c = {gx, P, P > 1 && M > kBalRowBlock ? kBalRowBlock : M};
+    const int gx = bal_gx(N, act, ncu);
+    const int P = bal_parts(K, N, bal_gx(N, false, ncu));    // from (K, N) alone: the same for ACT
+    if (P == 1) {
+        if (!bal_fits(M, K, N, gx, 1, act)) return no;
+        BalChoice c = {gx, 1, M};
+        return c;
+    }
+    int rb = 0;
+    while (rb < kBalRowBlock && bal_fits(rb + 1, K, N, gx, P, act)) ++rb;
+    if (rb == 0) return no;
+    BalChoice c = {gx, P, rb};
     return c;
 }
 
-q4g128_status run_gemv(const void *x, int M, int K, const uint32_t *W, const void *scale,
-                       const void *min, int N, float *out, int S, hipStream_t stream)
+q4g128::GemvArgs gemv_args(const void *x, int M, int K, const uint32_t *W, const void *scale, const void *min, int N,
+                           float *out, int S)
 {
     q4g128::GemvArgs a;
     a.x = static_cast<const uint16_t *>(x);
@@ -142,12 +152,23 @@ q4g128_status run_gemv(const void *x, int M, int K, const uint32_t *W, const voi
     a.N = N;
     a.out = out;
     a.S = S;
-    const BalChoice bc = plan_bal(M, K, N, S, scale, min);
+    return a;
+}
+
+// S == 1: y[M][N] in `out`, by the balanced kernel (K-part shapes in launches
+// of at most rb rows) or the per-tile kernel.  S > 1: the per-tile kernel's
+// S partial slices [S][M][N] in `out`.
+q4g128_status run_gemv(const void *x, int M, int K, const uint32_t *W, const void *scale,
+                       const void *min, int N, float *out, int S, hipStream_t stream)
+{
+    q4g128::GemvArgs a = gemv_args(x, M, K, W, scale, min, N, out, S);
+    const BalChoice bc = S == 1 ? plan_bal(M, K, N, scale, min) : BalChoice{0, 1, 0};
     hipError_t e = hipSuccess;
     if (bc.gx > 0) {
-        for (int r0 = 0; r0 < M && e == hipSuccess; r0 += bc.rows) {      // S == 1: y rows are contiguous
+        const int rows = bc.P > 1 ? bc.rb : M;
+        for (int r0 = 0; r0 < M && e == hipSuccess; r0 += rows) {        // y rows are contiguous
             a.x = static_cast<const uint16_t *>(x) + (size_t)r0 * K;
-            a.M = M - r0 < bc.rows ? M - r0 : bc.rows;
+            a.M = M - r0 < rows ? M - r0 : rows;
             a.out = out + (size_t)r0 * N;
             e = q4g128::launch_gemv_bal(a, bc.gx, bc.P, stream);
         }
@@ -161,42 +182,68 @@ q4g128_status run_gemv(const void *x, int M, int K, const uint32_t *W, const voi
     return Q4G128_OK;
 }
 
+// The product with K cut into S ranges of whole 8-group blocks.  When S is
+// the shape's K-part count and one balanced launch holds all M rows, that
+// launch writes the summed result to `dst` as a single slice; otherwise the
+// per-tile kernel writes S partial slices to `ws`.  *slices tells which (1:
+// in dst; S: in ws).  Both give the same bits after the split-order sum.
+q4g128_status run_split(const void *x, int M, int K, const uint32_t *W, const void *scale, const void *min,
+                        int N, int S, float *ws, float *dst, int *slices, hipStream_t stream)
+{
+    if (S == 1) {
+        *slices = 1;
+        return run_gemv(x, M, K, W, scale, min, N, dst, 1, stream);
+    }
+    const BalChoice bc = plan_bal(M, K, N, scale, min);
+    if (bc.gx > 0 && bc.P == S && M <= bc.rb) {
+        *slices = 1;
+        q4g128::GemvArgs a = gemv_args(x, M, K, W, scale, min, N, dst, 1);
+        hipError_t e = q4g128::launch_gemv_bal(a, bc.gx, bc.P, stream);
+        if (e != hipSuccess) {
+            set_error("gemv launch", e);
+            return Q4G128_EHIP;
+        }
+        return Q4G128_OK;
+    }
+    *slices = S;
+    return run_gemv(x, M, K, W, scale, min, N, ws, S, stream);
+}
+
 // The fused gate/up product with bf16 silu(gate) * up written to act: one
 // launch of the balanced kernel when the shape allows it, else the product's
 // partial sums into the workspace and sum_swiglu over them.  The per-column
 // sums are the plain product's in both cases, so both give the same bits.
+// K parts of the fused gate/up plan (1 if it has none or the shape takes the
+// per-tile kernel): the split count its fallback must use.
+int swiglu_parts(int K, int N)
+{
+    const int ncu = device_cus();
+    if (K % 1024 != 0 || ncu < 1) return 1;
+    const int P = bal_parts(K, N, bal_gx(N, false, ncu));
+    return P > 1 && bal_fits(1, K, N, bal_gx(N, true, ncu), P, true) ? P : 1;
+}
+
 q4g128_status run_swiglu(const void *x, int M, int K, const uint32_t *W, const void *scale, const void *min,
                          int N, uint16_t *act, float *ws, hipStream_t stream)
 {
-    const BalChoice bc = plan_bal(M, K, N, 1, scale, min, true);
-    if (bc.gx > 0) {
-        q4g128::GemvArgs a;
-        a.x = static_cast<const uint16_t *>(x);
-        a.M = M;
-        a.K = K;
-        a.W = W;
-        a.scale = static_cast<const uint16_t *>(scale);
-        a.mn = static_cast<const uint16_t *>(min);
-        a.N = N;
-        a.out = nullptr;
-        a.S = 1;
-        hipError_t e = hipSuccess;
-        for (int r0 = 0; r0 < M && e == hipSuccess; r0 += bc.rows) {
-            a.x = static_cast<const uint16_t *>(x) + (size_t)r0 * K;
-            a.M = M - r0 < bc.rows ? M - r0 : bc.rows;
-            a.act = act + (size_t)r0 * (N / 2);
-            e = q4g128::launch_gemv_bal(a, bc.gx, bc.P, stream);
-        }
+    const BalChoice bc = plan_bal(M, K, N, scale, min, true);
+    if (bc.gx > 0 && (bc.P == 1 || M <= bc.rb)) {
+        q4g128::GemvArgs a = gemv_args(x, M, K, W, scale, min, N, nullptr, 1);
+        a.act = act;
+        hipError_t e = q4g128::launch_gemv_bal(a, bc.gx, bc.P, stream);
         if (e != hipSuccess) {
             set_error("gemv+swiglu launch", e);
             return Q4G128_EHIP;
         }
         return Q4G128_OK;
     }
-    const int S = q4g128_splitk_default_splits(K, N);
-    q4g128_status rc = run_gemv(x, M, K, W, scale, min, N, ws, S, stream);
+    // A K-part shape too wide for one launch runs as exactly P K splits (the
+    // same bits as its one-launch form); any other shape as the default split.
+    const int S = bc.gx > 0 && bc.P > 1 ? bc.P : q4g128_splitk_default_splits(K, N);
+    int slices = 0;
+    q4g128_status rc = run_split(x, M, K, W, scale, min, N, S, ws, ws, &slices, stream);
     if (rc != Q4G128_OK) return rc;
-    hipError_t e = q4g128::launch_sum_swiglu(ws, S, M, N, act, stream);
+    hipError_t e = q4g128::launch_sum_swiglu(ws, slices, M, N, act, stream);
     if (e != hipSuccess) {
         set_error("swiglu launch", e);
         return Q4G128_EHIP;
@@ -241,15 +288,16 @@ size_t q4g128_splitk_workspace_bytes(int M, int N, int splits)
 int q4g128_splitk_default_splits(int K, int N)
 {
     if (K <= 0 || K % Q4G128_GROUP != 0 || N <= 0 || K > kMaxK || N > kMaxN) return 0;
-    // No K splits where the balanced kernel spreads the shape over every CU:
-    // with whole tiles when x for one row fits it (wider M falls back to the
-    // per-tile kernel, which then has enough tiles), and with K parts when x
-    // for a block of kBalRowBlock rows fits (such shapes take it for every M,
-    // block by block, or not at all).
+    // No splits where the balanced kernel takes the shape in one launch for
+    // the usual M: with whole tiles when x for one row fits (wider M falls
+    // back to the per-tile kernel, which then has enough tiles), with K parts
+    // when one launch holds kBalRowBlock rows.  Short-N shapes whose K-part
+    // launch holds fewer rows (the 17408 -> 5120 down projection: 2) stream
+    // faster as K splits and a reduce: narrow tiles leave each CU fewer bytes
+    // in flight (measured over the whole decode step).
     const int ncu = device_cus();
     if (K % 1024 == 0 && ncu > 0) {
-        const int N8 = (N + 7) / 8;
-        const int gx = ncu < N8 ? ncu : N8;
+        const int gx = bal_gx(N, false, ncu);
         const int P = bal_parts(K, N, gx);
         if (bal_fits(P > 1 ? kBalRowBlock : 1, K, N, gx, P, false)) return 1;
     }
@@ -264,6 +312,16 @@ int q4g128_splitk_default_splits(int K, int N)
     const long widest = (nb + s - 1) / s;
     while (s > 1 && (nb + s - 2) / (s - 1) == widest) --s;
     return (int)s;
+}
+
+int q4g128_gemm_parts(int K, int N)
+{
+    if (K <= 0 || K % Q4G128_GROUP != 0 || N <= 0 || K > kMaxK || N > kMaxN) return 0;
+    const int ncu = device_cus();
+    if (K % 1024 != 0 || ncu < 1) return 1;
+    const int gx = bal_gx(N, false, ncu);
+    const int P = bal_parts(K, N, gx);
+    return P > 1 && bal_fits(1, K, N, gx, P, false) ? P : 1;
 }
 
 q4g128_status q4g128_gemm(const void *x, int M, int K, const uint32_t *W, const void *scale,
@@ -283,8 +341,9 @@ q4g128_status q4g128_gemm_splitk(const void *x, int M, int K, const uint32_t *W,
     if (splits == 1) return run_gemv(x, M, K, W, scale, min, N, y, 1, st);
     if (!workspace || !aligned(workspace, 4)) return Q4G128_EINVAL;
     if (workspace_bytes < q4g128_splitk_workspace_bytes(M, N, splits)) return Q4G128_EWORKSPACE;
-    q4g128_status rc = run_gemv(x, M, K, W, scale, min, N, workspace, splits, st);
-    if (rc != Q4G128_OK) return rc;
+    int slices = 0;
+    q4g128_status rc = run_split(x, M, K, W, scale, min, N, splits, workspace, y, &slices, st);
+    if (rc != Q4G128_OK || slices == 1) return rc;               // one launch wrote y
     hipError_t e = q4g128::launch_splitk_sum(workspace, splits, (size_t)M * (size_t)N, y, st);
     if (e != hipSuccess) {
         set_error("split-K sum launch", e);
@@ -374,7 +433,9 @@ q4g128_status q4g128_quantize(const void *w, int K, int N, int ncand, uint32_t *
 size_t q4g128_swiglu_workspace_bytes(int M, int K, int N)
 {
     if (M < 1 || M > Q4G128_MAX_M || N < 2 || N % 2) return 0;
-    const int S = q4g128_splitk_default_splits(K, N);
+    int S = q4g128_splitk_default_splits(K, N);
+    const int P = swiglu_parts(K, N);
+    if (P > S) S = P;
     if (S < 1) return 0;
     return (size_t)S * (size_t)M * (size_t)N * sizeof(float);
 }
@@ -403,9 +464,10 @@ q4g128_status q4g128_gemm_rmsnorm(const void *x, int M, int K, const uint32_t *W
     if (!workspace || !aligned(workspace, 4)) return Q4G128_EINVAL;
     if (workspace_bytes < q4g128_splitk_workspace_bytes(M, N, splits)) return Q4G128_EWORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    q4g128_status rc = run_gemv(x, M, K, W, scale, min, N, workspace, splits, st);
+    int slices = 0;
+    q4g128_status rc = run_split(x, M, K, W, scale, min, N, splits, workspace, workspace, &slices, st);
     if (rc != Q4G128_OK) return rc;
-    hipError_t e = q4g128::launch_sum_residual_rmsnorm(workspace, splits, M, N, residual,
+    hipError_t e = q4g128::launch_sum_residual_rmsnorm(workspace, slices, M, N, residual,
                                                        static_cast<const uint16_t *>(gamma), eps, h,
                                                        static_cast<uint16_t *>(x_out), st);
     if (e != hipSuccess) {

@@ -447,9 +447,12 @@ struct BalTile : Tile<1, true, RING, SML, PAD> {
 };
 
 // PARTS: a workgroup with few tiles cuts each tile's K range into P parts
-// (one wave each, boundaries at even groups); the parts' fp32 sums go to LDS
-// and, after a barrier, are added in part order, so the result depends on
-// (K, N, P) only.  P comes from (K, N) and the CU count, never from M.
+// (one wave each) at the block boundaries a K split into P splits uses; the
+// parts' fp32 sums go to LDS and, after a barrier, are added in part order.
+// The result depends on (K, N, P) only (P comes from (K, N) and the CU count,
+// never from M), and it is the bits the per-tile kernel gives with P K
+// splits and the split-order reduce: the same groups in the same order per
+// part, the same additions afterwards.
 // ACT: N = 2I is a fused gate/up product.  The workgroup owns pair-columns
 // [n0, n1) of I, cut in units of 4 (the same bytes per CU as the plain cut);
 // a tile holds 8 pairs, gate columns in its first 8 MFMA columns and the
@@ -478,14 +481,13 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     // them XCD by XCD before cutting the column range gives every XCD the same
     // mix of larger and smaller shares.
     const int c = (gx % 8 == 0) ? (int)(blockIdx.x % 8) * (gx / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-    // Columns [n0, n1), cut in units of 8 so every CU streams the same bytes to
-    // within 8 columns (N = 34816 on 256 CUs: 136 each, 9 tiles of 15-16);
-    // ACT: pair-columns of I = N/2 in units of 4 (68 pairs each).
+    // Columns [n0, n1), cut in units of 4 so every CU streams the same bytes to
+    // within 4 columns (N = 34816 on 256 CUs: 136 each, 9 tiles of 15-16;
+    // N = 5120: 20 each); ACT: pair-columns of I = N/2, likewise (68 pairs).
     const int NC = ACT ? (N >> 1) : N;
-    const int CU = ACT ? 4 : 8;
-    const int NU = (NC + CU - 1) / CU;
-    const int n0 = (int)((long)c * NU / gx) * CU;
-    const int n1 = min((int)((long)(c + 1) * NU / gx) * CU, NC);
+    const int NU = (NC + 3) >> 2;
+    const int n0 = (int)((long)c * NU / gx) * 4;
+    const int n1 = min((int)((long)(c + 1) * NU / gx) * 4, NC);
     // Tiles of at most TW columns (ACT: pairs), as few as that allows, of
     // equal widths: tile k covers [n0 + k*width/nchunk, n0 + (k+1)*width/nchunk).
     // (136 columns make 9 tiles of 15-16 columns rather than 8 of 16 and one
@@ -500,7 +502,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     const int nunit = PARTS ? nchunk * P : nchunk;        // (tile, part) units
     const bool active = wave < nunit;                     // wave-uniform
 
-    BalTile<RING, SML, PARTS, ACT> B;
+    BalTile<RING, SML, false, ACT> B;
     B.i = lane & 15;
     B.h = lane >> 4;
     B.la = lane >> 2;
@@ -526,8 +528,10 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
         const int k = PARTS ? u / P : u;
         const int p = PARTS ? u - k * P : 0;
         tile(k, cb, cw);
-        cs = PARTS ? gs + 2 * ((p * (ng >> 1)) / P) : gs;
-        ce = PARTS ? gs + 2 * (((p + 1) * (ng >> 1)) / P) : ge;
+        // Part p: 8-group blocks [p*nbs/P, (p+1)*nbs/P) of the split's nbs,
+        // the same cut as a K split of the per-tile kernel into P splits.
+        cs = PARTS ? gs + ((p * (ng >> 3)) / P) * 8 : gs;
+        ce = PARTS ? gs + (((p + 1) * (ng >> 3)) / P) * 8 : ge;
     };
     XStage<kBalThreads, kBalStage> xst;
     xst.load(x, M, K, gs, ge);
@@ -833,12 +837,12 @@ BalPlan bal_plan(int M, int K, int N, int S, int gx, int P, bool act)
         const int NU = (N / 2 + 3) / 4;
         tiles = ((NU + gx - 1) / gx * 4 + 7) / 8;               // tiles of at most 8 gate/up pairs
     } else {
-        const int N8 = (N + 7) / 8;
-        tiles = ((N8 + gx - 1) / gx * 8 + 15) / 16;
+        const int N4 = (N + 3) / 4;
+        tiles = ((N4 + gx - 1) / gx * 4 + 15) / 16;
     }
     const int units = tiles * P;
     const int nw = units < kBalWaves ? units : kBalWaves;
-    const int pg = P > 1 ? 2 * (((ngmax / 2) + P - 1) / P) : ngmax;   // longest part, in groups
+    const int pg = P > 1 ? (ngmax / 8 + P - 1) / P * 8 : ngmax;        // longest part, in groups
     bp.nblp = ((pg + 7) / 8) | 1;
     bp.nps = P > 1 ? units : 0;
     bp.lds = (size_t)M * ngmax * 256 + (size_t)ngmax * kXsRows * 4 + (size_t)bp.nps * 1024 +

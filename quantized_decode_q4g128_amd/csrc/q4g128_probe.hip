@@ -6,7 +6,7 @@
 //
 //   probe_tile_read    the product's pattern and work split: one
 //                      12-wave workgroup per compute unit owning an equal
-//                      share of the rows (cut in units of 8, workgroups
+//                      share of the rows (cut in units of 4, workgroups
 //                      numbered XCD by XCD), tiles of 16 consecutive rows,
 //                      one tile per wave at a time; per step each lane quad
 //                      reads 64 contiguous bytes (one 128-weight group) of
@@ -44,9 +44,9 @@ __global__ __launch_bounds__(64 * kTileWaves) void probe_tile_read(const uint32_
     const int wave = threadIdx.x >> 6;
     const int gx = gridDim.x;
     const int c = (gx % 8 == 0) ? (int)(blockIdx.x % 8) * (gx / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-    const int N8 = (N + 7) >> 3;
-    const int n0 = (int)((long)c * N8 / gx) * 8;
-    const int n1 = min((int)((long)(c + 1) * N8 / gx) * 8, N);
+    const int N4 = (N + 3) >> 2;
+    const int n0 = (int)((long)c * N4 / gx) * 4;
+    const int n1 = min((int)((long)(c + 1) * N4 / gx) * 4, N);
     const int ntile = (n1 - n0 + 15) >> 4;
     const int G = K / 128;
     const uint32_t rowb = (uint32_t)(K / 2);         // bytes per row
@@ -134,8 +134,8 @@ int q4g128_probe_tile_read(const uint32_t *W, int K, int N, uint32_t *sink, void
         return (int)hipErrorInvalidValue;
     const int ncu = compute_units();
     if (ncu < 1 || ncu > 1024) return (int)hipErrorInvalidDevice;
-    const int N8 = (N + 7) / 8;
-    const int gx = ncu < N8 ? ncu : N8;
+    const int N4 = (N + 3) / 4;
+    const int gx = ncu < N4 ? ncu : N4;
     // The product's LDS request (over half the CU's 160 KB) keeps two
     // workgroups off one CU; the probe asks for the same.
     static bool done[64];                        // per device: the attribute is set once on each

@@ -42,6 +42,11 @@ def test_version_and_status_strings(L):
     assert q.q4g128_status_string(99) == "unknown status"
 
 
+def test_gemm_parts_arguments(L):
+    assert q.q4g128_gemm_parts(100, 10) == 0 and q.q4g128_gemm_parts(1024, 0) == 0
+    assert q.q4g128_gemm_parts(640, 100) == 1                 # K not a multiple of 1024: never cut
+
+
 def test_workspace_bytes(L):
     assert q.q4g128_splitk_workspace_bytes(1, 5120, 7) == 7 * 5120 * 4
     assert q.q4g128_splitk_workspace_bytes(8, 34816, 2) == 2 * 8 * 34816 * 4

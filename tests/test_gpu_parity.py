@@ -225,9 +225,11 @@ def test_rows_bit_identical_across_kernel_choice(K, N):
 # Verify wider than 8 rows (a draft of up to 15 tokens plus the next one):
 # rows of every M up to 16 equal the 16-row call's.  At K = 5120, N = 34816
 # the balanced kernel takes M <= 9 and the per-tile kernel M >= 10; at K =
-# 2048, N = 1001 the balanced kernel cuts K into parts for every M (x for 16
-# rows fits); 17408 -> 5120 runs split-K; 6144 -> 5120 the per-tile kernel.
-@pytest.mark.parametrize("K,N,split", [(5120, 34816, False), (2048, 1001, False), (17408, 5120, True),
+# 8192, N = 777 the balanced kernel cuts K into 2 parts and holds 6 rows per
+# launch; 17408 -> 5120 (5 parts, 2 rows per launch) runs with its default
+# splits (one launch for M <= 2, 5 K splits beyond); 6144 -> 5120 (2 parts,
+# 8 rows per launch) without splits.
+@pytest.mark.parametrize("K,N,split", [(5120, 34816, False), (8192, 777, False), (17408, 5120, True),
                                        (6144, 5120, False)])
 def test_rows_bit_identical_up_to_16_rows(K, N, split):
     case = synth.make_random(16, K, N, 60 + K // 1024, outlier_frac=0.01)
@@ -264,3 +266,29 @@ def test_balanced_column_sharing(orc, M, N):
     y_ref, a_ref = orc.gemm(case.x, wt.W, wt.scale, wt.mn)
     y = host_f32(q.q4g128_gemm(dev_x(case.x), *dev_weights(wt)))
     assert_within_tolerance(y, y_ref, a_ref, f"balanced M={M} N={N}")
+
+
+def _misaligned(t):
+    buf = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    view = buf[1:1 + t.numel()].view(t.shape)
+    view.copy_(t)
+    return view
+
+
+# K-part shapes: one balanced launch whose parts are the blocks of P K splits
+# gives the bits of the per-tile kernel with P splits and the split-order
+# reduce (forced here by scales/minimums off a 16-byte boundary), for the
+# rows one launch holds and beyond.
+@pytest.mark.parametrize("K,N", [(17408, 5120), (6144, 5120), (8192, 777)])
+def test_k_parts_equal_split_k(K, N):
+    case = synth.make_random(8, K, N, 120 + K // 1024, outlier_frac=0.01)
+    W, s, m = dev_weights(case.weights)
+    S = q.q4g128_gemm_parts(K, N)
+    assert S >= 2
+    for M in (1, 2, 3, 8):
+        x = dev_x(case.x[:M])
+        fast = host_f32(q.q4g128_gemm_splitk(x, W, s, m, splits=S))
+        tile = host_f32(q.q4g128_gemm_splitk(x, W, _misaligned(s), _misaligned(m), splits=S))
+        plain = host_f32(q.q4g128_gemm(x, W, s, m))
+        assert np.array_equal(bits(fast), bits(tile)), (M, "parts vs splits")
+        assert np.array_equal(bits(fast), bits(plain)), (M, "splits vs no split")
