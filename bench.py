@@ -527,6 +527,77 @@ def measure_read_ceiling(torch, case, reps=20):
                    "per wave per step, 1024 waves, 8 in flight")
     del copies
     torch.cuda.empty_cache()
+    # The same contiguous read over 4x the bytes (K = 20480): how far the
+    # 89 MB figures are from the streaming rate once start-up is amortised.
+    K4 = 4 * K
+    B4 = K4 * N // 2
+    g = torch.Generator(device=dev)
+    g.manual_seed(97)
+    big = [torch.randint(-2**31, 2**31 - 1, (N, K4 // 8), dtype=torch.int32, device=dev, generator=g)
+           for _ in range(max(2, math.ceil(ROTATE_BYTES / B4)))]
+    lin4 = [lambda st, w=w: P.q4g128_probe_linear_read(w.data_ptr(), K4, N, PROBE_LINEAR_WAVES, sink.data_ptr(), st)
+            for w in big]
+    passes = max(1, reps * 13 // len(lin4))
+    t = timed_calls(torch, lin4, passes, 2) * 1e-3 / (passes * len(lin4))
+    out["linear_4x"] = {"bytes_per_launch": B4, "us_per_launch": round(t * 1e6, 3), "GBps": round(B4 / t / 1e9, 1)}
+    del big, lin4
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_product_vs_probe(torch, q, reps=20):
+    """The product at M = 1, N = 34816 for K = 3072, 5120 and 7168 (the same
+    tiles per CU, loop length proportional to K) beside the tile-pattern read
+    probe on the same codes: `extra_us`, product minus probe, is what a
+    launch of the product costs beyond reading its codes in the same
+    pattern (its scales and minimums, x staging, arithmetic, tail).  Weights
+    are seeded random codes with constant scales and minimums (the time
+    does not depend on the values); each launch reads its own copy."""
+    import ctypes
+    from quantized_decode_q4g128_amd.build import PROBE_PATH
+    if not os.path.exists(PROBE_PATH):
+        return None
+    P = ctypes.CDLL(PROBE_PATH)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    P.q4g128_probe_sink_words.argtypes = [ci, ci, ci]
+    P.q4g128_probe_sink_words.restype = ctypes.c_size_t
+    P.q4g128_probe_tile_read.argtypes = [vp, ci, ci, vp, vp]
+    dev = torch.device("cuda:0")
+    L = q.lib()
+    N = 34816
+    sink = torch.empty(P.q4g128_probe_sink_words(0, N, PROBE_LINEAR_WAVES), dtype=torch.int32, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(98)
+    out = {}
+    for K in (3072, 5120, 7168):
+        G = K // 128
+        B = synth.algorithmic_bytes(1, K, N)
+        x = torch.randint(-2**15, 2**15 - 1, (1, K), dtype=torch.int16, device=dev, generator=g) & 0x3FFF
+        y = torch.empty((1, N), dtype=torch.float32, device=dev)
+        sets = [(torch.randint(-2**31, 2**31 - 1, (N, K // 8), dtype=torch.int32, device=dev, generator=g),
+                 torch.full((N, G), 0x3C24, dtype=torch.int16, device=dev),
+                 torch.full((N, G), -0x425C, dtype=torch.int16, device=dev))
+                for _ in range(max(2, math.ceil(ROTATE_BYTES / B)))]
+        prod = [lambda st, a=(x.data_ptr(), 1, K, W.data_ptr(), s.data_ptr(), m.data_ptr(), N, y.data_ptr()):
+                L.q4g128_gemm(*a, st) for W, s, m in sets]
+        probe = [lambda st, w=W: P.q4g128_probe_tile_read(w.data_ptr(), K, N, sink.data_ptr(), st)
+                 for W, _, _ in sets]
+        passes = max(1, reps * 13 // len(sets))
+        # First passes over fresh allocations run slow (~2 us per launch at
+        # first): warm both over every copy, then alternate and keep the best.
+        timed_calls(torch, prod, 1, 4)
+        timed_calls(torch, probe, 1, 4)
+        tp = tr = float("inf")
+        for _ in range(2):
+            tp = min(tp, timed_calls(torch, prod, passes, 1) * 1e-3 / (passes * len(sets)))
+            tr = min(tr, timed_calls(torch, probe, passes, 1) * 1e-3 / (passes * len(sets)))
+        out[str(K)] = {"product_us": round(tp * 1e6, 3), "product_GBps": round(B / tp / 1e9, 1),
+                       "tile_probe_us": round(tr * 1e6, 3), "tile_probe_GBps": round(K * N // 2 / tr / 1e9, 1),
+                       "extra_us": round((tp - tr) * 1e6, 3)}
+        del sets, prod, probe
+        torch.cuda.empty_cache()
+    out["note"] = ("M=1, N=34816: the product (algorithmic bytes) and the tile-pattern read probe (codes only) "
+                   "on the same seeded random codes; extra_us = product - probe")
     return out
 
 
@@ -765,6 +836,8 @@ def main():
     wider = None if args.no_verify else measure_wide_verify(torch, q, raw, t_dec, args.steps, args.warmup)
     traffic = traffic_from_summary()
     ceiling = None if args.no_read_ceiling else measure_read_ceiling(torch, dec_case)
+    if ceiling is not None:
+        ceiling["product_vs_probe"] = measure_product_vs_probe(torch, q)
     down = None if args.no_down else measure_down(torch, q, args.steps, args.warmup)
     stream_step = measure_stream(torch, q) if not args.no_stream else None
     epilogues = None if args.no_epilogues else measure_epilogues(torch, q, args.steps, args.warmup)
