@@ -640,8 +640,68 @@ def cpu_baseline(dec_case, budget_s, y_dec, ver_case=None, y_ver=None, quant=Non
             "sample": f"{reps} full fp64 oracle calls on the same M={case.M} K={case.K} N={case.N} "
                       f"input ({dt * 1e3:.1f} ms per call, {reps * dt:.1f} s in all)",
             "one_thread": {"value": round(B / dt1 / 1e9, 4), "unit": "GB/s",
-                           "sample": f"every 16th column ({cols.size} of {case.N}) on 1 thread, scaled to all N"}}, \
+                           "sample": f"every 16th column ({cols.size} of {case.N}) on 1 thread, scaled to all N"},
+            "per_config": oracle_per_config(orc, ver_case)}, \
         checks
+
+
+def oracle_per_config(orc, ver_case, min_s=0.3):
+    """The oracle (all threads) on the other workloads: tiny, down, the
+    7-row verify, and the decode-step stream extrapolated from one call per
+    distinct shape (64 x the four layer shapes + the output projection)."""
+    def per_call(case):
+        wt = case.weights
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            orc.gemm(case.x, wt.W, wt.scale, wt.mn)
+            n += 1
+            if time.perf_counter() - t0 >= min_s:
+                return (time.perf_counter() - t0) / n
+    out = {}
+    for name, case in (("tiny", synth.make_case("tiny")), ("down_M1", synth.make_case("down")),
+                       ("verify_M7", ver_case)):
+        if case is None:
+            continue
+        dt = per_call(case)
+        out[name] = {"GBps": round(synth.algorithmic_bytes(case.M, case.K, case.N) / dt / 1e9, 4),
+                     "ms_per_call": round(dt * 1e3, 3)}
+    t_step, b_step = 0.0, 0
+    shapes = synth.stream_shapes()
+    for i, (K, N, seed) in enumerate(shapes):
+        c = synth.make_random(1, K, N, seed)
+        reps = 1 if i == len(shapes) - 1 else synth.STREAM_LAYERS
+        t_step += per_call(c) * reps
+        b_step += synth.algorithmic_bytes(1, K, N) * reps
+        del c
+    out["decode_step_stream"] = {"GBps": round(b_step / t_step / 1e9, 4), "ms_per_step": round(t_step * 1e3, 1),
+                                 "note": "one call per distinct shape, extrapolated to the 257-product step"}
+    return out
+
+
+def env_info(torch):
+    """The device, the software stack and the GPU clock state (rocm-smi's
+    report, read right after the timed decode run; None where unavailable)."""
+    import shutil
+    import subprocess
+    props = torch.cuda.get_device_properties(0)
+    info = {"device": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hip": torch.version.hip, "torch": torch.__version__,
+            "rocm": None, "clocks": None}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    try:
+        r = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        card = next(iter(json.loads(r.stdout).values()))
+        info["clocks"] = {k.strip().rstrip(":"): v for k, v in card.items()
+                          if "clk" in k.lower() or "clock" in k.lower()}
+    except Exception:
+        pass
+    return info
 
 
 # ---- HBM traffic from counters ------------------------------------------------
@@ -742,11 +802,11 @@ def trace_summarize(trace_dir, out, command):
         f.write("# command (rocprofv3 started from /tmp with TMPDIR=/tmp; REPO = repository root):\n")
         f.write(f"#   {command}\n")
         f.write(f"#   python3 bench.py --trace-summarize OUT {os.path.relpath(out, ROOT)}\n")
-        f.write("# kernel | grid x,y | workgroup | launches | avg us | median us | min us | max us\n")
+        f.write("# kernel | grid x,y | workgroup | launches | avg us | median us | min us | p90 us | max us\n")
         for key in sorted(rows, key=lambda k: -sum(rows[k])):
             v = np.array(rows[key])
             f.write(f"{key[0]} | {key[2]},{key[3]} | {key[4]} | {len(v)} | {v.mean():.3f} | {np.median(v):.3f} | "
-                    f"{v.min():.3f} | {v.max():.3f}\n")
+                    f"{v.min():.3f} | {np.percentile(v, 90):.3f} | {v.max():.3f}\n")
     print(open(out).read())
 
 
@@ -826,6 +886,7 @@ def main():
     t_dec = wall_d * 1e-3 / n_dec                 # s per launch (back to back)
     gbps = B_dec * n_dec / (wall_d * 1e-3) / 1e9
     achieved = B_dec / t_dec / 1e9
+    env = env_info(torch)
     verify = None
     if ver_calls:
         n_ver = max(1, args.steps // len(ver_calls)) * len(ver_calls)
@@ -893,6 +954,7 @@ def main():
                                               if ceiling else None)},
         "read_ceiling": ceiling,
         "cpu_baseline": cpu,
+        "env": env,
     }
     print(json.dumps(line))
 
