@@ -95,6 +95,7 @@ constexpr int kBalMinTiles = 8;             // fewer tiles per workgroup: cut ea
 #define Q4G128_BAL_MINPART 24
 #endif
 constexpr int kBalMinPart = Q4G128_BAL_MINPART;   // groups per K part, at least
+constexpr int kBalShortK = 8192;            // K up to which partial-tile shapes get whole tiles and 1-block parts
 constexpr size_t kBalMaxLds = 160 * 1024;
 
 // Launch geometry of the balanced kernel for M rows, S K splits, gx
