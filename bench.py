@@ -681,7 +681,7 @@ def oracle_per_config(orc, ver_case, min_s=0.3):
 
 def env_info(torch):
     """The device, the software stack and the GPU clock state (rocm-smi's
-    report, read right after the timed decode run; None where unavailable)."""
+    report, read after the GPU legs; None where unavailable)."""
     import shutil
     import subprocess
     props = torch.cuda.get_device_properties(0)
@@ -886,7 +886,6 @@ def main():
     t_dec = wall_d * 1e-3 / n_dec                 # s per launch (back to back)
     gbps = B_dec * n_dec / (wall_d * 1e-3) / 1e9
     achieved = B_dec / t_dec / 1e9
-    env = env_info(torch)
     verify = None
     if ver_calls:
         n_ver = max(1, args.steps // len(ver_calls)) * len(ver_calls)
@@ -904,6 +903,7 @@ def main():
     epilogues = None if args.no_epilogues else measure_epilogues(torch, q, args.steps, args.warmup)
     chain = measure_chain(torch, q) if not (args.no_stream or args.no_epilogues) else None
     quant, quant_out = (None, None) if args.no_quantize else measure_quantize(torch, q)
+    env = env_info(torch)            # after every GPU leg: rocm-smi leaves the GPU idle for a second or two
 
     # The CPU leg last: oracle baseline and the parity references.
     cpu, checks = cpu_baseline(dec_case, 0.0 if args.no_cpu_baseline else args.cpu_seconds, y_dec,
