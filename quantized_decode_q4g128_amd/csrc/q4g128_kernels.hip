@@ -52,13 +52,29 @@ namespace q4g128 {
 // minimum ride in the code ring, and a range may end inside a block: the
 // groups past its end are processed with scale and minimum zero (exact zeros)
 // on a copy of its last group's x.
-template <int TPW, bool VSM, int RING, bool SML = false, bool PAD = false>
+//
+// PAIR (TPW = 1, VSM, no PAD; ranges of whole 8-group blocks at even group
+// offsets): the codes of two consecutive groups, 128 contiguous bytes of each
+// column, arrive in two loads, columns 0-7 and 8-15 of the tile, lane l
+// reading bytes 16*(l%8) of column l/8 (+8).  Every load then covers whole
+// 128-byte lines, which lets them carry the non-temporal hint (the weights
+// are read once per call); a load covering half lines with the hint reads
+// slower than without it.  A ring slot holds one pair; the MFMA pieces of the
+// pair's first and second group come out of the two loads by a row-shift
+// merge and one lane permute each, so every MFMA sees the same operands as
+// with one group per load.
+template <int TPW, bool VSM, int RING, bool SML = false, bool PAD = false, bool PAIR = false>
 struct Tile {
     // PAD (with VSM): the range may end inside an 8-group block; groups past
     // its end are processed with scale and minimum zero, as without VSM.
     static constexpr bool kClamp = !VSM || PAD;
+    static_assert(!PAIR || (TPW == 1 && VSM && !PAD && RING % 2 == 0), "paired loads: one tile, whole blocks");
     int i, h, M, K, G, gs, ge;
-    int src;                                      // lane holding this lane's code piece
+    int src;                                      // lane holding this lane's code piece (one group per load)
+    int src_e, src_o;                             // PAIR: lanes holding the first / second group's piece
+    uint32_t vw2;                                 // PAIR: lane offset of the columns 8-15 load
+    u32x4 cb2[RING];                              // PAIR: columns 8-15 of pair slot q (cb[q][0]: columns 0-7)
+    u32x4 codd;                                   // PAIR: the second group's piece, gathered with the first's
     // SML: scales and minimums of the wave's tile sit in LDS ([scale, min]
     // [column][block of 8 groups from smg0], nbl blocks per column row).
     const uint16_t *sml;
@@ -73,6 +89,11 @@ struct Tile {
 
     __device__ __forceinline__ void fetch(int q, int g)
     {
+        if (PAIR) {                               // pair slot q: groups g, g + 1 (g even)
+            cb[q][0] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw[0], 64 * g, kPairCpol);
+            cb2[q] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw2, 64 * g, kPairCpol);
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             cb[q][u] = __builtin_amdgcn_raw_buffer_load_b128(rw, vw[u], 64 * g, 0);
@@ -105,6 +126,11 @@ struct Tile {
         // Scales and minimums first: the loop's first wait for them then
         // leaves the code loads in flight.
         if (VSM && !SML) fetch_sm(0, cs);        // SML: read from LDS once it is written
+        if (PAIR) {
+#pragma unroll
+            for (int q = 0; q < RING / 2; ++q) fetch(q, min(cs + 2 * q, ce - 2));
+            return;
+        }
 #pragma unroll
         for (int q = 0; q < RING; ++q) fetch(q, min(cs + q, ce - 1));
     }
@@ -124,15 +150,28 @@ struct Tile {
         // compiler from sinking the refill below the arithmetic.
         u32x4 c[TPW];
         float s[TPW], m[TPW];
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-            c[u] = lane_gather(cb[q][u], src);
-            if (!VSM) {                           // scale and minimum ride in the same slot
-                s[u] = bf16_lo(sb[q][u]);
-                m[u] = bf16_lo(mb[q][u]);
+        if (PAIR) {
+            // q = (g - cs) % RING with cs and RING even: pair slot q / 2, and
+            // the group's place in its pair is q % 2.
+            if ((q & 1) == 0) {
+                const int pq = q >> 1;
+                c[0] = lane_gather(merge_rows(cb[pq][0], cb2[pq], false), src_e);
+                codd = lane_gather(merge_rows(cb[pq][0], cb2[pq], true), src_o);
+                fetch(pq, min(g + RING, ce - 2));
+            } else {
+                c[0] = codd;
             }
+        } else {
+#pragma unroll
+            for (int u = 0; u < TPW; ++u) {
+                c[u] = lane_gather(cb[q][u], src);
+                if (!VSM) {                       // scale and minimum ride in the same slot
+                    s[u] = bf16_lo(sb[q][u]);
+                    m[u] = bf16_lo(mb[q][u]);
+                }
+            }
+            fetch(q, min(g + RING, ce - 1));
         }
-        fetch(q, min(g + RING, ce - 1));
         __builtin_amdgcn_sched_barrier(0);
         u32x4 bq[TPW][4];
 #pragma unroll
@@ -344,8 +383,8 @@ __device__ __forceinline__ uint16_t swiglu_bf16(float g, float u)
 // bits.  Needs K/128 a multiple of 8 and 16-byte aligned scale/min.
 
 template <int RING, bool SML, bool PAD, bool ACT = false>
-struct BalTile : Tile<1, true, RING, SML, PAD> {
-    typedef Tile<1, true, RING, SML, PAD> Base;
+struct BalTile : Tile<1, true, RING, SML, PAD, kBalPair> {
+    typedef Tile<1, true, RING, SML, PAD, kBalPair> Base;
     int la, lb, nblk, ncols, wact, NC;
 
     // Column of W that tile column c (0..15) reads, relative to the tile's
@@ -373,7 +412,12 @@ struct BalTile : Tile<1, true, RING, SML, PAD> {
         this->rw = make_rsrc(W + (size_t)cbase * this->K8, (uint32_t)(span * this->K8 * 4));
         this->rs = make_rsrc(scale + (size_t)cbase * this->G, (uint32_t)(span * this->G * 2));
         this->rm = make_rsrc(mn + (size_t)cbase * this->G, (uint32_t)(span * this->G * 2));
-        this->vw[0] = (uint32_t)((size_t)colmap(la) * this->K8 * 4 + 16 * lb);
+        if (kBalPair) {                                    // columns (lane / 8) and 8 + (lane / 8), bytes 16 * (lane % 8)
+            this->vw[0] = (uint32_t)((size_t)colmap(la >> 1) * this->K8 * 4 + 16 * (4 * (la & 1) + lb));
+            this->vw2 = (uint32_t)((size_t)colmap(8 + (la >> 1)) * this->K8 * 4 + 16 * (4 * (la & 1) + lb));
+        } else {
+            this->vw[0] = (uint32_t)((size_t)colmap(la) * this->K8 * 4 + 16 * lb);
+        }
         this->vs[0] = (uint32_t)((size_t)colmap(la) * this->G * 2);   // !SML: per-block loads, quad order
 #pragma unroll
         for (int r = 0; r < 4; ++r) this->acc[0][r] = 0.0f;
@@ -508,6 +552,12 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     B.la = lane >> 2;
     B.lb = lane & 3;
     B.src = 4 * B.i + B.h;
+    // Paired loads: column i's bytes of the pair's first group sit in lanes
+    // 8*(i%8) + h of the columns-(i/8) load; the row-shift merge moves the
+    // columns 8-15 pieces to lanes 8*(i%8) + 4 + h (first group) and 8*(i%8) + h
+    // (second group), beside the columns 0-7 pieces they do not collide with.
+    B.src_e = 8 * (B.i & 7) + 4 * (B.i >> 3) + B.h;
+    B.src_o = 8 * (B.i & 7) + 4 * (1 - (B.i >> 3)) + B.h;
     B.M = M;
     B.K = K;
     B.G = G;

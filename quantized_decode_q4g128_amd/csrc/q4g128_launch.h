@@ -86,6 +86,16 @@ constexpr int kBalRing = Q4G128_BAL_RING;   // groups of codes in flight per wav
 #define Q4G128_BAL_SML 1
 #endif
 constexpr bool kBalSml = Q4G128_BAL_SML;    // scales/minimums staged in LDS per tile (else loaded per block)
+#ifndef Q4G128_BAL_PAIR
+#define Q4G128_BAL_PAIR 1
+#endif
+constexpr bool kBalPair = Q4G128_BAL_PAIR;  // codes loaded two groups (128 B per column) at a time
+#ifndef Q4G128_PAIR_CPOL
+#define Q4G128_PAIR_CPOL 2
+#endif
+// Cache policy of the paired code loads: 2 = nt (non-temporal: the lines are
+// read once per call; held in the caches, they only displace other data).
+constexpr int kPairCpol = Q4G128_PAIR_CPOL;
 constexpr int kBalThreads = 64 * kBalWaves;
 constexpr int kBalStage = 8;                // x pieces per thread: M * ng * 16 <= 6144 (M = 8 at K = 6144, 9 at 5120)
 constexpr int kBalSmRounds = 2;             // scale/min pieces per lane: 16 * nblk <= 128, nblk <= 8
