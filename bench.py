@@ -495,7 +495,7 @@ def measure_read_ceiling(torch, case, reps=20):
     """What HBM delivers on this GPU to a pure read of the gate/up codes
     (K*N/2 bytes, no arithmetic): in the product's access pattern and work
     split (one 12-wave workgroup per CU owning an equal share of the rows,
-    tiles of 16 rows, 64 contiguous bytes per row per step) and read contiguously
+    tiles of 16 rows, 128 contiguous bytes per row per step) and read contiguously
     (1 KB per wave per step, 1024 waves).  Each launch reads its own copy of
     the codes, as the timed product does."""
     import ctypes
@@ -523,8 +523,8 @@ def measure_read_ceiling(torch, case, reps=20):
         t = timed_calls(torch, calls, passes, 2) * 1e-3 / (passes * len(calls))
         out[name] = {"us_per_launch": round(t * 1e6, 3), "GBps": round(B / t / 1e9, 1)}
     out["note"] = ("pure reads of the gate/up codes: tile_pattern = the product's work split (12-wave "
-                   "workgroup per CU, 16-row tiles, 64 B per row per step, 4 steps in flight); linear = 1 KB "
-                   "per wave per step, 1024 waves, 8 in flight")
+                   "workgroup per CU, 16-row tiles, 128 B per row per step (two groups), 2 steps in flight); "
+                   "linear = 1 KB per wave per step, 1024 waves, 8 in flight; both with the non-temporal hint")
     del copies
     torch.cuda.empty_cache()
     # The same contiguous read over 4x the bytes (K = 20480): how far the

@@ -279,7 +279,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    Tile<TPW, VSM, RING> T;
+    // One tile per wave with whole 8-group blocks: codes loaded two groups at
+    // a time (see Tile).
+    constexpr bool PR = kTilePair && TPW == 1 && VSM;
+    Tile<TPW, VSM, RING, false, false, PR> T;
     T.i = lane & 15;    // column within a tile; A row
     T.h = lane >> 4;    // 16-byte code piece within a group; D row block
     T.M = M;
@@ -307,10 +310,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
     // i + 16h, which fetches it from lane 4i + h when it is consumed.
     const int la = lane >> 2, lb = lane & 3;
     T.src = 4 * T.i + T.h;
+    T.src_e = 8 * (T.i & 7) + 4 * (T.i >> 3) + T.h;   // paired loads (see the balanced kernel)
+    T.src_o = 8 * (T.i & 7) + 4 * (1 - (T.i >> 3)) + T.h;
+    if (PR) {                                     // columns lane / 8 and 8 + lane / 8, bytes 16 * (lane % 8)
+        T.vw2 = (uint32_t)((size_t)min(8 + (lane >> 3), ncols - 1) * T.K8 * 4 + 16 * (lane & 7));
+    }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         const int cl = min(16 * u + la, ncols - 1);   // ragged tail: read a real column
-        T.vw[u] = (uint32_t)((size_t)cl * T.K8 * 4 + 16 * lb);
+        T.vw[u] = PR ? (uint32_t)((size_t)min(lane >> 3, ncols - 1) * T.K8 * 4 + 16 * (lane & 7))
+                     : (uint32_t)((size_t)cl * T.K8 * 4 + 16 * lb);
         // 16-byte scale/minimum loads (VSM) follow the same quad order and are
         // gathered once per block; 2-byte ones are read by the lane using them.
         const int c = min(16 * u + (VSM ? la : T.i), ncols - 1);

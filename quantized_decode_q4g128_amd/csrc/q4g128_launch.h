@@ -54,6 +54,10 @@ constexpr int kSmallM = Q4G128_SMALL_M;
 constexpr int kRing = 8;                   // K splits align to blocks of 8 groups (1024 k)
 constexpr int kRingDepth = Q4G128_RING;    // groups of codes in flight per wave (4, 8 or 16)
 constexpr int kStageMax = Q4G128_STAGE;    // 16-byte x pieces staged per thread per chunk
+#ifndef Q4G128_TILE_PAIR
+#define Q4G128_TILE_PAIR 1
+#endif
+constexpr bool kTilePair = Q4G128_TILE_PAIR; // per-tile kernel: codes two groups at a time where ranges are whole blocks
 
 struct GemvArgs {
     const uint16_t *x;       // bf16 [M][K]

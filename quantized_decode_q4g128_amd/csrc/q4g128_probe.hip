@@ -8,13 +8,17 @@
 //                      12-wave workgroup per compute unit owning an equal
 //                      share of the rows (cut in units of 4, workgroups
 //                      numbered XCD by XCD), tiles of 16 consecutive rows,
-//                      one tile per wave at a time; per step each lane quad
-//                      reads 64 contiguous bytes (one 128-weight group) of
-//                      one row, 16 rows per wave instruction, 4 groups in
-//                      flight per wave;
+//                      one tile per wave at a time; per step each run of 8
+//                      lanes reads 128 contiguous bytes (two 128-weight
+//                      groups) of one row, 8 rows per wave instruction, two
+//                      instructions per step, 2 steps (4 groups) in flight
+//                      per wave;
 //   probe_linear_read  the same bytes read contiguously: each wave owns an
 //                      equal span of the buffer and reads 1 KB per step
 //                      (16 bytes per lane); 8 steps in flight per wave.
+//
+// Both carry the non-temporal hint, as the product's code loads do: every
+// line is read once.
 //
 // Every load is in bounds (indices are clamped, never left to the buffer
 // descriptor); the loaded words are folded into one word per lane and
@@ -31,8 +35,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t b
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-constexpr int kTileRing = 4;
+constexpr int kTileRing = 2;                    // steps of two groups
 constexpr int kLinRing = 8;
+constexpr int kNt = 2;                          // cache policy: non-temporal
 
 constexpr int kTileWaves = 12;
 constexpr int kOwnCuLds = 81 * 1024;
@@ -52,23 +57,30 @@ __global__ __launch_bounds__(64 * kTileWaves) void probe_tile_read(const uint32_
     const uint32_t rowb = (uint32_t)(K / 2);         // bytes per row
     const __amdgpu_buffer_rsrc_t r = rsrc(W, (uint32_t)((size_t)N * rowb));
     uint32_t acc = 0;
+    const int G2 = G >> 1;                         // steps of two groups (K % 256 == 0)
     for (int t = wave; t < ntile; t += kTileWaves) {
-        const int row = min(n0 + 16 * t + (lane >> 2), n1 - 1);
-        const uint32_t base = (uint32_t)row * rowb + 16 * (lane & 3);
-        u32x4 ring[kTileRing];
+        const int rowa = min(n0 + 16 * t + (lane >> 3), n1 - 1);
+        const int rowb8 = min(n0 + 16 * t + 8 + (lane >> 3), n1 - 1);
+        const uint32_t ba = (uint32_t)rowa * rowb + 16 * (lane & 7);
+        const uint32_t bb = (uint32_t)rowb8 * rowb + 16 * (lane & 7);
+        u32x4 ra[kTileRing], rb[kTileRing];
 #pragma unroll
-        for (int u = 0; u < kTileRing; ++u)
-            ring[u] = __builtin_amdgcn_raw_buffer_load_b128(r, base + 64 * (uint32_t)min(u, G - 1), 0, 0);
-        for (int g = 0; g < G; g += kTileRing) {
+        for (int u = 0; u < kTileRing; ++u) {
+            ra[u] = __builtin_amdgcn_raw_buffer_load_b128(r, ba + 128 * (uint32_t)min(u, G2 - 1), 0, kNt);
+            rb[u] = __builtin_amdgcn_raw_buffer_load_b128(r, bb + 128 * (uint32_t)min(u, G2 - 1), 0, kNt);
+        }
+        for (int g = 0; g < G2; g += kTileRing) {
 #pragma unroll
             for (int u = 0; u < kTileRing; ++u) {
-                acc ^= ring[u].x ^ ring[u].y ^ ring[u].z ^ ring[u].w;
-                const int gn = min(g + u + kTileRing, G - 1);
-                ring[u] = __builtin_amdgcn_raw_buffer_load_b128(r, base + 64 * (uint32_t)gn, 0, 0);
+                acc ^= ra[u].x ^ ra[u].y ^ ra[u].z ^ ra[u].w ^ rb[u].x ^ rb[u].y ^ rb[u].z ^ rb[u].w;
+                const int gn = min(g + u + kTileRing, G2 - 1);
+                ra[u] = __builtin_amdgcn_raw_buffer_load_b128(r, ba + 128 * (uint32_t)gn, 0, kNt);
+                rb[u] = __builtin_amdgcn_raw_buffer_load_b128(r, bb + 128 * (uint32_t)gn, 0, kNt);
             }
         }
 #pragma unroll
-        for (int u = 0; u < kTileRing; ++u) acc ^= ring[u].x ^ ring[u].y ^ ring[u].z ^ ring[u].w;
+        for (int u = 0; u < kTileRing; ++u)
+            acc ^= ra[u].x ^ ra[u].y ^ ra[u].z ^ ra[u].w ^ rb[u].x ^ rb[u].y ^ rb[u].z ^ rb[u].w;
     }
     sink[((size_t)blockIdx.x * kTileWaves + wave) * 64 + lane] = acc;
 }
@@ -97,13 +109,13 @@ __global__ __launch_bounds__(256) void probe_linear_read(const uint32_t *__restr
     u32x4 ring[kLinRing];
 #pragma unroll
     for (int u = 0; u < kLinRing; ++u)
-        ring[u] = __builtin_amdgcn_raw_buffer_load_b128(r, base + 1024 * (uint32_t)min(u, steps - 1), 0, 0);
+        ring[u] = __builtin_amdgcn_raw_buffer_load_b128(r, base + 1024 * (uint32_t)min(u, steps - 1), 0, kNt);
     for (int k = 0; k < steps; k += kLinRing) {
 #pragma unroll
         for (int u = 0; u < kLinRing; ++u) {
             acc ^= ring[u].x ^ ring[u].y ^ ring[u].z ^ ring[u].w;
             const int kn = min(k + u + kLinRing, steps - 1);
-            ring[u] = __builtin_amdgcn_raw_buffer_load_b128(r, base + 1024 * (uint32_t)kn, 0, 0);
+            ring[u] = __builtin_amdgcn_raw_buffer_load_b128(r, base + 1024 * (uint32_t)kn, 0, kNt);
         }
     }
 #pragma unroll
@@ -126,11 +138,11 @@ size_t q4g128_probe_sink_words(int K, int N, int linear_waves)
     return w * 64;
 }
 
-// One launch of the tile-pattern probe over W [N][K/8] (K % 128 == 0,
+// One launch of the tile-pattern probe over W [N][K/8] (K % 256 == 0,
 // N * K / 2 < 2^32 bytes, W 16-byte aligned).  Returns a hipError_t.
 int q4g128_probe_tile_read(const uint32_t *W, int K, int N, uint32_t *sink, void *stream)
 {
-    if (!W || !sink || K <= 0 || K % 128 || N <= 0 || (size_t)N * (size_t)(K / 2) >= (1ull << 32))
+    if (!W || !sink || K <= 0 || K % 256 || N <= 0 || (size_t)N * (size_t)(K / 2) >= (1ull << 32))
         return (int)hipErrorInvalidValue;
     const int ncu = compute_units();
     if (ncu < 1 || ncu > 1024) return (int)hipErrorInvalidDevice;
