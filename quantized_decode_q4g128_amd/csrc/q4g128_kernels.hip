@@ -63,7 +63,10 @@ namespace q4g128 {
 // pair's first and second group come out of the two loads by a row-shift
 // merge and one lane permute each, so every MFMA sees the same operands as
 // with one group per load.
-template <int TPW, bool VSM, int RING, bool SML = false, bool PAD = false, bool PAIR = false>
+// RL: D rows per lane that are accumulated (4, or 1 when M = 1: lane i + 16h
+// holds rows 4h..4h+3 and only row 0 is ever stored).  A row's instructions
+// do not depend on RL, so its bits do not either.
+template <int TPW, bool VSM, int RING, bool SML = false, bool PAD = false, bool PAIR = false, int RL = 4>
 struct Tile {
     // PAD (with VSM): the range may end inside an 8-group block; groups past
     // its end are processed with scale and minimum zero, as without VSM.
@@ -201,7 +204,7 @@ struct Tile {
                 m_adj = 0.0f;
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
+            for (int r = 0; r < RL; ++r) {
                 acc[u][r] = fmaf(sc, d[r], acc[u][r]);
                 acc[u][r] = fmaf(m_adj, xsum[r], acc[u][r]);
             }
@@ -391,9 +394,9 @@ __device__ __forceinline__ uint16_t swiglu_bf16(float g, float u)
 // per-column instructions are those of gemv_q4g128, so results are the same
 // bits.  Needs K/128 a multiple of 8 and 16-byte aligned scale/min.
 
-template <int RING, bool SML, bool PAD, bool ACT = false>
-struct BalTile : Tile<1, true, RING, SML, PAD, kBalPair> {
-    typedef Tile<1, true, RING, SML, PAD, kBalPair> Base;
+template <int RING, bool SML, bool PAD, bool ACT = false, int RL = 4>
+struct BalTile : Tile<1, true, RING, SML, PAD, kBalPair, RL> {
+    typedef Tile<1, true, RING, SML, PAD, kBalPair, RL> Base;
     int la, lb, nblk, ncols, wact, NC;
 
     // Column of W that tile column c (0..15) reads, relative to the tile's
@@ -512,7 +515,7 @@ struct BalTile : Tile<1, true, RING, SML, PAD, kBalPair> {
 // matching up columns in the last 8, so a pair meets in one wave's
 // registers and bf16 silu(gate) * up goes straight to act [M][I].  The
 // per-column sums are those of the plain product.
-template <int RING, bool SML, bool PARTS, bool ACT>
+template <int RING, bool SML, bool PARTS, bool ACT, int RL>
 __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ mn, int N,
@@ -555,7 +558,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     const int nunit = PARTS ? nchunk * P : nchunk;        // (tile, part) units
     const bool active = wave < nunit;                     // wave-uniform
 
-    BalTile<RING, SML, false, ACT> B;
+    BalTile<RING, SML, false, ACT, RL> B;
     B.i = lane & 15;
     B.h = lane >> 4;
     B.la = lane >> 2;
@@ -910,18 +913,26 @@ BalPlan bal_plan(int M, int K, int N, int S, int gx, int P, bool act)
     return bp;
 }
 
-template <bool PARTS, bool ACT>
-static hipError_t launch_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)
+template <bool PARTS, bool ACT, int RL>
+static hipError_t launch_bal_rl(const GemvArgs &a, int gx, int P, hipStream_t stream)
 {
     static LdsFlags done;
     const hipError_t attr = allow_dynamic_lds(
-        reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT>), (int)kBalMaxLds, done);
+        reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT, RL>), (int)kBalMaxLds, done);
     if (attr != hipSuccess) return attr;
     BalPlan bp = bal_plan(a.M, a.K, a.N, a.S, gx, P, ACT);
-    hipLaunchKernelGGL((gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT>), dim3((unsigned)gx, (unsigned)a.S, 1),
+    hipLaunchKernelGGL((gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT, RL>), dim3((unsigned)gx, (unsigned)a.S, 1),
                        dim3(kBalThreads, 1, 1), bp.lds, stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out,
                        a.act, a.S, bp.nblp, P, bp.nps);
     return hipGetLastError();
+}
+
+// One row accumulates one D row per lane; more rows all four.
+template <bool PARTS, bool ACT>
+static hipError_t launch_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)
+{
+    return (kBalOneRow && a.M == 1) ? launch_bal_rl<PARTS, ACT, 1>(a, gx, P, stream)
+                                     : launch_bal_rl<PARTS, ACT, 4>(a, gx, P, stream);
 }
 
 hipError_t launch_gemv_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)

@@ -100,6 +100,10 @@ constexpr bool kBalPair = Q4G128_BAL_PAIR;  // codes loaded two groups (128 B pe
 // Cache policy of the paired code loads: 2 = nt (non-temporal: the lines are
 // read once per call; held in the caches, they only displace other data).
 constexpr int kPairCpol = Q4G128_PAIR_CPOL;
+#ifndef Q4G128_BAL_ONEROW
+#define Q4G128_BAL_ONEROW 1
+#endif
+constexpr bool kBalOneRow = Q4G128_BAL_ONEROW;   // M = 1: accumulate only the one D row per lane that is stored
 constexpr int kBalThreads = 64 * kBalWaves;
 constexpr int kBalStage = 8;                // x pieces per thread: M * ng * 16 <= 6144 (M = 8 at K = 6144, 9 at 5120)
 constexpr int kBalSmRounds = 2;             // scale/min pieces per lane: 16 * nblk <= 128, nblk <= 8
