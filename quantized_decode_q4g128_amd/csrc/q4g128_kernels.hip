@@ -394,9 +394,9 @@ __device__ __forceinline__ uint16_t swiglu_bf16(float g, float u)
 // per-column instructions are those of gemv_q4g128, so results are the same
 // bits.  Needs K/128 a multiple of 8 and 16-byte aligned scale/min.
 
-template <int RING, bool SML, bool PAD, bool ACT = false, int RL = 4>
-struct BalTile : Tile<1, true, RING, SML, PAD, kBalPair, RL> {
-    typedef Tile<1, true, RING, SML, PAD, kBalPair, RL> Base;
+template <int RING, bool SML, bool PAD, bool ACT = false, int RL = 4, bool PAIR = true>
+struct BalTile : Tile<1, true, RING, SML, PAD, PAIR, RL> {
+    typedef Tile<1, true, RING, SML, PAD, PAIR, RL> Base;
     int la, lb, nblk, ncols, wact, NC;
 
     // Column of W that tile column c (0..15) reads, relative to the tile's
@@ -424,7 +424,7 @@ struct BalTile : Tile<1, true, RING, SML, PAD, kBalPair, RL> {
         this->rw = make_rsrc(W + (size_t)cbase * this->K8, (uint32_t)(span * this->K8 * 4));
         this->rs = make_rsrc(scale + (size_t)cbase * this->G, (uint32_t)(span * this->G * 2));
         this->rm = make_rsrc(mn + (size_t)cbase * this->G, (uint32_t)(span * this->G * 2));
-        if (kBalPair) {                                    // columns (lane / 8) and 8 + (lane / 8), bytes 16 * (lane % 8)
+        if (PAIR) {                                        // columns (lane / 8) and 8 + (lane / 8), bytes 16 * (lane % 8)
             this->vw[0] = (uint32_t)((size_t)colmap(la >> 1) * this->K8 * 4 + 16 * (4 * (la & 1) + lb));
             this->vw2 = (uint32_t)((size_t)colmap(8 + (la >> 1)) * this->K8 * 4 + 16 * (4 * (la & 1) + lb));
         } else {
@@ -515,7 +515,10 @@ struct BalTile : Tile<1, true, RING, SML, PAD, kBalPair, RL> {
 // matching up columns in the last 8, so a pair meets in one wave's
 // registers and bf16 silu(gate) * up goes straight to act [M][I].  The
 // per-column sums are those of the plain product.
-template <int RING, bool SML, bool PARTS, bool ACT, int RL>
+// PAIR: codes loaded two groups at a time (see Tile); the plan takes it for
+// workgroups with many tiles, where it streams faster, and leaves it off for
+// a few tiles per CU, where it streamed slower.  It never changes a bit.
+template <int RING, bool SML, bool PARTS, bool ACT, int RL, bool PAIR>
 __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ mn, int N,
@@ -558,7 +561,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     const int nunit = PARTS ? nchunk * P : nchunk;        // (tile, part) units
     const bool active = wave < nunit;                     // wave-uniform
 
-    BalTile<RING, SML, false, ACT, RL> B;
+    BalTile<RING, SML, false, ACT, RL, PAIR> B;
     B.i = lane & 15;
     B.h = lane >> 4;
     B.la = lane >> 2;
@@ -904,6 +907,7 @@ BalPlan bal_plan(int M, int K, int N, int S, int gx, int P, bool act)
     }
     const int units = tiles * P;
     const int nw = units < kBalWaves ? units : kBalWaves;
+    bp.pair = kBalPair && units >= kBalPairUnits;
     const int pg = P > 1 ? (ngmax / 8 + P - 1) / P * 8 : ngmax;        // longest part, in groups
     bp.nblp = ((pg + 7) / 8) | 1;
     bp.nps = P > 1 ? units : 0;
@@ -913,18 +917,26 @@ BalPlan bal_plan(int M, int K, int N, int S, int gx, int P, bool act)
     return bp;
 }
 
-template <bool PARTS, bool ACT, int RL>
-static hipError_t launch_bal_rl(const GemvArgs &a, int gx, int P, hipStream_t stream)
+template <bool PARTS, bool ACT, int RL, bool PAIR>
+static hipError_t launch_bal_v(const GemvArgs &a, int gx, int P, const BalPlan &bp, hipStream_t stream)
 {
     static LdsFlags done;
     const hipError_t attr = allow_dynamic_lds(
-        reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT, RL>), (int)kBalMaxLds, done);
+        reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT, RL, PAIR>), (int)kBalMaxLds,
+        done);
     if (attr != hipSuccess) return attr;
-    BalPlan bp = bal_plan(a.M, a.K, a.N, a.S, gx, P, ACT);
-    hipLaunchKernelGGL((gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT, RL>), dim3((unsigned)gx, (unsigned)a.S, 1),
-                       dim3(kBalThreads, 1, 1), bp.lds, stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out,
-                       a.act, a.S, bp.nblp, P, bp.nps);
+    hipLaunchKernelGGL((gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT, RL, PAIR>),
+                       dim3((unsigned)gx, (unsigned)a.S, 1), dim3(kBalThreads, 1, 1), bp.lds, stream, a.x, a.M, a.K,
+                       a.W, a.scale, a.mn, a.N, a.out, a.act, a.S, bp.nblp, P, bp.nps);
     return hipGetLastError();
+}
+
+template <bool PARTS, bool ACT, int RL>
+static hipError_t launch_bal_rl(const GemvArgs &a, int gx, int P, hipStream_t stream)
+{
+    const BalPlan bp = bal_plan(a.M, a.K, a.N, a.S, gx, P, ACT);
+    return bp.pair ? launch_bal_v<PARTS, ACT, RL, true>(a, gx, P, bp, stream)
+                   : launch_bal_v<PARTS, ACT, RL, false>(a, gx, P, bp, stream);
 }
 
 // One row accumulates one D row per lane; more rows all four.

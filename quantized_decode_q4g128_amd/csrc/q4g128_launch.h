@@ -94,6 +94,10 @@ constexpr bool kBalSml = Q4G128_BAL_SML;    // scales/minimums staged in LDS per
 #define Q4G128_BAL_PAIR 1
 #endif
 constexpr bool kBalPair = Q4G128_BAL_PAIR;  // codes loaded two groups (128 B per column) at a time
+// ... for workgroups of at least this many (tile, K part) units: with 3 tiles
+// per CU (5120 -> 12288) the paired loads streamed 4% slower, with 9 or more
+// 1-13% faster.
+constexpr int kBalPairUnits = 8;
 #ifndef Q4G128_PAIR_CPOL
 #define Q4G128_PAIR_CPOL 2
 #endif
@@ -122,6 +126,7 @@ struct BalPlan {
     size_t lds;     // dynamic LDS bytes (at least kBalOwnCu: one workgroup per CU)
     int nblp;       // 8-group blocks per column row of a wave's scale/min area (odd)
     int nps;        // part-sum slots (P > 1)
+    bool pair;      // codes loaded two groups at a time (workgroups of at least kBalPairUnits units)
 };
 BalPlan bal_plan(int M, int K, int N, int S, int gx, int P, bool act = false);
 // y (S == 1) or partials [S][M][N] (S > 1) with gx workgroups per split.
