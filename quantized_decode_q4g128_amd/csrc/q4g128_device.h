@@ -73,26 +73,18 @@ __device__ __forceinline__ u32x4 lane_gather(const u32x4 &v, int src_lane)
     return r;
 }
 
-// Lane l of a gets b's word from lane l - 4 where l % 8 >= 4 (second == false),
-// or from lane l + 4 where l % 8 < 4 (second == true), and keeps its own word
-// elsewhere: a DPP row shift by 4 written to two of the four 4-lane banks of
-// each 16-lane row.  Never crosses an 8-lane block.
-__device__ __forceinline__ u32x4 merge_rows(const u32x4 &a, const u32x4 &b, bool second)
+// Per lane: a where take_a, else b.
+__device__ __forceinline__ u32x4 pick(bool take_a, const u32x4 &a, const u32x4 &b)
 {
     u32x4 r;
-    if (second) {
-        r.x = (uint32_t)__builtin_amdgcn_update_dpp((int)a.x, (int)b.x, 0x104, 0xF, 0x5, false);   // row_shl:4, banks 0, 2
-        r.y = (uint32_t)__builtin_amdgcn_update_dpp((int)a.y, (int)b.y, 0x104, 0xF, 0x5, false);
-        r.z = (uint32_t)__builtin_amdgcn_update_dpp((int)a.z, (int)b.z, 0x104, 0xF, 0x5, false);
-        r.w = (uint32_t)__builtin_amdgcn_update_dpp((int)a.w, (int)b.w, 0x104, 0xF, 0x5, false);
-    } else {
-        r.x = (uint32_t)__builtin_amdgcn_update_dpp((int)a.x, (int)b.x, 0x114, 0xF, 0xA, false);   // row_shr:4, banks 1, 3
-        r.y = (uint32_t)__builtin_amdgcn_update_dpp((int)a.y, (int)b.y, 0x114, 0xF, 0xA, false);
-        r.z = (uint32_t)__builtin_amdgcn_update_dpp((int)a.z, (int)b.z, 0x114, 0xF, 0xA, false);
-        r.w = (uint32_t)__builtin_amdgcn_update_dpp((int)a.w, (int)b.w, 0x114, 0xF, 0xA, false);
-    }
+    r.x = take_a ? a.x : b.x;
+    r.y = take_a ? a.y : b.y;
+    r.z = take_a ? a.z : b.z;
+    r.w = take_a ? a.w : b.w;
     return r;
 }
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
 // bf16 held in the low / high half of a 32-bit register -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }

@@ -55,14 +55,15 @@ namespace q4g128 {
 //
 // PAIR (TPW = 1, VSM, no PAD; ranges of whole 8-group blocks at even group
 // offsets): the codes of two consecutive groups, 128 contiguous bytes of each
-// column, arrive in two loads, columns 0-7 and 8-15 of the tile, lane l
-// reading bytes 16*(l%8) of column l/8 (+8).  Every load then covers whole
-// 128-byte lines, which lets them carry the non-temporal hint (the weights
-// are read once per call); a load covering half lines with the hint reads
-// slower than without it.  A ring slot holds one pair; the MFMA pieces of the
-// pair's first and second group come out of the two loads by a row-shift
-// merge and one lane permute each, so every MFMA sees the same operands as
-// with one group per load.
+// column, arrive in two loads, columns 0-7 and 8-15 of the tile: lane l reads
+// column l/8 (+8) at bytes 16*(l%8) (columns 0-7) or 16*((l%8)^4) (columns
+// 8-15, halves mirrored).  Every load then covers whole 128-byte lines, which
+// lets them carry the non-temporal hint (the weights are read once per
+// call); a load covering half lines with the hint reads slower than without
+// it.  A ring slot holds one pair; the MFMA pieces of the pair's first and
+// second group come out of the two loads by a per-lane select and one lane
+// permute each, so every MFMA sees the same operands as with one group per
+// load.
 // RL: D rows per lane that are accumulated (4, or 1 when M = 1: lane i + 16h
 // holds rows 4h..4h+3 and only row 0 is ever stored).  A row's instructions
 // do not depend on RL, so its bits do not either.
@@ -77,7 +78,6 @@ struct Tile {
     int src_e, src_o;                             // PAIR: lanes holding the first / second group's piece
     uint32_t vw2;                                 // PAIR: lane offset of the columns 8-15 load
     u32x4 cb2[RING];                              // PAIR: columns 8-15 of pair slot q (cb[q][0]: columns 0-7)
-    u32x4 codd;                                   // PAIR: the second group's piece, gathered with the first's
     // SML: scales and minimums of the wave's tile sit in LDS ([scale, min]
     // [column][block of 8 groups from smg0], nbl blocks per column row).
     const uint16_t *sml;
@@ -138,44 +138,21 @@ struct Tile {
         for (int q = 0; q < RING; ++q) fetch(q, min(cs + q, ce - 1));
     }
 
-    // Group g (LDS group index lg) from ring slot q; `set`/`j` locate its
-    // scale and minimum (VSM).
-    __device__ __forceinline__ void group(const uint16_t *rbase, const int (&aoff)[4], const float *xrow,
-                                          int ce, int q, int g, int lg, int set, int j, UnpackConsts uc)
+    // The x rows (A operand) and x row sums of LDS group lg.
+    __device__ __forceinline__ void xread(const uint16_t *rbase, const int (&aoff)[4], const float *xrow, int lg,
+                                          u32x4 (&a)[4], f32x4 &xsum) const
     {
         const uint16_t *gp = rbase + lg * 128;
-        u32x4 a[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u32x4 *>(gp + aoff[t]);
-        const f32x4 xsum = *reinterpret_cast<const f32x4 *>(xrow + lg * kXsRows);
-        // Take the ring slot out (the gather reads it), then refill it at once
-        // so RING groups stay in flight; the scheduling barrier keeps the
-        // compiler from sinking the refill below the arithmetic.
-        u32x4 c[TPW];
-        float s[TPW], m[TPW];
-        if (PAIR) {
-            // q = (g - cs) % RING with cs and RING even: pair slot q / 2, and
-            // the group's place in its pair is q % 2.
-            if ((q & 1) == 0) {
-                const int pq = q >> 1;
-                c[0] = lane_gather(merge_rows(cb[pq][0], cb2[pq], false), src_e);
-                codd = lane_gather(merge_rows(cb[pq][0], cb2[pq], true), src_o);
-                fetch(pq, min(g + RING, ce - 2));
-            } else {
-                c[0] = codd;
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < TPW; ++u) {
-                c[u] = lane_gather(cb[q][u], src);
-                if (!VSM) {                       // scale and minimum ride in the same slot
-                    s[u] = bf16_lo(sb[q][u]);
-                    m[u] = bf16_lo(mb[q][u]);
-                }
-            }
-            fetch(q, min(g + RING, ce - 1));
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        xsum = *reinterpret_cast<const f32x4 *>(xrow + lg * kXsRows);
+    }
+
+    // Group g's arithmetic once its code pieces c are in the MFMA lanes.
+    __device__ __forceinline__ void arith(const u32x4 (&a)[4], const f32x4 &xsum, const u32x4 (&c)[TPW],
+                                          float (&s)[TPW], float (&m)[TPW], int ce, int g, int set, int j,
+                                          UnpackConsts uc)
+    {
         u32x4 bq[TPW][4];
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
@@ -209,6 +186,53 @@ struct Tile {
                 acc[u][r] = fmaf(m_adj, xsum[r], acc[u][r]);
             }
         }
+    }
+
+    // Group g (LDS group index lg) from ring slot q; `set`/`j` locate its
+    // scale and minimum (VSM).  PAIR: the call for the first group of a pair
+    // (q even) does both groups; the call for the second does nothing.
+    __device__ __forceinline__ void group(const uint16_t *rbase, const int (&aoff)[4], const float *xrow,
+                                          int ce, int q, int g, int lg, int set, int j, UnpackConsts uc)
+    {
+        if (PAIR && (q & 1)) return;
+        u32x4 a[4];
+        f32x4 xsum;
+        xread(rbase, aoff, xrow, lg, a, xsum);
+        // Take the ring slot out (the gather reads it), then refill it at once
+        // so RING groups stay in flight; the scheduling barrier keeps the
+        // compiler from sinking the refill below the arithmetic.
+        u32x4 c[TPW];
+        float s[TPW], m[TPW];
+        if (PAIR) {
+            // q = (g - cs) % RING with cs and RING even: pair slot q / 2.
+            const int pq = q >> 1;
+            u32x4 c2[TPW];
+            // The columns 8-15 load holds the pair's second group in lanes
+            // 8c..8c+3 and its first in 8c+4..8c+7 (the mirror of the columns
+            // 0-7 load), so each group's pieces are a per-lane choice between
+            // the two loads, then one permute.
+            const bool lo = (i & 4) == 0;
+            c[0] = lane_gather(pick(lo, cb[pq][0], cb2[pq]), src_e);
+            c2[0] = lane_gather(pick(lo, cb2[pq], cb[pq][0]), src_o);
+            fetch(pq, min(g + RING, ce - 2));
+            __builtin_amdgcn_sched_barrier(0);
+            arith(a, xsum, c, s, m, ce, g, set, j, uc);
+            __builtin_amdgcn_sched_barrier(0);              // keeps the second group's x reads here (registers)
+            xread(rbase, aoff, xrow, lg + 1, a, xsum);     // the pair's second group: g + 1, slot j + 1
+            arith(a, xsum, c2, s, m, ce, g + 1, set, j + 1, uc);
+            return;
+        }
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            c[u] = lane_gather(cb[q][u], src);
+            if (!VSM) {                           // scale and minimum ride in the same slot
+                s[u] = bf16_lo(sb[q][u]);
+                m[u] = bf16_lo(mb[q][u]);
+            }
+        }
+        fetch(q, min(g + RING, ce - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        arith(a, xsum, c, s, m, ce, g, set, j, uc);
     }
 
     // Groups [cs, ce) of x staged in LDS for the groups [xg0, xg0 + xng)
@@ -315,8 +339,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
     T.src = 4 * T.i + T.h;
     T.src_e = 8 * (T.i & 7) + 4 * (T.i >> 3) + T.h;   // paired loads (see the balanced kernel)
     T.src_o = 8 * (T.i & 7) + 4 * (1 - (T.i >> 3)) + T.h;
-    if (PR) {                                     // columns lane / 8 and 8 + lane / 8, bytes 16 * (lane % 8)
-        T.vw2 = (uint32_t)((size_t)min(8 + (lane >> 3), ncols - 1) * T.K8 * 4 + 16 * (lane & 7));
+    if (PR) {                                     // columns lane / 8 and 8 + lane / 8 (halves mirrored)
+        T.vw2 = (uint32_t)((size_t)min(8 + (lane >> 3), ncols - 1) * T.K8 * 4 + 16 * ((lane ^ 4) & 7));
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
@@ -424,9 +448,9 @@ struct BalTile : Tile<1, true, RING, SML, PAD, PAIR, RL> {
         this->rw = make_rsrc(W + (size_t)cbase * this->K8, (uint32_t)(span * this->K8 * 4));
         this->rs = make_rsrc(scale + (size_t)cbase * this->G, (uint32_t)(span * this->G * 2));
         this->rm = make_rsrc(mn + (size_t)cbase * this->G, (uint32_t)(span * this->G * 2));
-        if (PAIR) {                                        // columns (lane / 8) and 8 + (lane / 8), bytes 16 * (lane % 8)
+        if (PAIR) {                                        // columns lane / 8 and 8 + lane / 8 (halves mirrored)
             this->vw[0] = (uint32_t)((size_t)colmap(la >> 1) * this->K8 * 4 + 16 * (4 * (la & 1) + lb));
-            this->vw2 = (uint32_t)((size_t)colmap(8 + (la >> 1)) * this->K8 * 4 + 16 * (4 * (la & 1) + lb));
+            this->vw2 = (uint32_t)((size_t)colmap(8 + (la >> 1)) * this->K8 * 4 + 16 * ((lane_id() ^ 4) & 7));
         } else {
             this->vw[0] = (uint32_t)((size_t)colmap(la) * this->K8 * 4 + 16 * lb);
         }
@@ -567,10 +591,10 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     B.la = lane >> 2;
     B.lb = lane & 3;
     B.src = 4 * B.i + B.h;
-    // Paired loads: column i's bytes of the pair's first group sit in lanes
-    // 8*(i%8) + h of the columns-(i/8) load; the row-shift merge moves the
-    // columns 8-15 pieces to lanes 8*(i%8) + 4 + h (first group) and 8*(i%8) + h
-    // (second group), beside the columns 0-7 pieces they do not collide with.
+    // Paired loads: piece h of column i < 8 sits in lane 8i + h (first group)
+    // and 8i + 4 + h (second group) of the columns 0-7 load; piece h of column
+    // i >= 8 in lane 8(i-8) + 4 + h (first) and 8(i-8) + h (second) of the
+    // mirrored columns 8-15 load.
     B.src_e = 8 * (B.i & 7) + 4 * (B.i >> 3) + B.h;
     B.src_o = 8 * (B.i & 7) + 4 * (1 - (B.i >> 3)) + B.h;
     B.M = M;
