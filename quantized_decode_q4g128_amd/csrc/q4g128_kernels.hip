@@ -64,9 +64,10 @@ namespace q4g128 {
 // second group come out of the two loads by a per-lane select and one lane
 // permute each, so every MFMA sees the same operands as with one group per
 // load.
-// RL: D rows per lane that are accumulated (4, or 1 when M = 1: lane i + 16h
-// holds rows 4h..4h+3 and only row 0 is ever stored).  A row's instructions
-// do not depend on RL, so its bits do not either.
+// RL: D rows per lane that are accumulated: 4; 2 when M <= 8 (x rows 0..7 sit
+// in the first two D rows of each lane, see rowpos); 1 when M = 1 (only D
+// row 0 of lane i is ever stored).  A row's instructions do not depend on RL,
+// so its bits do not either.
 template <int TPW, bool VSM, int RING, bool SML = false, bool PAD = false, bool PAIR = false, int RL = 4>
 struct Tile {
     // PAD (with VSM): the range may end inside an 8-group block; groups past
@@ -242,7 +243,7 @@ struct Tile {
     {
         const UnpackConsts uc = unpack_consts();
         const int ng = ce - cs;
-        const int arow = min(i, M - 1);          // rows >= M read a real row; never stored
+        const int arow = min(kRowPerm ? rowof(i) : i, M - 1);   // rows >= M read a real row; never stored
         const uint16_t *rbase = xs + arow * xng * 128;
         const float *xrow = reinterpret_cast<const float *>(xs + M * xng * 128) + 4 * h;
         const int lg0 = cs - xg0;                // LDS group index of cs
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
     }
 
     if (!CHUNKED) {
-        XStage<64 * WAVES, kStageMax> xst;
+        XStage<64 * WAVES, kStageMax, kRowPerm> xst;
         xst.load(x, M, K, T.gs, T.ge);
         T.prime(T.gs, T.ge);
         xst.store(xs, M, T.gs, T.ge);
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
     } else {
         for (int cs = T.gs; cs < T.ge; cs += CG) {
             const int ce = min(cs + CG, T.ge);
-            XStage<64 * WAVES, kStageMax> xst;
+            XStage<64 * WAVES, kStageMax, kRowPerm> xst;
             xst.load(x, M, K, cs, ce);
             T.prime(cs, ce);
             xst.store(xs, M, cs, ce);
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
         if (n < N) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = 4 * T.h + r;
+                const int row = kRowPerm ? rowof(4 * T.h + r) : 4 * T.h + r;
                 if (row < M) o[(size_t)row * N + n] = T.acc[u][r];
             }
         }
@@ -500,7 +501,7 @@ struct BalTile : Tile<1, true, RING, SML, PAD, PAIR, RL> {
         if (this->i < ncols) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = 4 * this->h + r;
+                const int row = kRowPerm ? rowof(4 * this->h + r) : 4 * this->h + r;
                 if (row < this->M)
                     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, this->acc[0][r]), ry,
                                                           (uint32_t)(row * N + n) * 4, 0, 0);
@@ -519,7 +520,7 @@ struct BalTile : Tile<1, true, RING, SML, PAD, PAIR, RL> {
         if (this->i < wact) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = 4 * this->h + r;
+                const int row = kRowPerm ? rowof(4 * this->h + r) : 4 * this->h + r;
                 if (row < this->M) act[(size_t)row * NC + cbase + this->i] = swiglu_bf16(this->acc[0][r], u[r]);
             }
         }
@@ -622,7 +623,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
         cs = PARTS ? gs + ((p * (ng >> 3)) / P) * 8 : gs;
         ce = PARTS ? gs + (((p + 1) * (ng >> 3)) / P) * 8 : ge;
     };
-    XStage<kBalThreads, kBalStage> xst;
+    XStage<kBalThreads, kBalStage, kRowPerm> xst;
     xst.load(x, M, K, gs, ge);
     xst.store(xs, M, gs, ge);
     lds_barrier();
@@ -967,12 +968,13 @@ static hipError_t launch_bal_rl(const GemvArgs &a, int gx, int P, hipStream_t st
                    : launch_bal_v<PARTS, ACT, RL, false>(a, gx, P, bp, stream);
 }
 
-// One row accumulates one D row per lane; more rows all four.
+// One row accumulates one D row per lane, up to 8 rows two (rowpos), more all four.
 template <bool PARTS, bool ACT>
 static hipError_t launch_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)
 {
-    return (kBalOneRow && a.M == 1) ? launch_bal_rl<PARTS, ACT, 1>(a, gx, P, stream)
-                                     : launch_bal_rl<PARTS, ACT, 4>(a, gx, P, stream);
+    if (kBalOneRow && a.M == 1) return launch_bal_rl<PARTS, ACT, 1>(a, gx, P, stream);
+    if (kRowPerm && a.M <= 8) return launch_bal_rl<PARTS, ACT, 2>(a, gx, P, stream);
+    return launch_bal_rl<PARTS, ACT, 4>(a, gx, P, stream);
 }
 
 hipError_t launch_gemv_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)

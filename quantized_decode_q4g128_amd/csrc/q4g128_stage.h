@@ -44,6 +44,18 @@ __device__ __forceinline__ float row16_sum(float v)
     return v;
 }
 
+// MFMA row of x row m (0..15) and its inverse.  Rows 0..7 take MFMA rows 4h
+// and 4h + 1 (h = 0..3), rows 8..15 MFMA rows 4h + 2 and 4h + 3: lane
+// i + 16h holds D rows 4h..4h+3, so x rows 0..7 land in the first two D rows
+// of every lane and an M <= 8 product accumulates two D rows per lane, not
+// four.  Every x row sits in the same MFMA row for every M.
+__device__ __forceinline__ int rowpos(int m) { return m < 8 ? 4 * (m >> 1) + (m & 1) : 4 * ((m - 8) >> 1) + 2 + (m & 1); }
+__device__ __forceinline__ int rowof(int j)
+{
+    const int h = j >> 2, r = j & 3;
+    return r < 2 ? 2 * h + r : 8 + 2 * h + (r - 2);
+}
+
 // Stage x[0..M)[cs*128 .. ce*128) into LDS (swizzled, pair order) and the
 // row sums Xs[g - cs][row] of each 128-group.  Piece p is 16 bytes: row
 // p / pr, block p % pr, pr = 16 * (ce - cs); the 16 pieces of one (row,
@@ -53,7 +65,9 @@ __device__ __forceinline__ float row16_sum(float v)
 // load() issues the global reads; store() waits for them and writes LDS.
 // Loads issued between the two (the first code loads) stay in flight: the
 // wait only covers memory operations older than them.
-template <int NT, int SMAX>
+// RP: row m's sums go to MFMA row rowpos(m) (the product kernels place x row
+// m there); else to row m.
+template <int NT, int SMAX, bool RP = false>
 struct XStage {
     u32x4 st[SMAX];
     int pieces, pr;
@@ -95,7 +109,7 @@ struct XStage {
                 part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, part, false);
                 part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, part, false);
                 const float tot = row16_sum(part);
-                if ((tid & 15) == 15 && pu < pieces) Xs[(blk >> 4) * kXsRows + row] = tot;
+                if ((tid & 15) == 15 && pu < pieces) Xs[(blk >> 4) * kXsRows + (RP ? rowpos(row) : row)] = tot;
             }
         }
     }
