@@ -461,15 +461,19 @@ struct BalTile : Tile<1, true, RING, SML, PAD, PAIR, RL> {
     }
 
     // Scale/minimum pieces (16 bytes = 8 groups of one column) of the tile's
-    // K range: piece q = column q / nblk, block q % nblk; lane takes q = lane + 64r.
+    // K range: slot q = lane + 64r holds column q >> sh, block q & (2^sh - 1),
+    // 2^sh the least power of two >= nblk (slots past nblk idle), so no lane
+    // divides by nblk.
+    __device__ __forceinline__ int sm_shift() const { return nblk <= 1 ? 0 : nblk <= 2 ? 1 : nblk <= 4 ? 2 : 3; }
+
     __device__ __forceinline__ void sm_load(u32x4 (&sr)[kBalSmRounds], u32x4 (&mr)[kBalSmRounds], int lane) const
     {
-        const int pieces = ncols * nblk;
+        const int sh = sm_shift();
 #pragma unroll
         for (int r = 0; r < kBalSmRounds; ++r) {
-            if (64 * r < pieces) {                         // wave-uniform
-                const int q = min(lane + 64 * r, pieces - 1);
-                const int col = q / nblk, b = q - col * nblk;
+            if (64 * r < (ncols << sh)) {                  // wave-uniform
+                const int q = lane + 64 * r;
+                const int col = min(q >> sh, ncols - 1), b = min(q & ((1 << sh) - 1), nblk - 1);   // idle: a real piece
                 const uint32_t off = (uint32_t)(((size_t)colmap(col) * this->G + this->gs + 8 * b) * 2);
                 sr[r] = __builtin_amdgcn_raw_buffer_load_b128(this->rs, off, 0, 0);
                 mr[r] = __builtin_amdgcn_raw_buffer_load_b128(this->rm, off, 0, 0);
@@ -480,13 +484,13 @@ struct BalTile : Tile<1, true, RING, SML, PAD, PAIR, RL> {
     __device__ __forceinline__ void sm_store(const u32x4 (&sr)[kBalSmRounds], const u32x4 (&mr)[kBalSmRounds],
                                              int lane) const
     {
-        const int pieces = ncols * nblk;
         uint16_t *dst = const_cast<uint16_t *>(this->sml);
+        const int sh = sm_shift();
 #pragma unroll
         for (int r = 0; r < kBalSmRounds; ++r) {
             const int q = lane + 64 * r;
-            if (64 * r < pieces && q < pieces) {
-                const int col = q / nblk, b = q - col * nblk;
+            const int col = q >> sh, b = q & ((1 << sh) - 1);
+            if (64 * r < (ncols << sh) && col < ncols && b < nblk) {
                 *reinterpret_cast<u32x4 *>(dst + (col * this->nbl + b) * 8) = sr[r];
                 *reinterpret_cast<u32x4 *>(dst + ((16 + col) * this->nbl + b) * 8) = mr[r];
             }
