@@ -564,6 +564,12 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     const int gs = (split * nb / S) * 8;
     const int ge = ((split + 1) * nb / S) * 8;
     const int ng = ge - gs;
+    // x first, and alone: every wave's code and scale/minimum loads wait until
+    // the workgroup's x is in LDS.  Issued together, its few kilobytes queue
+    // behind megabytes of weight requests from all CUs, and the barrier waits
+    // for the slowest wave's x.  Its loads go out before any other set-up.
+    XStage<kBalThreads, kBalStage, kRowPerm> xst;
+    xst.load(x, M, K, gs, ge);
     const int gx = gridDim.x;
     // Workgroups are dealt to the 8 XCDs in turn (c -> XCD c % 8); numbering
     // them XCD by XCD before cutting the column range gives every XCD the same
@@ -574,8 +580,13 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     // N = 5120: 20 each); ACT: pair-columns of I = N/2, likewise (68 pairs).
     const int NC = ACT ? (N >> 1) : N;
     const int NU = (NC + 3) >> 2;
-    const int n0 = (int)((long)c * NU / gx) * 4;
-    const int n1 = min((int)((long)(c + 1) * NU / gx) * 4, NC);
+    // (32-bit division where c * NU cannot overflow: a 64-bit one costs the
+    // set-up some hundred instructions.)
+    const bool n32 = NU < (1 << 22) && gx <= 1024;
+    const int n0 = n32 ? (int)((unsigned)c * (unsigned)NU / (unsigned)gx) * 4 : (int)((long)c * NU / gx) * 4;
+    const int n1 = min(n32 ? (int)((unsigned)(c + 1) * (unsigned)NU / (unsigned)gx) * 4
+                           : (int)((long)(c + 1) * NU / gx) * 4,
+                       NC);
     // Tiles of at most TW columns (ACT: pairs), as few as that allows, of
     // equal widths: tile k covers [n0 + k*width/nchunk, n0 + (k+1)*width/nchunk).
     // (136 columns make 9 tiles of 15-16 columns rather than 8 of 16 and one
@@ -613,10 +624,6 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     float *slots = reinterpret_cast<float *>(xs + M * ng * 128 + ng * kXsRows * 2);
     B.sml = xs + M * ng * 128 + ng * kXsRows * 2 + nps * 512 + wave * (2 * 16 * nblp * 8);
 
-    // x first, and alone: every wave's code and scale/minimum loads wait until
-    // the workgroup's x is in LDS.  Issued together, its few kilobytes queue
-    // behind megabytes of weight requests from all CUs, and the barrier waits
-    // for the slowest wave's x.
     // A unit's column base and group range.
     auto unit = [&](int u, int &cb, int &cw, int &cs, int &ce) {
         const int k = PARTS ? u / P : u;
@@ -627,8 +634,6 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
         cs = PARTS ? gs + ((p * (ng >> 3)) / P) * 8 : gs;
         ce = PARTS ? gs + (((p + 1) * (ng >> 3)) / P) * 8 : ge;
     };
-    XStage<kBalThreads, kBalStage, kRowPerm> xst;
-    xst.load(x, M, K, gs, ge);
     xst.store(xs, M, gs, ge);
     lds_barrier();
     if (!PARTS && !active) return;
