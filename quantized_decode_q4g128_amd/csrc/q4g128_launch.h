@@ -107,11 +107,11 @@ constexpr int kPairCpol = Q4G128_PAIR_CPOL;
 #ifndef Q4G128_BAL_ONEROW
 #define Q4G128_BAL_ONEROW 1
 #endif
-constexpr bool kBalOneRow = Q4G128_BAL_ONEROW;
+constexpr bool kBalOneRow = Q4G128_BAL_ONEROW;   // M = 1: accumulate only the one D row per lane that is stored
 #ifndef Q4G128_ROWPERM
 #define Q4G128_ROWPERM 1
 #endif
-constexpr bool kRowPerm = Q4G128_ROWPERM;   // x row m in MFMA row rowpos(m) (product kernels)   // M = 1: accumulate only the one D row per lane that is stored
+constexpr bool kRowPerm = Q4G128_ROWPERM;   // x row m in MFMA row rowpos(m) (product kernels)
 constexpr int kBalThreads = 64 * kBalWaves;
 constexpr int kBalStage = 8;                // x pieces per thread: M * ng * 16 <= 6144 (M = 8 at K = 6144, 9 at 5120)
 constexpr int kBalSmRounds = 2;             // scale/min pieces per lane: 16 * nblk <= 128, nblk <= 8
