@@ -72,17 +72,36 @@ struct XStage {
     u32x4 st[SMAX];
     int pieces, pr;
 
+    // Piece tid + NT*j lies at (row0 + j*dq + carries, blk0 + j*dr - carries*pr):
+    // one division per thread, then an add and a compare per round.
+    int row0, blk0, dq, dr;
+
     __device__ __forceinline__ void load(const uint16_t *__restrict__ x, int M, int K, int cs, int ce)
     {
         const int tid = threadIdx.x;
         pr = (ce - cs) * 16;
         pieces = M * pr;
+        row0 = tid / pr;
+        blk0 = tid - row0 * pr;
+        dq = NT / pr;
+        dr = NT - dq * pr;
+        int row = row0, blk = blk0;
 #pragma unroll
         for (int j = 0; j < SMAX; ++j) {
-            if (NT * j < pieces) {            // workgroup-uniform
-                const int p = min(tid + NT * j, pieces - 1);
-                const int row = p / pr, blk = p - row * pr;
-                st[j] = *reinterpret_cast<const u32x4 *>(x + (size_t)row * K + (size_t)cs * 128 + blk * 8);
+            if (NT * j >= pieces) break;      // workgroup-uniform
+            {
+                int r = row, b = blk;
+                if (tid + NT * j >= pieces) {   // past the end: the last piece
+                    r = M - 1;
+                    b = pr - 1;
+                }
+                st[j] = *reinterpret_cast<const u32x4 *>(x + (size_t)r * K + (size_t)cs * 128 + b * 8);
+            }
+            row += dq;
+            blk += dr;
+            if (blk >= pr) {
+                blk -= pr;
+                ++row;
             }
         }
     }
@@ -94,12 +113,13 @@ struct XStage {
         const int ng = ce - cs;
         float *Xs = reinterpret_cast<float *>(xs + M * ng * 128);
         const bf16x2 ones = __builtin_bit_cast(bf16x2, kOnePair);
+        int prow = row0, pblk = blk0;
 #pragma unroll
         for (int j = 0; j < SMAX; ++j) {
-            if (NT * j < pieces) {
+            if (NT * j >= pieces) break;      // workgroup-uniform
+            {
                 const int pu = tid + NT * j;
-                const int p = min(pu, pieces - 1);
-                const int row = p / pr, blk = p - row * pr;
+                const int row = pu < pieces ? prow : M - 1, blk = pu < pieces ? pblk : pr - 1;
                 *reinterpret_cast<u32x4 *>(&xs[(row * pr + swz(blk, row)) * 8]) = pair_order(st[j]);
                 // Each element goes through a scalar before the bit cast: this
                 // compiler bit-casts a vector element expression as element 0.
@@ -110,6 +130,12 @@ struct XStage {
                 part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, part, false);
                 const float tot = row16_sum(part);
                 if ((tid & 15) == 15 && pu < pieces) Xs[(blk >> 4) * kXsRows + (RP ? rowpos(row) : row)] = tot;
+            }
+            prow += dq;
+            pblk += dr;
+            if (pblk >= pr) {
+                pblk -= pr;
+                ++prow;
             }
         }
     }
