@@ -550,8 +550,9 @@ struct BalTile : Tile<1, true, RING, SML, PAD, PAIR, RL, kPairCpol> {
 // registers and bf16 silu(gate) * up goes straight to act [M][I].  The
 // per-column sums are those of the plain product.
 // PAIR: codes loaded two groups at a time (see Tile); the plan takes it for
-// workgroups with many tiles, where it streams faster, and leaves it off for
-// a few tiles per CU, where it streamed slower.  It never changes a bit.
+// workgroups of 4 or more units, where it streams faster, and leaves it off
+// for 3 or fewer tiles per CU, where it streamed slower.  It never changes a
+// bit.
 template <int RING, bool SML, bool PARTS, bool ACT, int RL, bool PAIR>
 __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,

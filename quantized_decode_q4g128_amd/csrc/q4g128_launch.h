@@ -94,10 +94,14 @@ constexpr bool kBalSml = Q4G128_BAL_SML;    // scales/minimums staged in LDS per
 #define Q4G128_BAL_PAIR 1
 #endif
 constexpr bool kBalPair = Q4G128_BAL_PAIR;  // codes loaded two groups (128 B per column) at a time
-// ... for workgroups of at least this many (tile, K part) units: with 3 tiles
-// per CU (5120 -> 12288) the paired loads streamed 4% slower, with 9 or more
-// 1-13% faster.
-constexpr int kBalPairUnits = 8;
+// ... for workgroups of at least this many (tile, K part) units.  K = 5120,
+// tiles per CU (us, paired / one group per load): 3: 11.31 / 10.35;
+// 4: 11.70 / 11.80; 5: 13.73 / 14.30; 6: 14.45 / 16.28; 7: 15.56 / 18.35;
+// 8.5 (gate/up) and the 131072-wide output projection: 1-13% faster paired.
+#ifndef Q4G128_PAIR_UNITS
+#define Q4G128_PAIR_UNITS 4
+#endif
+constexpr int kBalPairUnits = Q4G128_PAIR_UNITS;
 #ifndef Q4G128_PAIR_CPOL
 #define Q4G128_PAIR_CPOL 2
 #endif
