@@ -58,6 +58,7 @@ import synth  # noqa: E402
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 PEAK_FP64_TFLOPS = 78.6         # MI355X fp64 vector peak
 ROTATE_BYTES = 1.2e9            # > 4x the 256 MB last-level cache
+WARM_S = 0.2                    # untimed launches before every timed leg, seconds
 METRIC = "achieved HBM GB/s (% of MI355X peak) for int4-g128 GEMV at M=1 and M=7"
 KERNEL = "gemv_q4g128"          # the dominant (only) kernel of a decode step
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_q4g128_gateup_pmc.txt")
@@ -149,11 +150,27 @@ class RawCalls:
         return next(y for c, y in self.ys if c is calls)
 
 
-def timed_calls(torch, seq, reps, warmup):
+def warm_up(torch, seq, seconds=WARM_S):
+    """Passes over `seq` for about `seconds`: the first passes over freshly
+    allocated weight copies run slower than the steady state, and an idle GPU
+    starts at low clocks."""
+    st = torch.cuda.current_stream().cuda_stream
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for c in seq:
+            if c(st) != 0:
+                raise RuntimeError("launch failed")
+        torch.cuda.synchronize()
+
+
+def timed_calls(torch, seq, reps, warmup, warm_s=WARM_S):
     """Milliseconds for `reps` passes over the launch sequence `seq`, bracketed
-    by HIP events on the launching stream."""
+    by HIP events on the launching stream, after `warm_s` seconds and
+    `warmup` passes of untimed launches."""
     stream = torch.cuda.current_stream()
     st = stream.cuda_stream
+    if warm_s > 0:
+        warm_up(torch, seq, warm_s)
     for _ in range(warmup):
         for c in seq:
             if c(st) != 0:
