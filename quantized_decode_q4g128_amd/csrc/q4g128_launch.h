@@ -111,7 +111,7 @@ constexpr int kPairCpol = Q4G128_PAIR_CPOL;
 #ifndef Q4G128_BAL_ONEROW
 #define Q4G128_BAL_ONEROW 1
 #endif
-constexpr bool kBalOneRow = Q4G128_BAL_ONEROW;   // M = 1: accumulate only the one D row per lane that is stored
+constexpr bool kBalOneRow = Q4G128_BAL_ONEROW;   // M <= 4: accumulate only the one D row per lane that is stored
 #ifndef Q4G128_ROWPERM
 #define Q4G128_ROWPERM 1
 #endif

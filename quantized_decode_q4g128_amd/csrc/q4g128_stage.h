@@ -44,17 +44,13 @@ __device__ __forceinline__ float row16_sum(float v)
     return v;
 }
 
-// MFMA row of x row m (0..15) and its inverse.  Rows 0..7 take MFMA rows 4h
-// and 4h + 1 (h = 0..3), rows 8..15 MFMA rows 4h + 2 and 4h + 3: lane
-// i + 16h holds D rows 4h..4h+3, so x rows 0..7 land in the first two D rows
-// of every lane and an M <= 8 product accumulates two D rows per lane, not
-// four.  Every x row sits in the same MFMA row for every M.
-__device__ __forceinline__ int rowpos(int m) { return m < 8 ? 4 * (m >> 1) + (m & 1) : 4 * ((m - 8) >> 1) + 2 + (m & 1); }
-__device__ __forceinline__ int rowof(int j)
-{
-    const int h = j >> 2, r = j & 3;
-    return r < 2 ? 2 * h + r : 8 + 2 * h + (r - 2);
-}
+// MFMA row of x row m (0..15) and its inverse: x row m = 4r + h sits in MFMA
+// row 4h + r.  Lane i + 16h holds D rows 4h..4h+3, so x rows 0..3 land in the
+// first D row of the four lane groups, rows 4..7 in the second, and so on:
+// an M-row product accumulates ceil(M/4) D rows per lane, not four.  Every
+// x row sits in the same MFMA row for every M.
+__device__ __forceinline__ int rowpos(int m) { return 4 * (m & 3) + (m >> 2); }
+__device__ __forceinline__ int rowof(int j) { return 4 * (j & 3) + (j >> 2); }
 
 // Stage x[0..M)[cs*128 .. ce*128) into LDS (swizzled, pair order) and the
 // row sums Xs[g - cs][row] of each 128-group.  Piece p is 16 bytes: row
