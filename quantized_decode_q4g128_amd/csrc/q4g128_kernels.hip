@@ -64,10 +64,9 @@ namespace q4g128 {
 // second group come out of the two loads by a per-lane select and one lane
 // permute each, so every MFMA sees the same operands as with one group per
 // load.
-// RL: D rows per lane that are accumulated: 4; 2 when M <= 8 and 1 when
-// M <= 4 (x rows 0..3 sit in the first D row of each lane, rows 4..7 in the
-// second, see rowpos).  A row's instructions do not depend on RL, so its
-// bits do not either.
+// RL: D rows per lane that are accumulated, ceil(M/4) (x rows 0..3 sit in
+// the first D row of each lane, rows 4..7 in the second, ..., see rowpos).
+// A row's instructions do not depend on RL, so its bits do not either.
 // CP: cache policy of the one-group-per-load code loads (the paired ones
 // always carry the non-temporal hint).
 template <int TPW, bool VSM, int RING, bool SML = false, bool PAD = false, bool PAIR = false, int RL = 4,
@@ -983,12 +982,13 @@ static hipError_t launch_bal_rl(const GemvArgs &a, int gx, int P, hipStream_t st
                    : launch_bal_v<PARTS, ACT, RL, false>(a, gx, P, bp, stream);
 }
 
-// Up to 4 rows accumulate one D row per lane, up to 8 two (rowpos), more all four.
+// Rows accumulate ceil(M/4) D rows per lane (rowpos).
 template <bool PARTS, bool ACT>
 static hipError_t launch_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)
 {
     if (kBalOneRow && (a.M == 1 || (kRowPerm && a.M <= 4))) return launch_bal_rl<PARTS, ACT, 1>(a, gx, P, stream);
     if (kRowPerm && a.M <= 8) return launch_bal_rl<PARTS, ACT, 2>(a, gx, P, stream);
+    if (kRowPerm && a.M <= 12) return launch_bal_rl<PARTS, ACT, 3>(a, gx, P, stream);
     return launch_bal_rl<PARTS, ACT, 4>(a, gx, P, stream);
 }
 
