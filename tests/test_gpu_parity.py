@@ -228,16 +228,20 @@ def test_rows_bit_identical_across_kernel_choice(K, N):
 # 8192, N = 777 the balanced kernel cuts K into 2 parts and holds 6 rows per
 # launch; 17408 -> 5120 (5 parts, 2 rows per launch) runs with its default
 # splits (one launch for M <= 2, 5 K splits beyond); 6144 -> 5120 (2 parts,
-# 8 rows per launch) without splits.
+# 8 rows per launch) without splits.  5120 -> 12288 (3 tiles per CU: the
+# balanced kernel loads one group per load) and 5120 -> 20480 (5 tiles per
+# CU: two groups per load) tie both load patterns of the balanced kernel to
+# the per-tile kernel's paired loads (M >= 10), and M = 3, 4, 5, 12, 13 cross
+# the 1-, 2-, 3- and 4-row accumulation of the balanced kernel.
 @pytest.mark.parametrize("K,N,split", [(5120, 34816, False), (8192, 777, False), (17408, 5120, True),
-                                       (6144, 5120, False)])
+                                       (6144, 5120, False), (5120, 12288, False), (5120, 20480, False)])
 def test_rows_bit_identical_up_to_16_rows(K, N, split):
-    case = synth.make_random(16, K, N, 60 + K // 1024, outlier_frac=0.01)
+    case = synth.make_random(16, K, N, 60 + K // 1024 + N % 1000, outlier_frac=0.01)
     W, s, m = dev_weights(case.weights)
     x16 = dev_x(case.x)
     f = q.q4g128_gemm_splitk if split else q.q4g128_gemm
     y16 = host_f32(f(x16, W, s, m))
-    for M in (1, 2, 5, 8, 9, 10, 12, 15):
+    for M in (1, 2, 3, 4, 5, 8, 9, 10, 12, 13, 15):
         yM = host_f32(f(x16[:M].contiguous(), W, s, m))
         assert np.array_equal(bits(yM), bits(y16[:M])), M
 
