@@ -26,9 +26,10 @@
  * Arithmetic: fp32 accumulation.  For every (K, N) the library fixes one
  * summation order that is the same for every M and every row, so row m of an
  * M-row call equals the one-row call on x[m] bit for bit (bw24 article,
- * exactness paragraph: verify must agree exactly with decode, and summation
- * order is part of the contract).  Results are deterministic run to run; the
- * library uses no atomics on results.
+ * exactness paragraph: a verify pass may only be accepted if it reproduces
+ * plain decode exactly, and two reductions that differ only in the order of
+ * their additions can already break that).  Results are deterministic run to
+ * run; the library uses no atomics on results.
  *
  * Conventions for every call below:
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
@@ -37,14 +38,18 @@
  *     K <= 0, K > 2^24 or K % 128 != 0, N <= 0 or N > 2^28, splits > 65535,
  *     x or W or w_out not 16-byte aligned,
  *     scale or min not 2-byte aligned, y or workspace not 4-byte aligned,
- *     splits outside [1, ceil(K/1024)]) or Q4G128_EWORKSPACE (workspace too
- *     small),
+ *     splits outside [1, K/128]) or Q4G128_EWORKSPACE (workspace too small),
  *     always before anything is enqueued.
  *   - A failed kernel launch returns Q4G128_EHIP; q4g128_last_error() then
- *     holds the HIP error text for the calling thread.
- *   - Outputs must not alias inputs.  The library allocates no memory, keeps
- *     no mutable global state and is safe to call from several threads; a
- *     split-K workspace must not be shared by calls in flight at once.
+ *     holds the HIP error text for the calling thread.  An error left pending
+ *     on the thread by an earlier, unrelated HIP call is cleared before this
+ *     call's launches, so EHIP always reports this call's own launches.
+ *   - Outputs must not alias inputs.  The library allocates no memory and is
+ *     safe to call from several threads: its only host-side state is
+ *     per-device caches of device properties and kernel attributes, held in
+ *     atomics and written with the same value by every thread that fills
+ *     them.  A split-K workspace must not be shared by calls in flight at
+ *     once.
  */
 #ifndef Q4G128_H
 #define Q4G128_H
@@ -78,13 +83,18 @@ q4g128_status q4g128_gemm(const void *x, int M, int K,
                           int N, float *y, void *stream);
 
 /* Bytes of workspace q4g128_gemm_splitk needs: splits * M * N * 4 (fp32
- * partial sums P[s][m][n]).  Returns 0 for invalid arguments. */
+ * partial sums P[s][m][n], one slice per split).  Returns 0 for invalid
+ * arguments.  Passage: Token Rush README, steps table rows 8-9 (a split-K
+ * GEMV: each K range leaves a partial sum that is added up afterwards). */
 size_t q4g128_splitk_workspace_bytes(int M, int N, int splits);
 
 /* Split count the library recommends for a (K, N) shape: a function of K, N
  * and the current device's compute-unit count only (never of M, so rows
- * stay bit-identical across M).  1 means "do not split"; returns 0 for
- * invalid K or N. */
+ * stay bit-identical across M), always whole blocks of 8 groups.  1 means
+ * "do not split"; returns 0 for invalid K or N.  Passages: Token Rush README,
+ * steps table rows 8-9 (split-K for the short-N projections) and bandwidth
+ * paragraph (decode runs at the rate the weights stream, so a short-N shape
+ * is split until every compute unit has enough of them in flight). */
 int q4g128_splitk_default_splits(int K, int N);
 
 /* K parts of q4g128_gemm's one-launch form for a (K, N) shape on the
@@ -93,13 +103,15 @@ int q4g128_splitk_default_splits(int K, int N);
  * of K, N and the compute-unit count; 0 for invalid K or N. */
 int q4g128_gemm_parts(int K, int N);
 
-/* The product with K cut into `splits` contiguous ranges of whole blocks of
- * 8 groups (1024 k): with nb = ceil(K/1024) blocks, split s covers blocks
- * [s*nb/splits, (s+1)*nb/splits), so 1 <= splits <= nb.  Each
- * range writes fp32 partial sums to the workspace; a second pass sums them
- * in ascending s into y.  Deterministic; for splits == 1 it computes exactly
- * what q4g128_gemm computes.  For short N, where one column per lane gives
- * too little parallelism.  Passage: Token Rush README, steps table rows 8-9
+/* The product with K cut into `splits` contiguous ranges, 1 <= splits <=
+ * K/128.  With nb = ceil(K/1024) blocks of 8 groups and splits <= nb, split s
+ * covers blocks [s*nb/splits, (s+1)*nb/splits); with more splits than
+ * blocks, split s covers the groups [s*G/splits, (s+1)*G/splits), G = K/128
+ * (every split at least one group).  Each range writes fp32 partial sums to
+ * the workspace; a second pass sums them in ascending s into y.
+ * Deterministic; for splits == 1 it computes exactly what q4g128_gemm
+ * computes.  For short N, where one column per lane gives too little
+ * parallelism.  Passage: Token Rush README, steps table rows 8-9
  * (a split-K GEMV whose partial sums are added afterwards). */
 q4g128_status q4g128_gemm_splitk(const void *x, int M, int K,
                                  const uint32_t *W, const void *scale, const void *min,
@@ -207,8 +219,9 @@ q4g128_status q4g128_dequant(const uint32_t *W, const void *scale, const void *m
  * dequantisation error sum_k (q*s + m - w)^2.
  *
  * Per group the codes come from a search over clipped ranges scored by
- * squared error (Token Rush README, quantization section: a per-group range
- * search that clips a few outliers so the rest get a finer grid).  With
+ * squared error (Token Rush README, quantization section: narrowing a
+ * group's range past its extremes buys a finer step for the other weights).
+ * With
  * lo, hi the group's extremes and c their midpoint, candidate (i, j),
  * 0 <= i, j < ncand, taken in the order i*ncand + j, uses the range
  * [lo + (i/20)(c - lo), hi - (j/20)(hi - c)], scale s = (range width)/15 and

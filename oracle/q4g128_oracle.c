@@ -268,8 +268,9 @@ int q4o_gemm(const uint16_t *x, long M, long K, const uint32_t *W,
  * Producing the format from bf16 weights (Token Rush README, quantization
  * section): codes, scale and minimum are chosen per group of 128 weights;
  * plain round-to-nearest is the baseline there, and a per-group search over
- * the range, scored by squared error, clips a few outliers so that the other
- * weights get a finer grid.  The pages give no formula; the reading taken
+ * narrowed ranges, scored by squared error, gives up accuracy on the extreme
+ * values for a finer step on the rest.  The pages give no formula; the reading
+ * taken
  * (one candidate = round-to-nearest):
  *
  *   v_k        the 128 weights of the group, decoded exactly to fp64

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "q4g128_launch.h"
 
 namespace {
@@ -37,8 +39,13 @@ bool operands_ok(const void *x, const uint32_t *W, const void *scale, const void
            aligned(min, 2) && aligned(y, 4);
 }
 
-// K splits align to blocks of kRing = 8 groups (1024 k).
-int max_splits(int K) { return (K / Q4G128_GROUP + q4g128::kRing - 1) / q4g128::kRing; }
+// Up to one split per 128-group; splits of whole 8-group blocks (1024 k)
+// while there are no more splits than blocks.
+int max_splits(int K) { return K / Q4G128_GROUP; }
+
+// Blocks of 8 groups (1024 k) along K: the default split count never
+// exceeds it, so default splits are always whole blocks.
+int k_blocks(int K) { return (K / Q4G128_GROUP + q4g128::kRing - 1) / q4g128::kRing; }
 
 // Output tiles of 16 columns per wave.  One tile per wave for every shape.
 int plan_tiles_per_wave(int /*K*/, int /*N*/) { return 1; }
@@ -48,17 +55,26 @@ int plan_tiles_per_wave(int /*K*/, int /*N*/) { return 1; }
 constexpr long kTargetWaves = 2048;
 
 // Compute units of the calling thread's current device, or -1.  Cached per
-// device (every thread that fills an entry writes the same value).
+// device in atomics (every thread that fills an entry stores the same value,
+// so relaxed ordering suffices).
 int device_cus()
 {
-    static int cache[64];
+    static std::atomic<int> cache[q4g128::kMaxDevices];
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return -1;
-    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+    const bool cached = dev >= 0 && dev < q4g128::kMaxDevices;
+    if (cached) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-    if (dev >= 0 && dev < 64) cache[dev] = ncu;
+    if (cached && ncu > 0) cache[dev].store(ncu, std::memory_order_relaxed);
     return ncu;
 }
+
+// Clears an error an earlier, unrelated HIP call may have left pending on
+// this thread, so that the launches of this call report their own.
+void clear_pending_error() { (void)hipGetLastError(); }
 
 // Balanced plan for gemv_q4g128_bal (one K split): workgroups (at most one
 // per CU) and K parts per tile, or gx = 0 when the shape needs the per-tile
@@ -193,6 +209,7 @@ q4g128::GemvArgs gemv_args(const void *x, int M, int K, const uint32_t *W, const
 q4g128_status run_gemv(const void *x, int M, int K, const uint32_t *W, const void *scale,
                        const void *min, int N, float *out, int S, hipStream_t stream)
 {
+    clear_pending_error();
     q4g128::GemvArgs a = gemv_args(x, M, K, W, scale, min, N, out, S);
     const BalChoice bc = S == 1 ? plan_bal(M, K, N, scale, min) : BalChoice{0, 1, 0};
     hipError_t e = hipSuccess;
@@ -222,6 +239,7 @@ q4g128_status run_gemv(const void *x, int M, int K, const uint32_t *W, const voi
 q4g128_status run_split(const void *x, int M, int K, const uint32_t *W, const void *scale, const void *min,
                         int N, int S, float *ws, float *dst, int *slices, hipStream_t stream)
 {
+    clear_pending_error();
     if (S == 1) {
         *slices = 1;
         return run_gemv(x, M, K, W, scale, min, N, dst, 1, stream);
@@ -258,6 +276,7 @@ int swiglu_parts(int K, int N)
 q4g128_status run_swiglu(const void *x, int M, int K, const uint32_t *W, const void *scale, const void *min,
                          int N, uint16_t *act, float *ws, hipStream_t stream)
 {
+    clear_pending_error();
     const BalChoice bc = plan_bal(M, K, N, scale, min, true);
     if (bc.gx > 0 && (bc.P == 1 || M <= bc.rb)) {
         q4g128::GemvArgs a = gemv_args(x, M, K, W, scale, min, N, nullptr, 1);
@@ -332,7 +351,7 @@ int q4g128_splitk_default_splits(int K, int N)
         const BalGrid g = plain_grid(K, N, ncu);
         if (bal_fits(g.P > 1 ? kBalRowBlock : 1, K, N, g.gx, g.P, false)) return 1;
     }
-    const long nb = max_splits(K);
+    const long nb = k_blocks(K);
     const long tpw = plan_tiles_per_wave(K, N);
     const long waves = ((long)N + 16 * tpw - 1) / (16 * tpw);
     if (waves >= kTargetWaves) return 1;
@@ -416,6 +435,7 @@ q4g128_status q4g128_gemm_streamk(const void *x, int M, int K, const uint32_t *W
     a.S = 1;
     float *parts = static_cast<float *>(workspace);
     uint32_t *cnt = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + kSkPartBytes);
+    clear_pending_error();
     hipError_t e = q4g128::launch_gemv_streamk(a, plan, parts, cnt, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
         set_error("stream-K launch", e);
@@ -430,6 +450,7 @@ q4g128_status q4g128_dequant(const uint32_t *W, const void *scale, const void *m
     if (!shape_ok(1, K, N) || !W || !scale || !min || !w_out) return Q4G128_EINVAL;
     if (!aligned(W, 16) || !aligned(scale, 2) || !aligned(min, 2) || !aligned(w_out, 16))
         return Q4G128_EINVAL;
+    clear_pending_error();
     hipError_t e = q4g128::launch_dequant(W, static_cast<const uint16_t *>(scale),
                                           static_cast<const uint16_t *>(min), K, N, w_out,
                                           static_cast<hipStream_t>(stream));
@@ -450,6 +471,7 @@ q4g128_status q4g128_quantize(const void *w, int K, int N, int ncand, uint32_t *
     const long ngroups = (long)N * (K / Q4G128_GROUP);
     const int gpw = q4g128::quantize_groups_per_block(ncand);
     if ((ngroups + gpw - 1) / gpw > 0x7FFFFFFFL) return Q4G128_EINVAL;
+    clear_pending_error();
     hipError_t e = q4g128::launch_quantize(static_cast<const uint16_t *>(w), ngroups, ncand, W,
                                            static_cast<uint16_t *>(scale), static_cast<uint16_t *>(min), err,
                                            static_cast<hipStream_t>(stream));

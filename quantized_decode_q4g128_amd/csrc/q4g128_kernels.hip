@@ -321,11 +321,19 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_q4g128(
     T.K8 = (size_t)(K >> 3);
     const int G = T.G;
 
-    // K split: split s covers 8-group blocks [s*nb/S, (s+1)*nb/S).
+    // K split: with S <= nb, split s covers 8-group blocks [s*nb/S, (s+1)*nb/S);
+    // with more splits than blocks (S <= G), groups [s*G/S, (s+1)*G/S), each
+    // at least one group (the launcher then takes the 2-byte scale/minimum
+    // loads, which handle ranges ending inside a block).
     const int nb = (G + kRing - 1) / kRing;
     const int split = blockIdx.y;
-    T.gs = (split * nb / S) * kRing;
-    T.ge = min(((split + 1) * nb / S) * kRing, G);
+    if (S <= nb) {
+        T.gs = (split * nb / S) * kRing;
+        T.ge = min(((split + 1) * nb / S) * kRing, G);
+    } else {
+        T.gs = (int)((long)split * G / S);
+        T.ge = (int)((long)(split + 1) * G / S);
+    }
 
     // Columns: waves past N alias the last column and store nothing.
     const int col0 = (blockIdx.x * WAVES + wave) * TPW * 16;
@@ -891,29 +899,30 @@ int chunk_groups(int M)
 }
 
 template <int TPW, bool CHUNKED, bool VSM, int WAVES>
-static void launch_one(const GemvArgs &a, dim3 grid, int cg, hipStream_t stream)
+static hipError_t launch_one(const GemvArgs &a, dim3 grid, int cg, hipStream_t stream)
 {
     // x for up to 16 rows of a chunk can pass 64 KiB (66.5 KiB at M = 16):
     // allow the kernel the CU's whole LDS.
     static LdsFlags done;
     const hipError_t attr = allow_dynamic_lds(
         reinterpret_cast<const void *>(&gemv_q4g128<TPW, CHUNKED, VSM, kRingDepth, WAVES>), (int)kBalMaxLds, done);
-    (void)attr;                                  // a failure shows up as the launch's error
+    if (attr != hipSuccess) return attr;
     const size_t lds = (size_t)a.M * (size_t)cg * 128 * 2 + (size_t)cg * kXsRows * 4;
     hipLaunchKernelGGL((gemv_q4g128<TPW, CHUNKED, VSM, kRingDepth, WAVES>), grid, dim3(64 * WAVES, 1, 1), lds,
                        stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.S, cg);
+    return hipGetLastError();
 }
 
 template <int WAVES>
-static void launch_waves(const GemvArgs &a, dim3 grid, bool chunked, bool vsm, int cg, int span, hipStream_t stream)
+static hipError_t launch_waves(const GemvArgs &a, dim3 grid, bool chunked, bool vsm, int cg, int span,
+                               hipStream_t stream)
 {
     if (vsm) {
-        if (chunked) launch_one<1, true, true, WAVES>(a, grid, cg, stream);
-        else launch_one<1, false, true, WAVES>(a, grid, span, stream);
-    } else {
-        if (chunked) launch_one<1, true, false, WAVES>(a, grid, cg, stream);
-        else launch_one<1, false, false, WAVES>(a, grid, span, stream);
+        if (chunked) return launch_one<1, true, true, WAVES>(a, grid, cg, stream);
+        return launch_one<1, false, true, WAVES>(a, grid, span, stream);
     }
+    if (chunked) return launch_one<1, true, false, WAVES>(a, grid, cg, stream);
+    return launch_one<1, false, false, WAVES>(a, grid, span, stream);
 }
 
 hipError_t launch_gemv(const GemvArgs &a, int tpw, hipStream_t stream)
@@ -921,18 +930,21 @@ hipError_t launch_gemv(const GemvArgs &a, int tpw, hipStream_t stream)
     if (tpw != 1) return hipErrorInvalidValue;
     const int waves = waves_for(a.M);
     const int cpb = columns_per_block(tpw, a.M);
-    // The widest split spans ceil(nb/S) blocks of 8 groups.
-    const int nb = (a.K / 128 + kRing - 1) / kRing;
-    const int span = (nb + a.S - 1) / a.S * kRing;
+    // The widest split spans ceil(nb/S) blocks of 8 groups, or ceil(G/S)
+    // groups when there are more splits than blocks.
+    const int G = a.K / 128;
+    const int nb = (G + kRing - 1) / kRing;
+    const bool fine = a.S > nb;
+    const int span = fine ? (G + a.S - 1) / a.S : (nb + a.S - 1) / a.S * kRing;
     const int cg = chunk_groups(a.M);
     const bool chunked = span > cg;
-    // 16-byte scale/minimum loads need K/128 a multiple of 8 and aligned bases.
-    const bool vsm = (a.K / 128) % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scale) & 15) == 0 &&
+    // 16-byte scale/minimum loads need K/128 a multiple of 8, aligned bases
+    // and ranges of whole blocks.
+    const bool vsm = !fine && G % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scale) & 15) == 0 &&
                      (reinterpret_cast<uintptr_t>(a.mn) & 15) == 0;
     dim3 grid((unsigned)((a.N + cpb - 1) / cpb), (unsigned)a.S, 1);
-    if (waves == kWavesSmall) launch_waves<kWavesSmall>(a, grid, chunked, vsm, cg, span, stream);
-    else launch_waves<kWavesLarge>(a, grid, chunked, vsm, cg, span, stream);
-    return hipGetLastError();
+    if (waves == kWavesSmall) return launch_waves<kWavesSmall>(a, grid, chunked, vsm, cg, span, stream);
+    return launch_waves<kWavesLarge>(a, grid, chunked, vsm, cg, span, stream);
 }
 
 BalPlan bal_plan(int M, int K, int N, int S, int gx, int P, bool act)

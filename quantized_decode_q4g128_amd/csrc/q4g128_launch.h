@@ -67,8 +67,9 @@ struct GemvArgs {
     const uint16_t *mn;      // bf16 [N][K/128]
     int N;
     float *out;              // S == 1: y [M][N]; S > 1: partials [S][M][N]
-    int S;                   // K splits, 1..ceil(K/1024): split s covers 8-group
-                             // blocks [s*nb/S, (s+1)*nb/S), nb = ceil(K/1024)
+    int S;                   // K splits, 1..K/128: for S <= nb = ceil(K/1024) split s
+                             // covers 8-group blocks [s*nb/S, (s+1)*nb/S), else
+                             // groups [s*G/S, (s+1)*G/S), G = K/128
     uint16_t *act = nullptr; // balanced kernel only: if set, N = 2I is a fused gate/up
                              // product and bf16 silu(gate) * up [M][I] is written
                              // here instead of y (out unused)

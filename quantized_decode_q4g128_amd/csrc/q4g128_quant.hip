@@ -4,9 +4,9 @@
 // paragraph): per group of 128 consecutive k of one column n, a bf16 scale s
 // and bf16 minimum m, codes q in 0..15, w ~ q*s + m.  Codes are chosen by a
 // per-group search over clipped ranges scored by squared error (Token Rush
-// README, quantization section: a range search per group that clips a few
-// outliers so that the rest of the group gets a finer grid; round-to-nearest
-// over the full range is its first candidate).
+// README, quantization section: narrowing a group's range past its extreme
+// values trades their error for a finer step on all the others;
+// round-to-nearest over the full range is the first candidate).
 //
 // Candidates (i, j), i, j = 0 .. ncand-1, taken in the order i*ncand + j:
 //   lo, hi = min, max of the group;  c = (lo + hi) / 2

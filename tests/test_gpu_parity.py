@@ -143,6 +143,43 @@ def test_split_k_deterministic_across_runs_and_streams():
     assert np.array_equal(bits(y1), bits(yg))
 
 
+# More splits than 1024-k blocks: up to one split per 128-group, cut at group
+# boundaries (K = 17408: 17 blocks, 136 groups).  Each split count stays
+# within the tolerance, repeats its bits on another run and on another
+# stream, and keeps rows bit-identical to one-row calls.
+@pytest.mark.parametrize("splits", [17, 34, 136])
+def test_split_k_up_to_one_split_per_group(orc, splits):
+    case = synth.make_random(3, 17408, 5120, 2, outlier_frac=0.01)
+    wt = case.weights
+    y_ref, a_ref = orc.gemm(case.x, wt.W, wt.scale, wt.mn)
+    W, s, m = dev_weights(wt)
+    x = dev_x(case.x)
+    ya = host_f32(q.q4g128_gemm_splitk(x, W, s, m, splits=splits))
+    r = assert_within_tolerance(ya, y_ref, a_ref, f"splits={splits}")
+    yb = host_f32(q.q4g128_gemm_splitk(x, W, s, m, splits=splits))
+    side = torch.cuda.Stream(DEV)
+    with torch.cuda.stream(side):
+        yc_t = q.q4g128_gemm_splitk(x, W, s, m, splits=splits, stream=side)
+    side.synchronize()
+    yc = host_f32(yc_t)
+    assert np.array_equal(bits(ya), bits(yb)) and np.array_equal(bits(ya), bits(yc))
+    for row in range(3):
+        y1 = host_f32(q.q4g128_gemm_splitk(x[row:row + 1].contiguous(), W, s, m, splits=splits))
+        assert np.array_equal(bits(y1[0]), bits(ya[row])), row
+    print(f"splits={splits}: worst |err|/tol {r:.2e}")
+
+
+# Group-granular splits of short K, ragged split widths (K = 640: 5 groups
+# in one block) and K not a multiple of 1024.
+@pytest.mark.parametrize("M,K,N,splits", [(2, 640, 100, 5), (2, 640, 100, 3), (1, 1152, 33, 9), (4, 3200, 70, 7)])
+def test_split_k_group_granular_edges(orc, M, K, N, splits):
+    case = synth.make_random(M, K, N, 140 + K // 128 + splits, outlier_frac=0.01)
+    wt = case.weights
+    y_ref, a_ref = orc.gemm(case.x, wt.W, wt.scale, wt.mn)
+    y = host_f32(q.q4g128_gemm_splitk(dev_x(case.x), *dev_weights(wt), splits=splits))
+    assert_within_tolerance(y, y_ref, a_ref, f"M={M} K={K} N={N} splits={splits}")
+
+
 @pytest.mark.parametrize("splits", [None, 1])
 def test_power_of_two_scaling_is_exact(splits):
     case = synth.make_random(3, 5120, 777, 9)
@@ -193,7 +230,7 @@ def test_invalid_arguments_are_rejected_before_launch():
     W, s, m = dev_weights(case.weights)
     x = dev_x(case.x)
     with pytest.raises(q.Q4G128Error) as e:
-        q.q4g128_gemm_splitk(x, W, s, m, splits=2)      # K=256 is one block of 1024 k
+        q.q4g128_gemm_splitk(x, W, s, m, splits=3)      # K=256 holds two 128-groups
     assert e.value.status == q.Q4G128_EINVAL
     with pytest.raises(q.Q4G128Error) as e:
         q.q4g128_gemm(dev_x(np.zeros((17, 256), np.uint16)), W, s, m)
