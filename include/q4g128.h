@@ -119,6 +119,24 @@ q4g128_status q4g128_gemm_splitk(const void *x, int M, int K,
                                  float *workspace, size_t workspace_bytes,
                                  void *stream);
 
+/* q4g128_gemm_splitk without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The partial sums go to a
+ * scratch array the library holds in device memory: 8 MiB (8388608 bytes)
+ * per GPU, allocated when the library's code is loaded on that GPU and held
+ * until the process ends.  Same arguments, results and bits as
+ * q4g128_gemm_splitk; calls nothing that allocates.  Returns
+ * Q4G128_EWORKSPACE (with a q4g128_last_error() text) before anything is
+ * enqueued if splits * M * N * 4 exceeds 8 MiB.  Every call on one GPU
+ * shares that GPU's scratch: calls that overlap in time on one GPU (other
+ * streams, other threads) race on it and must be serialised by the caller;
+ * calls in order on one stream are safe.  The scratch keeps the last call's
+ * partial sums; nothing in it needs clearing (each call overwrites every
+ * partial it reads). */
+q4g128_status q4g128_gemm_splitk_noalloc(const void *x, int M, int K,
+                                         const uint32_t *W, const void *scale, const void *min,
+                                         int N, float *y, int splits, void *stream);
+
 /* Bytes of workspace q4g128_gemm_streamk needs for a (K, N) shape: 2 MiB of
  * partial-sum slots plus 4 * ceil(N/16) bytes of counters, rounded up to
  * 256.  Independent of M.  Returns 0 if the shape is not supported (K not a

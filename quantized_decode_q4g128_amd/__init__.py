@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
         L.q4g128_gemm.restype = ci
         L.q4g128_gemm_splitk.argtypes = [vp, ci, ci, vp, vp, vp, ci, vp, ci, vp, sz, vp]
         L.q4g128_gemm_splitk.restype = ci
+        L.q4g128_gemm_splitk_noalloc.argtypes = [vp, ci, ci, vp, vp, vp, ci, vp, ci, vp]
+        L.q4g128_gemm_splitk_noalloc.restype = ci
         L.q4g128_gemm_streamk.argtypes = [vp, ci, ci, vp, vp, vp, ci, vp, vp, sz, vp]
         L.q4g128_gemm_streamk.restype = ci
         L.q4g128_streamk_workspace_bytes.argtypes = [ci, ci]
@@ -190,6 +192,22 @@ def q4g128_gemm_splitk(x, W, scale, min, splits=None, workspace=None, y=None, st
                                   y.data_ptr(), int(splits), workspace.data_ptr(), ws_bytes,
                                   _stream(stream, x.device))
     _check(st, "q4g128_gemm_splitk")
+    return y
+
+
+def q4g128_gemm_splitk_noalloc(x, W, scale, min, y, splits=None, stream=None) -> torch.Tensor:
+    """q4g128_gemm_splitk with the partial sums in the library's own device
+    scratch (8 MiB per GPU): the call allocates nothing, so y must be given.
+    Calls overlapping on one GPU race on that scratch."""
+    x, W, scale, min, M, K, N = _operands(x, W, scale, min)
+    if y is None:
+        raise ValueError("y must be given: q4g128_gemm_splitk_noalloc allocates nothing")
+    y = _out(y, M, N, x.device)
+    if splits is None:
+        splits = q4g128_splitk_default_splits(K, N)
+    st = lib().q4g128_gemm_splitk_noalloc(x.data_ptr(), M, K, W.data_ptr(), scale.data_ptr(), min.data_ptr(), N,
+                                          y.data_ptr(), int(splits), _stream(stream, x.device))
+    _check(st, "q4g128_gemm_splitk_noalloc")
     return y
 
 
@@ -337,7 +355,7 @@ def q4g128_quantize(w, ncand: int = 9, W=None, scale=None, min=None, err=None, s
 
 
 __all__ = ["q4g128_gemm", "q4g128_quantize", "q4g128_gemm_swiglu", "q4g128_swiglu_workspace_bytes",
-           "q4g128_gemm_rmsnorm", "q4g128_gemm_splitk", "q4g128_gemm_streamk", "q4g128_streamk_workspace",
+           "q4g128_gemm_rmsnorm", "q4g128_gemm_splitk", "q4g128_gemm_splitk_noalloc", "q4g128_gemm_streamk", "q4g128_streamk_workspace",
            "q4g128_streamk_workspace_bytes", "q4g128_dequant", "q4g128_splitk_workspace_bytes",
            "q4g128_splitk_default_splits", "q4g128_gemm_parts", "q4g128_status_string", "q4g128_last_error",
            "q4g128_abi_version", "Q4G128Error", "lib", "LIB_PATH"]

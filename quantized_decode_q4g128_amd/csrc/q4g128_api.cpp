@@ -311,6 +311,23 @@ size_t streamk_ws_bytes(int N)
     return (kSkPartBytes + tiles * 4 + 255) / 256 * 256;
 }
 
+// Split-K partial sums into `workspace` (validated, large enough), then their
+// sum in ascending split order into y; one launch when the balanced kernel's
+// K parts are these splits.
+q4g128_status run_splitk(const void *x, int M, int K, const uint32_t *W, const void *scale, const void *min, int N,
+                         float *y, int splits, float *workspace, hipStream_t st)
+{
+    int slices = 0;
+    q4g128_status rc = run_split(x, M, K, W, scale, min, N, splits, workspace, y, &slices, st);
+    if (rc != Q4G128_OK || slices == 1) return rc;               // one launch wrote y
+    hipError_t e = q4g128::launch_splitk_sum(workspace, splits, (size_t)M * (size_t)N, y, st);
+    if (e != hipSuccess) {
+        set_error("split-K sum launch", e);
+        return Q4G128_EHIP;
+    }
+    return Q4G128_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -390,15 +407,29 @@ q4g128_status q4g128_gemm_splitk(const void *x, int M, int K, const uint32_t *W,
     if (splits == 1) return run_gemv(x, M, K, W, scale, min, N, y, 1, st);
     if (!workspace || !aligned(workspace, 4)) return Q4G128_EINVAL;
     if (workspace_bytes < q4g128_splitk_workspace_bytes(M, N, splits)) return Q4G128_EWORKSPACE;
-    int slices = 0;
-    q4g128_status rc = run_split(x, M, K, W, scale, min, N, splits, workspace, y, &slices, st);
-    if (rc != Q4G128_OK || slices == 1) return rc;               // one launch wrote y
-    hipError_t e = q4g128::launch_splitk_sum(workspace, splits, (size_t)M * (size_t)N, y, st);
+    return run_splitk(x, M, K, W, scale, min, N, y, splits, workspace, st);
+}
+
+q4g128_status q4g128_gemm_splitk_noalloc(const void *x, int M, int K, const uint32_t *W, const void *scale,
+                                         const void *min, int N, float *y, int splits, void *stream)
+{
+    if (!shape_ok(M, K, N) || !operands_ok(x, W, scale, min, y)) return Q4G128_EINVAL;
+    if (splits < 1 || splits > max_splits(K) || splits > kMaxSplits) return Q4G128_EINVAL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (splits == 1) return run_gemv(x, M, K, W, scale, min, N, y, 1, st);
+    if (q4g128_splitk_workspace_bytes(M, N, splits) > q4g128::kScratchBytes) {
+        snprintf(g_last_error, sizeof g_last_error,
+                 "q4g128_gemm_splitk_noalloc: splits*M*N*4 = %zu bytes exceeds the library scratch of %zu bytes",
+                 q4g128_splitk_workspace_bytes(M, N, splits), q4g128::kScratchBytes);
+        return Q4G128_EWORKSPACE;
+    }
+    float *ws = nullptr;
+    const hipError_t e = q4g128::scratch_pointer(&ws);
     if (e != hipSuccess) {
-        set_error("split-K sum launch", e);
+        set_error("scratch address lookup", e);
         return Q4G128_EHIP;
     }
-    return Q4G128_OK;
+    return run_splitk(x, M, K, W, scale, min, N, y, splits, ws, st);
 }
 
 size_t q4g128_streamk_workspace_bytes(int K, int N)

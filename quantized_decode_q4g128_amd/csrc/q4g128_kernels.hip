@@ -885,6 +885,31 @@ __global__ __launch_bounds__(256) void dequant_q4g128(const uint32_t *__restrict
     dst[1] = hi;
 }
 
+// ---- library-owned scratch ---------------------------------------------------
+
+// Split-K partial sums of q4g128_gemm_splitk_noalloc.  Every call on a GPU
+// shares that GPU's copy; calls that overlap on one GPU race on it.
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+hipError_t scratch_pointer(float **p)
+{
+    static std::atomic<float *> ptr[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    float *v = ptr[dev].load(std::memory_order_relaxed);
+    if (!v) {
+        void *addr = nullptr;
+        e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));   // this device's copy, with it current
+        if (e != hipSuccess) return e;
+        v = static_cast<float *>(addr);
+        ptr[dev].store(v, std::memory_order_relaxed);         // every thread stores the same address
+    }
+    *p = v;
+    return hipSuccess;
+}
+
 // ---- launchers ---------------------------------------------------------------
 
 int waves_for(int M) { return M <= kSmallM ? kWavesSmall : kWavesLarge; }

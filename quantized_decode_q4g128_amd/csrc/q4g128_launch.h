@@ -173,6 +173,14 @@ int waves_for(int M);
 int columns_per_block(int tpw, int M);
 
 hipError_t launch_gemv(const GemvArgs &a, int tpw, hipStream_t stream);
+
+// Library-owned scratch for callers that cannot allocate: a file-scope
+// device array of kScratchBytes on every GPU the library runs on (each GPU
+// holds its own copy until the process ends).  scratch_pointer() returns
+// this device's copy's address, looked up once per device; host code uses
+// that address, never the array's name (a host-side stand-in).
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+hipError_t scratch_pointer(float **p);
 hipError_t launch_splitk_sum(const float *P, int S, size_t MN, float *y, hipStream_t stream);
 hipError_t launch_dequant(const uint32_t *W, const uint16_t *scale, const uint16_t *mn, int K, int N,
                           float *w, hipStream_t stream);

@@ -181,3 +181,14 @@ def test_epilogue_rejects(L):
     assert g(*base, FAKE, FAKE, 1e-6, FAKE, FAKE, 0, FAKE, wsb, None) == q.Q4G128_EINVAL    # splits 0
     assert g(*base, FAKE, FAKE, 1e-6, FAKE, FAKE, 9, FAKE, 10 ** 6, None) == q.Q4G128_EINVAL   # > K/128
     assert g(*base, FAKE, FAKE, 1e-6, FAKE, FAKE, 1, FAKE, wsb - 4, None) == q.Q4G128_EWORKSPACE
+
+
+def test_splitk_noalloc_rejects_before_launch(L):
+    f = L.q4g128_gemm_splitk_noalloc
+    args = [FAKE, 1, 256, FAKE, FAKE, FAKE, 16, FAKE]
+    assert f(*args, 0, None) == q.Q4G128_EINVAL                           # splits < 1
+    assert f(*args, 3, None) == q.Q4G128_EINVAL                           # splits > K/128
+    assert f(None, 1, 256, FAKE, FAKE, FAKE, 16, FAKE, 2, None) == q.Q4G128_EINVAL
+    # 136 splits x 16 rows x 5120 columns x 4 bytes = 44.6 MB > the 8 MiB scratch
+    assert f(FAKE, 16, 17408, FAKE, FAKE, FAKE, 5120, FAKE, 136, None) == q.Q4G128_EWORKSPACE
+    assert b"exceeds the library scratch" in L.q4g128_last_error()
