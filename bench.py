@@ -60,8 +60,10 @@ PEAK_FP64_TFLOPS = 78.6         # MI355X fp64 vector peak
 ROTATE_BYTES = 1.2e9            # > 4x the 256 MB last-level cache
 WARM_S = 0.2                    # untimed launches before every timed leg, seconds
 METRIC = "achieved HBM GB/s (% of MI355X peak) for int4-g128 GEMV at M=1 and M=7"
-KERNEL = "gemv_q4g128"          # the dominant (only) kernel of a decode step
+KERNEL = "gemv_q4g128_lds"      # the kernel of the decode gate/up launch (all of its time)
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_q4g128_gateup_pmc.txt")
+TRACE_SUMMARY = os.path.join(ROOT, "profiles", "gemv_q4g128_gateup_kernel_trace.txt")
+DIST_CALLS = 1300               # per-launch distribution: at least this many launches (100 passes over 13 copies)
 COPY_BYTES = 256 << 20          # calibration copy for the traffic counters
 PMC_LAUNCHES = 24
 
@@ -187,6 +189,79 @@ def timed_calls(torch, seq, reps, warmup, warm_s=WARM_S):
     return t0.elapsed_time(t1)
 
 
+def timed_launches(torch, seq, n, warmup, warm_s=WARM_S):
+    """Milliseconds for exactly `n` launches, launch i on copy i % len(seq)
+    (cycling through the weight copies, no rounding to whole passes),
+    bracketed by HIP events on the launching stream, after `warm_s` seconds
+    and `warmup` untimed launches."""
+    stream = torch.cuda.current_stream()
+    st = stream.cuda_stream
+    if warm_s > 0:
+        warm_up(torch, seq, warm_s)
+    for i in range(warmup):
+        if seq[i % len(seq)](st) != 0:
+            raise RuntimeError("launch failed")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(n):
+        seq[i % len(seq)](st)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1)
+
+
+def per_call_distribution(torch, seq, n):
+    """Per-launch time distribution over at least `n` launches: batches of
+    one pass over the weight copies (len(seq) launches, back to back), an
+    event between batches, so a batch's time divided by its launches is one
+    sample (events between single launches cost ~3 us each here, more than
+    the spread they would show).  Returns microseconds per launch: median,
+    min, p90 and mean over the batches."""
+    stream = torch.cuda.current_stream()
+    st = stream.cuda_stream
+    warm_up(torch, seq, WARM_S)
+    nb = max(1, -(-n // len(seq)))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for b in range(nb):
+        for c in seq:
+            c(st)
+        ev[b + 1].record(stream)
+    torch.cuda.synchronize()
+    dt = np.array([ev[b].elapsed_time(ev[b + 1]) * 1e3 / len(seq) for b in range(nb)])
+    return {"launches": nb * len(seq), "batches": nb, "launches_per_batch": len(seq),
+            "median_us": round(float(np.median(dt)), 3), "min_us": round(float(dt.min()), 3),
+            "p90_us": round(float(np.percentile(dt, 90)), 3), "mean_us": round(float(dt.mean()), 3)}
+
+
+def trace_reading(kernel_prefix):
+    """Median and mean duration of the dominant launch shape of a kernel in
+    the committed rocprofv3 trace summary, when that summary was taken on the
+    current kernel sources (else None)."""
+    if not os.path.exists(TRACE_SUMMARY):
+        return None
+    src, best = None, None
+    with open(TRACE_SUMMARY) as f:
+        for line in f:
+            if line.startswith("# kernel_source_hash:"):
+                src = line.split(":", 1)[1].strip()
+            if line.startswith("#") or "|" not in line:
+                continue
+            cols = [c.strip() for c in line.split("|")]
+            if not cols[0].split("::")[-1].startswith(kernel_prefix):
+                continue
+            n = int(cols[3])
+            if best is None or n > best[0]:
+                best = (n, float(cols[4]), float(cols[5]), cols[0])
+    if best is None or src != kernel_source_hash():
+        return None
+    return {"kernel": best[3], "launches": best[0], "mean_us": best[1], "median_us": best[2],
+            "file": os.path.relpath(TRACE_SUMMARY, ROOT)}
+
+
 def measure_wide_verify(torch, q, raw, t_dec, steps, warmup):
     """Verify steps wider than the 7-row one on the gate/up shape: M = 9 (a
     draft of 8 tokens plus the next) and M = 16 (the MFMA tile's rows), each
@@ -196,8 +271,8 @@ def measure_wide_verify(torch, q, raw, t_dec, steps, warmup):
         case = synth.make_random(M, 5120, 34816, 80 + M)
         B = synth.algorithmic_bytes(M, case.K, case.N)
         calls, _ = raw.prepare(case, max(2, math.ceil(ROTATE_BYTES / B)), splits=1)
-        n = max(1, steps // len(calls)) * len(calls)
-        t = timed_calls(torch, calls, n // len(calls), max(1, warmup // len(calls))) * 1e-3 / n
+        n = max(steps, len(calls))
+        t = timed_launches(torch, calls, n, warmup) * 1e-3 / n
         out[f"M{M}"] = {"us_per_call": round(t * 1e6, 3), "GBps": round(B / t / 1e9, 1), "bytes_per_call": B,
                         "time_ratio_vs_M1": round(t / t_dec, 4)}
     return out
@@ -210,9 +285,8 @@ def measure_down(torch, q, steps, warmup):
     B = synth.algorithmic_bytes(case.M, case.K, case.N)
     rc = RawCalls(torch, q)
     calls, splits = rc.prepare(case, max(2, math.ceil(ROTATE_BYTES / B)))
-    ms = timed_calls(torch, calls, max(1, steps // len(calls)), 1)
-    n = max(1, steps // len(calls)) * len(calls)
-    t = ms * 1e-3 / n
+    n = max(steps, len(calls))
+    t = timed_launches(torch, calls, n, warmup) * 1e-3 / n
     return {"us_per_call": round(t * 1e6, 3), "GBps": round(B / t / 1e9, 1), "splits": splits,
             "bytes_per_call": B, "kernels_per_call": 2 if splits > 1 else 1}
 
@@ -819,6 +893,7 @@ def trace_summarize(trace_dir, out, command):
         f.write("# command (rocprofv3 started from /tmp with TMPDIR=/tmp; REPO = repository root):\n")
         f.write(f"#   {command}\n")
         f.write(f"#   python3 bench.py --trace-summarize OUT {os.path.relpath(out, ROOT)}\n")
+        f.write(f"# kernel_source_hash: {kernel_source_hash()}\n")
         f.write("# kernel | grid x,y | workgroup | launches | avg us | median us | min us | p90 us | max us\n")
         for key in sorted(rows, key=lambda k: -sum(rows[k])):
             v = np.array(rows[key])
@@ -897,16 +972,17 @@ def main():
         for c in dec_calls:
             c(st)
         torch.cuda.synchronize()
-    n_dec = max(1, args.steps // len(dec_calls)) * len(dec_calls)      # whole passes over the copies
-    wall_d = timed_calls(torch, dec_calls, n_dec // len(dec_calls), max(1, args.warmup // len(dec_calls)))
+    n_dec = args.steps                            # exactly the launches asked for, cycling the copies
+    wall_d = timed_launches(torch, dec_calls, n_dec, args.warmup)
     ms_step = wall_d / n_dec
     t_dec = wall_d * 1e-3 / n_dec                 # s per launch (back to back)
     gbps = B_dec * n_dec / (wall_d * 1e-3) / 1e9
     achieved = B_dec / t_dec / 1e9
+    dist = per_call_distribution(torch, dec_calls, max(DIST_CALLS, args.steps))
     verify = None
     if ver_calls:
-        n_ver = max(1, args.steps // len(ver_calls)) * len(ver_calls)
-        wall_v = timed_calls(torch, ver_calls, n_ver // len(ver_calls), max(1, args.warmup // len(ver_calls)))
+        n_ver = max(args.steps, len(ver_calls))
+        wall_v = timed_launches(torch, ver_calls, n_ver, args.warmup)
         t_ver = wall_v * 1e-3 / n_ver
         verify = {"GBps": round(B_ver / t_ver / 1e9, 1), "us_per_call": round(t_ver * 1e6, 3),
                   "bytes_per_call": B_ver, "time_ratio_vs_M1": round(t_ver / t_dec, 4)}
@@ -966,6 +1042,7 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": round(traffic) if traffic is not None else None,
                      "kernel": KERNEL, "us_per_launch": round(t_dec * 1e6, 3),
+                     "per_call": dist, "trace": trace_reading(KERNEL),
                      "algorithmic_bytes_per_launch": B_dec,
                      "frac_of_read_ceiling": (round(achieved / ceiling["tile_pattern"]["GBps"], 4)
                                               if ceiling else None)},

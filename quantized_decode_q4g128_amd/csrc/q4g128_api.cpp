@@ -187,6 +187,36 @@ BalChoice plan_bal(int M, int K, int N, const void *scale, const void *min, bool
     return c;
 }
 
+// Which balanced kernel runs a planned launch.  Both give the same bits.
+// Workgroups of many whole tiles (8 or more, K not cut: gate/up, the output
+// projection, their SwiGLU and verify forms) take the LDS-fed kernel, with a
+// ring of 2 group pairs per wave and the weights requested before x:
+// gate/up 19.7-20.6 -> 18.3-18.6 us, verify M = 7 21.5 -> 20.6 us, SwiGLU
+// 20.6 -> 18.7 us (one box, interleaved).  Deeper rings (4 pairs) were
+// slower on every shape.  Short shapes (few tiles per CU, or K parts) stay on
+// the register-ring kernel, which was as fast or faster there (5120 -> 12288:
+// 10.3 vs 10.6-13.1 us; 6144 -> 5120: 7.6 vs 7.8 us).  A shape whose LDS does
+// not fit the LDS-fed kernel takes the other one.
+#ifndef Q4G128_LDS_MODE
+#define Q4G128_LDS_MODE -1
+#endif
+hipError_t launch_balanced(const q4g128::GemvArgs &a, int gx, int P, hipStream_t stream)
+{
+    using namespace q4g128;
+    int mode = Q4G128_LDS_MODE;                 // 0: register ring; 1-4: LDS-fed (rd 2/2/4/4, burst on 2 and 4)
+    if (mode < 0) {
+        const int tiles = a.act ? (((a.N / 2 + 3) / 4 + gx - 1) / gx * 4 + 7) / 8 : bal_tiles(a.N, gx);
+        mode = (P == 1 && tiles >= kBalMinTiles) ? 2 : 0;
+    }
+    if (mode > 0) {
+        const int rd = mode >= 3 ? 4 : 2;
+        const bool burst = mode == 2 || mode == 4;
+        if (lds_plan(a.M, a.K, a.N, gx, P, a.act != nullptr, rd).total <= kBalMaxLds)
+            return launch_gemv_lds(a, gx, P, rd, burst, stream);
+    }
+    return launch_gemv_bal(a, gx, P, stream);
+}
+
 q4g128::GemvArgs gemv_args(const void *x, int M, int K, const uint32_t *W, const void *scale, const void *min, int N,
                            float *out, int S)
 {
@@ -219,7 +249,7 @@ q4g128_status run_gemv(const void *x, int M, int K, const uint32_t *W, const voi
             a.x = static_cast<const uint16_t *>(x) + (size_t)r0 * K;
             a.M = M - r0 < rows ? M - r0 : rows;
             a.out = out + (size_t)r0 * N;
-            e = q4g128::launch_gemv_bal(a, bc.gx, bc.P, stream);
+            e = launch_balanced(a, bc.gx, bc.P, stream);
         }
     } else {
         e = q4g128::launch_gemv(a, plan_tiles_per_wave(K, N), stream);
@@ -248,7 +278,7 @@ q4g128_status run_split(const void *x, int M, int K, const uint32_t *W, const vo
     if (bc.gx > 0 && bc.P == S && M <= bc.rb) {
         *slices = 1;
         q4g128::GemvArgs a = gemv_args(x, M, K, W, scale, min, N, dst, 1);
-        hipError_t e = q4g128::launch_gemv_bal(a, bc.gx, bc.P, stream);
+        hipError_t e = launch_balanced(a, bc.gx, bc.P, stream);
         if (e != hipSuccess) {
             set_error("gemv launch", e);
             return Q4G128_EHIP;
@@ -281,7 +311,7 @@ q4g128_status run_swiglu(const void *x, int M, int K, const uint32_t *W, const v
     if (bc.gx > 0 && (bc.P == 1 || M <= bc.rb)) {
         q4g128::GemvArgs a = gemv_args(x, M, K, W, scale, min, N, nullptr, 1);
         a.act = act;
-        hipError_t e = q4g128::launch_gemv_bal(a, bc.gx, bc.P, stream);
+        hipError_t e = launch_balanced(a, bc.gx, bc.P, stream);
         if (e != hipSuccess) {
             set_error("gemv+swiglu launch", e);
             return Q4G128_EHIP;

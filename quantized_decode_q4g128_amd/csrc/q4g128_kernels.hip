@@ -696,6 +696,316 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     }
 }
 
+// ---- LDS-fed balanced kernel ----------------------------------------------------
+//
+// The balanced kernel's work split (one workgroup per CU, equal column shares,
+// (tile, K part) units, one unit per wave at a time) and its per-group
+// arithmetic, with the weights brought in by the buffer unit's direct-to-LDS
+// loads: no register holds a load in flight, and the codes land already in
+// the order the MFMA lanes read them.
+//
+// Codes: each wave owns a ring of RD slots in LDS, one group pair per slot:
+// two 1 KB loads, columns 0-7 and 8-15 of its tile, 128 contiguous bytes
+// (two groups) of each column per load.  Lane 8c + j of a load reads 16-byte
+// piece j ^ c of column c's line (every run of four lanes still covers one
+// aligned 64-byte half, and the XOR spreads the MFMA lanes' later reads of
+// one piece index over all eight 16-byte bank groups), so MFMA lane i + 16h
+// finds piece h of group e of column i at 16-byte position
+// 64 [i >= 8] + 8 (i & 7) + ((4e + h) ^ (i & 7)) of its slot: one LDS read per
+// group and lane replaces the register ring's lane permutes and selects.
+// Slots are refilled RD pairs ahead (no refill past the unit's end); before
+// a slot is read the wave waits, by an explicit count, for the loads that
+// filled it (the compiler's own tracking of direct-to-LDS loads is not relied
+// on), and before a slot or area is refilled, for its earlier LDS reads.
+//
+// Scales and minimums: the unit's pieces (8 groups of one column, 16 bytes)
+// are loaded straight into the wave's LDS area, [column][block] order; one
+// 4-byte LDS read per lane gives a pair's two scales (two minimums).
+//
+// BURST: the first unit's scales, minimums and ring are requested before x,
+// so the weights stream from the first microsecond; for short shapes whose
+// units fit their ring this is the whole unit.  Otherwise x is staged first
+// (alone, it is back in ~1.2 us; behind the weight requests of every CU it
+// would wait ~2.5 us).
+//
+// Bits: the same groups in the same order with the same instructions per
+// column as gemv_q4g128_bal and gemv_q4g128 (group_fma below is their
+// per-group arithmetic), the same K parts and part-order sum; the choice
+// between the kernels never changes a bit.
+
+constexpr int kLdsSlotU4 = 128;            // u32x4 per wave and ring slot: one group pair of a 16-column tile
+
+// Waits until the loads of a ring slot have landed, given how many later
+// pairs (two loads each) this wave has requested since (0 .. 3).  Vector
+// memory loads complete in order, so "at most 2n outstanding" covers the
+// slot and everything requested before it (the unit's scale/minimum pieces).
+__device__ __forceinline__ void wait_ring(int newer)
+{
+    if (newer >= 3) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else if (newer == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if (newer == 1) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Per-group arithmetic shared by the LDS-fed kernel: D = x . (128 + q) by
+// four MFMAs, then acc = fma(s, D, acc), acc = fma(m - 128 s, X, acc) for
+// the RL accumulated D rows.  Identical to Tile::arith for one tile.
+template <int RL>
+__device__ __forceinline__ void group_fma(const u32x4 (&a)[4], const f32x4 &xsum, const u32x4 &c, float s, float m,
+                                          float (&acc)[4], UnpackConsts uc)
+{
+    u32x4 bq[4];
+    bq[0] = unpack_biased(c.x, uc);
+    bq[1] = unpack_biased(c.y, uc);
+    bq[2] = unpack_biased(c.z, uc);
+    bq[3] = unpack_biased(c.w, uc);
+    f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) d = mfma_16x16x32(a[t], bq[t], d);
+    const float m_adj = fmaf(-kBias, s, m);           // mn - 128*s, one rounding
+#pragma unroll
+    for (int r = 0; r < RL; ++r) {
+        acc[r] = fmaf(s, d[r], acc[r]);
+        acc[r] = fmaf(m_adj, xsum[r], acc[r]);
+    }
+}
+
+template <int RD, bool PARTS, bool ACT, int RL>
+__global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
+    const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,
+    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ mn, int N,
+    float *__restrict__ out, uint16_t *__restrict__ act, int P, int nps, int nblm, int burst)
+{
+    static_assert(RD == 2 || RD == 4, "ring depth: units are whole blocks of 4 pairs");
+    __shared__ __attribute__((aligned(16))) u32x4 ring0[kBalWaves * kLdsSlotU4];
+    __shared__ __attribute__((aligned(16))) u32x4 ring1[kBalWaves * kLdsSlotU4];
+    __shared__ __attribute__((aligned(16))) u32x4 ring2[RD > 2 ? kBalWaves * kLdsSlotU4 : 1];
+    __shared__ __attribute__((aligned(16))) u32x4 ring3[RD > 2 ? kBalWaves * kLdsSlotU4 : 1];
+    extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+    u32x4 *const rings[4] = {ring0, ring1, ring2, ring3};
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int G = K >> 7;
+    const size_t K8 = (size_t)(K >> 3);
+    const int gx = gridDim.x;
+    const int c = (gx % 8 == 0) ? (int)(blockIdx.x % 8) * (gx / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    const int NC = ACT ? (N >> 1) : N;
+    const int NU = (NC + 3) >> 2;
+    const bool n32 = NU < (1 << 22) && gx <= 1024;
+    const int n0 = n32 ? (int)((unsigned)c * (unsigned)NU / (unsigned)gx) * 4 : (int)((long)c * NU / gx) * 4;
+    const int n1 = min(n32 ? (int)((unsigned)(c + 1) * (unsigned)NU / (unsigned)gx) * 4
+                           : (int)((long)(c + 1) * NU / gx) * 4,
+                       NC);
+    const int TW = ACT ? 8 : 16;
+    const int width = n1 - n0;
+    const int nchunk = (width + TW - 1) / TW;
+    auto tile = [&](int k, int &cb, int &cw) {
+        cb = n0 + (k * width) / nchunk;
+        cw = n0 + ((k + 1) * width) / nchunk - cb;
+    };
+    const int nunit = PARTS ? nchunk * P : nchunk;
+    const bool active = wave < nunit;                     // wave-uniform
+    const int nb = G >> 3;
+    auto unit = [&](int u, int &cb, int &cw, int &cs, int &ce) {
+        const int k = PARTS ? u / P : u;
+        const int p = PARTS ? u - k * P : 0;
+        tile(k, cb, cw);
+        cs = PARTS ? ((p * nb) / P) * 8 : 0;
+        ce = PARTS ? (((p + 1) * nb) / P) * 8 : G;
+    };
+
+    // LDS: x [M][G*128] bf16, row sums [G][16] fp32, nps part slots of 256
+    // fp32, then one scale/minimum area per wave: [scale, min][16 columns][nblm
+    // blocks] of 16 bytes.
+    float *slots = reinterpret_cast<float *>(xs + M * G * 128 + G * kXsRows * 2);
+    uint8_t *smarea = reinterpret_cast<uint8_t *>(slots + nps * 256) + (size_t)wave * (512 * nblm);
+
+    const int i = lane & 15, h = lane >> 4;
+    const int cq = lane >> 3, jq = lane & 7;
+    // MFMA lane (i, h): piece h of the pair's first group, piece 4 + h of its second.
+    const int boff0 = ((i & 8) ? 64 : 0) + 8 * (i & 7) + (h ^ (i & 7));
+    const int boff1 = ((i & 8) ? 64 : 0) + 8 * (i & 7) + ((4 + h) ^ (i & 7));
+
+    // Per-unit load state (wave-uniform descriptors, per-lane offsets).
+    __amdgpu_buffer_rsrc_t rw, rs, rm;
+    uint32_t voffA = 0, voffB = 0;
+    int ucs = 0, unp = 0, unblk = 1, ucw = 1, ucb = 0;
+    auto colmap = [&](int cc, int cw) -> int {
+        if (ACT) return cc < 8 ? min(cc, cw - 1) : NC + min(cc - 8, cw - 1);
+        return min(cc, cw - 1);
+    };
+    // Loads of ring slot r <- pair p of the current unit (two 1 KB loads).
+    auto fill = [&](int r, int p) {
+        u32x4 *dst = rings[r] + wave * kLdsSlotU4;
+        // The slot's earlier reads are complete before the load may write it.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const uint32_t so = (uint32_t)(64 * ucs + 128 * p);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void *)dst, 16, voffA, so, 0,
+                                                 kPairCpol);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void *)(dst + 64), 16, voffB,
+                                                 so, 0, kPairCpol);
+    };
+    // Unit u: descriptors and its scale/minimum pieces into the wave's area.
+    auto setup_unit = [&](int u) {
+        // The area's earlier reads are complete before new pieces may land.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        int cb, cw, cs, ce;
+        unit(u, cb, cw, cs, ce);
+        cb = __builtin_amdgcn_readfirstlane(cb);
+        cw = __builtin_amdgcn_readfirstlane(cw);
+        ucs = __builtin_amdgcn_readfirstlane(cs);
+        unp = __builtin_amdgcn_readfirstlane((ce - cs) >> 1);
+        unblk = __builtin_amdgcn_readfirstlane((ce - cs) >> 3);
+        ucw = cw;
+        ucb = cb;
+        const size_t span = ACT ? (size_t)NC + cw : (size_t)cw;
+        rw = make_rsrc(W + (size_t)cb * K8, (uint32_t)(span * K8 * 4));
+        rs = make_rsrc(scale + (size_t)cb * G, (uint32_t)(span * G * 2));
+        rm = make_rsrc(mn + (size_t)cb * G, (uint32_t)(span * G * 2));
+        voffA = (uint32_t)((size_t)colmap(cq, cw) * K8 * 4 + 16 * (jq ^ cq));
+        voffB = (uint32_t)((size_t)colmap(8 + cq, cw) * K8 * 4 + 16 * (jq ^ cq));
+        // pieces q = column * nblk + block, 64 per load; lanes past the last idle
+        const float rcp = 1.0f / (float)unblk;
+        for (int q0 = 0; q0 < 16 * unblk; q0 += 64) {
+            const int q = q0 + lane;
+            if (q < 16 * unblk) {
+                const int col = (int)(((float)q + 0.5f) * rcp);
+                const int b = q - col * unblk;
+                const uint32_t off = (uint32_t)(((size_t)colmap(col, cw) * G + cs + 8 * b) * 2);
+                uint8_t *ds = smarea + 16 * q0;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)ds, 16, off, 0,
+                                                         0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rm, (__attribute__((address_space(3))) void *)(ds + 256 * nblm),
+                                                         16, off, 0, 0, 0);
+            }
+        }
+    };
+    // The ring primed with the unit's first RD pairs.
+    auto prime = [&]() {
+#pragma unroll
+        for (int r = 0; r < RD; ++r) fill(r, min(r, unp - 1));
+    };
+
+    XStage<kBalThreads, kBalStage, kRowPerm> xst;
+    if (burst && active) setup_unit(wave);
+    xst.load(x, M, K, 0, G);
+    if (burst && active) prime();                 // after x: x's loads stay the oldest of the wave
+    xst.store(xs, M, 0, G);
+    lds_barrier();
+    if (!PARTS && !active) return;
+
+    const UnpackConsts uc = unpack_consts();
+    const int arow = min(kRowPerm ? rowof(i) : i, M - 1);
+    const uint16_t *rbase = xs + arow * G * 128;
+    const float *xrow = reinterpret_cast<const float *>(xs + M * G * 128) + 4 * h;
+    int aoff[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) aoff[t] = swz(4 * h + t, arow) * 8;
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(out, (uint32_t)(M * N * 4));
+
+    if (active) {
+        for (int u = wave; u < nunit; u += kBalWaves) {
+            if (!(burst && u == wave)) {
+                setup_unit(u);
+                prime();
+            }
+            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            const uint8_t *sbase = smarea + i * unblk * 16;
+            for (int p0 = 0; p0 < unp; p0 += RD) {
+#pragma unroll
+                for (int r = 0; r < RD; ++r) {
+                    const int p = p0 + r;
+                    // Requested after pair p: pairs p+1 .. min(p+RD-1, unp-1).
+                    wait_ring(min(RD - 1, unp - 1 - p));
+                    const u32x4 *slot = rings[r] + wave * kLdsSlotU4;
+                    const u32x4 c0 = slot[boff0];
+                    const u32x4 c1 = slot[boff1];
+                    const uint32_t sw = *reinterpret_cast<const uint32_t *>(sbase + 4 * p);
+                    const uint32_t mw = *reinterpret_cast<const uint32_t *>(sbase + 256 * nblm + 4 * p);
+                    if (p + RD < unp) fill(r, p + RD);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int g = ucs + 2 * p;
+                    u32x4 a[4];
+                    f32x4 xsum;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u32x4 *>(rbase + g * 128 + aoff[t]);
+                    xsum = *reinterpret_cast<const f32x4 *>(xrow + g * kXsRows);
+                    group_fma<RL>(a, xsum, c0, bf16_lo(sw), bf16_lo(mw), acc, uc);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        a[t] = *reinterpret_cast<const u32x4 *>(rbase + (g + 1) * 128 + aoff[t]);
+                    xsum = *reinterpret_cast<const f32x4 *>(xrow + (g + 1) * kXsRows);
+                    group_fma<RL>(a, xsum, c1, bf16_hi(sw), bf16_hi(mw), acc, uc);
+                }
+            }
+            if (!PARTS) {
+                if (ACT) {
+                    float up[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) up[r] = __shfl_down(acc[r], 8);
+                    if (i < ucw) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int row = kRowPerm ? rowof(4 * h + r) : 4 * h + r;
+                            if (row < M) act[(size_t)row * NC + ucb + i] = swiglu_bf16(acc[r], up[r]);
+                        }
+                    }
+                } else if (i < ucw) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = kRowPerm ? rowof(4 * h + r) : 4 * h + r;
+                        if (row < M)
+                            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc[r]), ry,
+                                                                  (uint32_t)(row * N + ucb + i) * 4, 0, 0);
+                    }
+                }
+            } else {
+                *reinterpret_cast<f32x4 *>(slots + u * 256 + lane * 4) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+            }
+        }
+        // No load into this workgroup's LDS may still be in flight when its
+        // waves end (the last refills were skipped, but make it explicit).
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+    if (PARTS) {
+        lds_barrier();
+        for (int k = wave; k < nchunk; k += kBalWaves) {
+            int cb, cw;
+            tile(k, cb, cw);
+            f32x4 vs = *reinterpret_cast<const f32x4 *>(slots + (k * P) * 256 + lane * 4);
+            for (int p = 1; p < P; ++p) vs += *reinterpret_cast<const f32x4 *>(slots + (k * P + p) * 256 + lane * 4);
+            // (elements copied out one by one: this compiler bit-casts a vector
+            // element expression as element 0)
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = vs[r];
+            if (ACT) {
+                float up[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) up[r] = __shfl_down(v[r], 8);
+                if (i < cw) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = kRowPerm ? rowof(4 * h + r) : 4 * h + r;
+                        if (row < M) act[(size_t)row * NC + cb + i] = swiglu_bf16(v[r], up[r]);
+                    }
+                }
+            } else if (i < cw) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = kRowPerm ? rowof(4 * h + r) : 4 * h + r;
+                    if (row < M)
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[r]), ry,
+                                                              (uint32_t)(row * N + cb + i) * 4, 0, 0);
+                }
+            }
+        }
+    }
+}
+
 // Partial sums of R elements e[j] (valid where ok[j]) over S splits,
 // t[j] = P[0][e] + P[1][e] + ... + P[S-1][e] in ascending s.  The loads of up
 // to BATCH splits are all issued before any is added, so a thread waits
@@ -1027,6 +1337,69 @@ static hipError_t launch_bal(const GemvArgs &a, int gx, int P, hipStream_t strea
     if (kRowPerm && a.M <= 8) return launch_bal_rl<PARTS, ACT, 2>(a, gx, P, stream);
     if (kRowPerm && a.M <= 12) return launch_bal_rl<PARTS, ACT, 3>(a, gx, P, stream);
     return launch_bal_rl<PARTS, ACT, 4>(a, gx, P, stream);
+}
+
+LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd)
+{
+    LdsPlan lp;
+    const int G = K / 128, nb = G / 8;
+    int tiles;
+    if (act) {
+        const int NU = (N / 2 + 3) / 4;
+        tiles = ((NU + gx - 1) / gx * 4 + 7) / 8;
+    } else {
+        const int N4 = (N + 3) / 4;
+        tiles = ((N4 + gx - 1) / gx * 4 + 15) / 16;
+    }
+    const int units = tiles * P;
+    const int nact = units < kBalWaves ? units : kBalWaves;
+    lp.nblm = P > 1 ? (nb + P - 1) / P : nb;
+    lp.nps = P > 1 ? units : 0;
+    const size_t stat = (size_t)(rd > 2 ? 4 : 2) * kBalWaves * kLdsSlotU4 * 16 + (rd > 2 ? 0 : 32);
+    lp.lds = (size_t)M * G * 256 + (size_t)G * kXsRows * 4 + (size_t)lp.nps * 1024 + (size_t)nact * 512 * lp.nblm;
+    if (lp.lds + stat < kBalOwnCu) lp.lds = kBalOwnCu - stat;
+    lp.total = lp.lds + stat;
+    return lp;
+}
+
+template <int RD, bool PARTS, bool ACT, int RL>
+static hipError_t launch_lds_v(const GemvArgs &a, int gx, int P, const LdsPlan &lp, bool burst, hipStream_t stream)
+{
+    static LdsFlags done;
+    const hipError_t attr = allow_dynamic_lds(reinterpret_cast<const void *>(&gemv_q4g128_lds<RD, PARTS, ACT, RL>),
+                                              (int)(kBalMaxLds - (lp.total - lp.lds)), done);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((gemv_q4g128_lds<RD, PARTS, ACT, RL>), dim3((unsigned)gx, 1, 1), dim3(kBalThreads, 1, 1),
+                       lp.lds, stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.act, P, lp.nps, lp.nblm,
+                       burst ? 1 : 0);
+    return hipGetLastError();
+}
+
+template <int RD, bool PARTS, bool ACT>
+static hipError_t launch_lds_rl(const GemvArgs &a, int gx, int P, bool burst, hipStream_t stream)
+{
+    const LdsPlan lp = lds_plan(a.M, a.K, a.N, gx, P, ACT, RD);
+    if (a.M <= 4) return launch_lds_v<RD, PARTS, ACT, 1>(a, gx, P, lp, burst, stream);
+    if (a.M <= 8) return launch_lds_v<RD, PARTS, ACT, 2>(a, gx, P, lp, burst, stream);
+    if (a.M <= 12) return launch_lds_v<RD, PARTS, ACT, 3>(a, gx, P, lp, burst, stream);
+    return launch_lds_v<RD, PARTS, ACT, 4>(a, gx, P, lp, burst, stream);
+}
+
+template <bool PARTS, bool ACT>
+static hipError_t launch_lds_rd(const GemvArgs &a, int gx, int P, int rd, bool burst, hipStream_t stream)
+{
+    return rd > 2 ? launch_lds_rl<4, PARTS, ACT>(a, gx, P, burst, stream)
+                  : launch_lds_rl<2, PARTS, ACT>(a, gx, P, burst, stream);
+}
+
+hipError_t launch_gemv_lds(const GemvArgs &a, int gx, int P, int rd, bool burst, hipStream_t stream)
+{
+    if (a.S != 1) return hipErrorInvalidValue;
+    if (a.act)
+        return P > 1 ? launch_lds_rd<true, true>(a, gx, P, rd, burst, stream)
+                     : launch_lds_rd<false, true>(a, gx, 1, rd, burst, stream);
+    return P > 1 ? launch_lds_rd<true, false>(a, gx, P, rd, burst, stream)
+                 : launch_lds_rd<false, false>(a, gx, 1, rd, burst, stream);
 }
 
 hipError_t launch_gemv_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)

@@ -143,6 +143,20 @@ BalPlan bal_plan(int M, int K, int N, int S, int gx, int P, bool act = false);
 // plan_bal (x and LDS fit).
 hipError_t launch_gemv_bal(const GemvArgs &a, int gx, int P, hipStream_t stream);
 
+// ---- LDS-fed balanced kernel ------------------------------------------------------
+// The balanced kernel's work split and arithmetic (same bits) with codes and
+// scales/minimums brought into LDS by direct-to-LDS loads: a ring of rd (2 or
+// 4) group pairs per wave; `burst` requests the first unit's weights before x.
+// Needs S == 1, K % 1024 == 0, 16-byte aligned scale/min, and total <= 160 KiB.
+struct LdsPlan {
+    size_t lds;     // dynamic LDS bytes
+    size_t total;   // dynamic + the rings' static LDS
+    int nblm;       // most 8-group blocks of one unit
+    int nps;        // part-sum slots (P > 1)
+};
+LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd);
+hipError_t launch_gemv_lds(const GemvArgs &a, int gx, int P, int rd, bool burst, hipStream_t stream);
+
 // ---- work-balanced (stream-K) kernel ----------------------------------------
 constexpr int kSkWaves = 8;                 // waves per workgroup, one workgroup per CU
 constexpr int kSkThreads = 64 * kSkWaves;
