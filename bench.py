@@ -287,8 +287,11 @@ def measure_down(torch, q, steps, warmup):
     calls, splits = rc.prepare(case, max(2, math.ceil(ROTATE_BYTES / B)))
     n = max(steps, len(calls))
     t = timed_launches(torch, calls, n, warmup) * 1e-3 / n
+    # With the default split count equal to the one-launch form's K parts, a
+    # one-row call is that single launch; other split counts add the reduce.
+    one = splits == 1 or splits == q.q4g128_gemm_parts(case.K, case.N)
     return {"us_per_call": round(t * 1e6, 3), "GBps": round(B / t / 1e9, 1), "splits": splits,
-            "bytes_per_call": B, "kernels_per_call": 2 if splits > 1 else 1}
+            "bytes_per_call": B, "kernels_per_call": 1 if one else 2}
 
 
 def measure_stream(torch, q, reps=5, warmup=2):

@@ -116,13 +116,14 @@ int bal_parts(int K, int N, int gx, int minpart)
 }
 
 // Workgroups and K parts of the plain product, from (K, N) and the CU count
-// only.  Short-K shapes (K <= kBalShortK, N a multiple of 16) whose columns
-// would leave each workgroup partial tiles (6144 -> 5120: two 10-column
+// only.  Shapes (N a multiple of 16) whose columns would leave each
+// workgroup partial tiles (6144 -> 5120 and 17408 -> 5120: two 10-column
 // tiles per CU) instead get whole 16-column tiles on fewer workgroups and
 // parts as short as one 8-group block (6144 -> 5120: 160 workgroups of two
-// tiles in 6 parts, 7.95 vs 8.78 us).  Longer K keeps the plain cut: there
-// the one launch stages all of x before any weight load, and K splits with a
-// reduce stream faster (17408 -> 5120).
+// tiles in 6 parts, 7.95 vs 8.78 us; 17408 -> 5120: 160 workgroups of two
+// tiles in 6 parts, one launch of the LDS-fed kernel with its weights
+// requested before x, 13.4 us, against 14.7-15.3 us for the plain cut in 5
+// parts and 13.1 us for 6 K splits and a reduce, one box).
 struct BalGrid {
     int gx;
     int P;
@@ -133,7 +134,7 @@ BalGrid plain_grid(int K, int N, int ncu)
     using namespace q4g128;
     BalGrid g = {bal_gx(N, false, ncu), 1};
     if (bal_tiles(N, g.gx) >= kBalMinTiles) return g;
-    if (K <= kBalShortK && N % 16 == 0 && N % (16 * g.gx) != 0) {
+    if (N % 16 == 0 && N % (16 * g.gx) != 0) {
         const int n16 = N / 16;
         const int per = (n16 + ncu - 1) / ncu;                 // whole tiles per workgroup
         const int gw = (n16 + per - 1) / per;
@@ -189,14 +190,14 @@ BalChoice plan_bal(int M, int K, int N, const void *scale, const void *min, bool
 
 // Which balanced kernel runs a planned launch.  Both give the same bits.
 // Workgroups of many whole tiles (8 or more, K not cut: gate/up, the output
-// projection, their SwiGLU and verify forms) take the LDS-fed kernel, with a
-// ring of 2 group pairs per wave and the weights requested before x:
-// gate/up 19.7-20.6 -> 18.3-18.6 us, verify M = 7 21.5 -> 20.6 us, SwiGLU
-// 20.6 -> 18.7 us (one box, interleaved).  Deeper rings (4 pairs) were
-// slower on every shape.  Short shapes (few tiles per CU, or K parts) stay on
-// the register-ring kernel, which was as fast or faster there (5120 -> 12288:
-// 10.3 vs 10.6-13.1 us; 6144 -> 5120: 7.6 vs 7.8 us).  A shape whose LDS does
-// not fit the LDS-fed kernel takes the other one.
+// projection, their SwiGLU and verify forms) take the LDS-fed kernel with a
+// ring of 2 group pairs per wave: gate/up 19.7-20.6 -> 18.3-18.6 us, verify
+// M = 7 21.5 -> 20.6 us, SwiGLU 20.6 -> 18.7 us (one box, interleaved).  K-part
+// shapes take it with the weights requested before x (17408 -> 5120 in 6
+// parts: 13.4 against 14.7 us; 6144 -> 5120: even).  Deeper rings (4 pairs)
+// were slower on every shape.  Few whole tiles per CU without parts (5120 ->
+// 12288) stay on the register-ring kernel (10.3 against 10.6-13.1 us).  A
+// shape whose LDS does not fit the LDS-fed kernel takes the other one.
 #ifndef Q4G128_LDS_MODE
 #define Q4G128_LDS_MODE -1
 #endif
@@ -206,12 +207,12 @@ hipError_t launch_balanced(const q4g128::GemvArgs &a, int gx, int P, hipStream_t
     int mode = Q4G128_LDS_MODE;                 // 0: register ring; 1-4: LDS-fed (rd 2/2/4/4, burst on 2 and 4)
     if (mode < 0) {
         const int tiles = a.act ? (((a.N / 2 + 3) / 4 + gx - 1) / gx * 4 + 7) / 8 : bal_tiles(a.N, gx);
-        mode = (P == 1 && tiles >= kBalMinTiles) ? 2 : 0;
+        mode = P > 1 ? (a.act ? 1 : 2) : tiles >= kBalMinTiles ? 1 : 0;
     }
     if (mode > 0) {
         const int rd = mode >= 3 ? 4 : 2;
         const bool burst = mode == 2 || mode == 4;
-        if (lds_plan(a.M, a.K, a.N, gx, P, a.act != nullptr, rd).total <= kBalMaxLds)
+        if (lds_plan(a.M, a.K, a.N, gx, P, a.act != nullptr, rd, burst).fits)
             return launch_gemv_lds(a, gx, P, rd, burst, stream);
     }
     return launch_gemv_bal(a, gx, P, stream);
@@ -386,17 +387,18 @@ size_t q4g128_splitk_workspace_bytes(int M, int N, int splits)
 int q4g128_splitk_default_splits(int K, int N)
 {
     if (K <= 0 || K % Q4G128_GROUP != 0 || N <= 0 || K > kMaxK || N > kMaxN) return 0;
-    // No splits where the balanced kernel takes the shape in one launch for
-    // the usual M: with whole tiles when x for one row fits (wider M falls
-    // back to the per-tile kernel, which then has enough tiles), with K parts
-    // when one launch holds kBalRowBlock rows.  Short-N shapes whose K-part
-    // launch holds fewer rows (the 17408 -> 5120 down projection: 2) stream
-    // faster as K splits and a reduce: narrow tiles leave each CU fewer bytes
-    // in flight (measured over the whole decode step).
+    // Where the balanced kernels take the shape in one launch for one row:
+    // no splits when it does not cut K (wider M falls back to the per-tile
+    // kernel, which then has enough tiles); when it cuts K into parts, that
+    // many splits, so that the split-K call runs the one launch for the rows
+    // it holds (the 17408 -> 5120 down projection: 6 parts, one row at a time
+    // in the LDS-fed kernel, two in the register-ring one) and the per-tile
+    // kernel with the same splits and a reduce beyond, which streams the
+    // weights once for any M (same bits either way).
     const int ncu = device_cus();
     if (K % 1024 == 0 && ncu > 0) {
         const BalGrid g = plain_grid(K, N, ncu);
-        if (bal_fits(g.P > 1 ? kBalRowBlock : 1, K, N, g.gx, g.P, false)) return 1;
+        if (bal_fits(1, K, N, g.gx, g.P, false)) return g.P;
     }
     const long nb = k_blocks(K);
     const long tpw = plan_tiles_per_wave(K, N);

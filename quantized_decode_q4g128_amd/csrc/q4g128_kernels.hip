@@ -734,6 +734,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
 // between the kernels never changes a bit.
 
 constexpr int kLdsSlotU4 = 128;            // u32x4 per wave and ring slot: one group pair of a 16-column tile
+constexpr int kLdsBurstBlocks = 4;         // BURST: blocks of 8 groups per unit, at most
 
 // Waits until the loads of a ring slot have landed, given how many later
 // pairs (two loads each) this wave has requested since (0 .. 3).  Vector
@@ -770,19 +771,26 @@ __device__ __forceinline__ void group_fma(const u32x4 (&a)[4], const f32x4 &xsum
     }
 }
 
-template <int RD, bool PARTS, bool ACT, int RL>
+template <int RD, bool PARTS, bool ACT, int RL, bool BURST>
 __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ mn, int N,
-    float *__restrict__ out, uint16_t *__restrict__ act, int P, int nps, int nblm, int burst)
+    float *__restrict__ out, uint16_t *__restrict__ act, int P, int nps, int nblm)
 {
     static_assert(RD == 2 || RD == 4, "ring depth: units are whole blocks of 4 pairs");
+    constexpr bool burst = BURST;
     __shared__ __attribute__((aligned(16))) u32x4 ring0[kBalWaves * kLdsSlotU4];
     __shared__ __attribute__((aligned(16))) u32x4 ring1[kBalWaves * kLdsSlotU4];
     __shared__ __attribute__((aligned(16))) u32x4 ring2[RD > 2 ? kBalWaves * kLdsSlotU4 : 1];
     __shared__ __attribute__((aligned(16))) u32x4 ring3[RD > 2 ? kBalWaves * kLdsSlotU4 : 1];
+    // BURST: the scale/minimum areas in an array of their own (units of at
+    // most kLdsBurstBlocks blocks), so that x, staged while every load of the
+    // burst is in flight, provably shares no LDS with them and its staging
+    // waits for the x loads alone.
+    __shared__ __attribute__((aligned(16))) uint8_t smst[BURST ? kBalWaves * 512 * kLdsBurstBlocks : 16];
     extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
     u32x4 *const rings[4] = {ring0, ring1, ring2, ring3};
+    if (BURST) nblm = kLdsBurstBlocks;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -820,7 +828,8 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     // fp32, then one scale/minimum area per wave: [scale, min][16 columns][nblm
     // blocks] of 16 bytes.
     float *slots = reinterpret_cast<float *>(xs + M * G * 128 + G * kXsRows * 2);
-    uint8_t *smarea = reinterpret_cast<uint8_t *>(slots + nps * 256) + (size_t)wave * (512 * nblm);
+    uint8_t *smarea = BURST ? smst + wave * (512 * kLdsBurstBlocks)
+                            : reinterpret_cast<uint8_t *>(slots + nps * 256) + (size_t)wave * (512 * nblm);
 
     const int i = lane & 15, h = lane >> 4;
     const int cq = lane >> 3, jq = lane & 7;
@@ -848,11 +857,15 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
                                                  so, 0, kPairCpol);
     };
     // Unit u: descriptors and its scale/minimum pieces into the wave's area.
-    auto setup_unit = [&](int u) {
+    // live == false (a wave without a unit, burst only): unit 0's geometry
+    // with empty descriptors, so its loads read nothing and only fill its own
+    // slots with zeros; every wave then issues the same sequence of loads,
+    // which lets the compiler count exactly the loads x's staging waits for.
+    auto setup_unit = [&](int u, bool live) {
         // The area's earlier reads are complete before new pieces may land.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         int cb, cw, cs, ce;
-        unit(u, cb, cw, cs, ce);
+        unit(live ? u : 0, cb, cw, cs, ce);
         cb = __builtin_amdgcn_readfirstlane(cb);
         cw = __builtin_amdgcn_readfirstlane(cw);
         ucs = __builtin_amdgcn_readfirstlane(cs);
@@ -860,7 +873,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
         unblk = __builtin_amdgcn_readfirstlane((ce - cs) >> 3);
         ucw = cw;
         ucb = cb;
-        const size_t span = ACT ? (size_t)NC + cw : (size_t)cw;
+        const size_t span = live ? (ACT ? (size_t)NC + cw : (size_t)cw) : 0;
         rw = make_rsrc(W + (size_t)cb * K8, (uint32_t)(span * K8 * 4));
         rs = make_rsrc(scale + (size_t)cb * G, (uint32_t)(span * G * 2));
         rm = make_rsrc(mn + (size_t)cb * G, (uint32_t)(span * G * 2));
@@ -889,9 +902,9 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     };
 
     XStage<kBalThreads, kBalStage, kRowPerm> xst;
-    if (burst && active) setup_unit(wave);
+    if (burst) setup_unit(wave, active);
     xst.load(x, M, K, 0, G);
-    if (burst && active) prime();                 // after x: x's loads stay the oldest of the wave
+    if (burst) prime();                           // after x: x's loads stay the oldest of the wave
     xst.store(xs, M, 0, G);
     lds_barrier();
     if (!PARTS && !active) return;
@@ -908,7 +921,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     if (active) {
         for (int u = wave; u < nunit; u += kBalWaves) {
             if (!(burst && u == wave)) {
-                setup_unit(u);
+                setup_unit(u, true);
                 prime();
             }
             float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1339,7 +1352,7 @@ static hipError_t launch_bal(const GemvArgs &a, int gx, int P, hipStream_t strea
     return launch_bal_rl<PARTS, ACT, 4>(a, gx, P, stream);
 }
 
-LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd)
+LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd, bool burst)
 {
     LdsPlan lp;
     const int G = K / 128, nb = G / 8;
@@ -1355,51 +1368,61 @@ LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd)
     const int nact = units < kBalWaves ? units : kBalWaves;
     lp.nblm = P > 1 ? (nb + P - 1) / P : nb;
     lp.nps = P > 1 ? units : 0;
-    const size_t stat = (size_t)(rd > 2 ? 4 : 2) * kBalWaves * kLdsSlotU4 * 16 + (rd > 2 ? 0 : 32);
-    lp.lds = (size_t)M * G * 256 + (size_t)G * kXsRows * 4 + (size_t)lp.nps * 1024 + (size_t)nact * 512 * lp.nblm;
+    const size_t stat = (size_t)(rd > 2 ? 4 : 2) * kBalWaves * kLdsSlotU4 * 16 + (rd > 2 ? 0 : 32) +
+                        (burst ? (size_t)kBalWaves * 512 * kLdsBurstBlocks : 16);
+    lp.fits = !burst || lp.nblm <= kLdsBurstBlocks;
+    lp.lds = (size_t)M * G * 256 + (size_t)G * kXsRows * 4 + (size_t)lp.nps * 1024 +
+             (burst ? 0 : (size_t)nact * 512 * lp.nblm);
     if (lp.lds + stat < kBalOwnCu) lp.lds = kBalOwnCu - stat;
     lp.total = lp.lds + stat;
+    lp.fits = lp.fits && lp.total <= kBalMaxLds;
     return lp;
 }
 
-template <int RD, bool PARTS, bool ACT, int RL>
-static hipError_t launch_lds_v(const GemvArgs &a, int gx, int P, const LdsPlan &lp, bool burst, hipStream_t stream)
+template <int RD, bool PARTS, bool ACT, int RL, bool BURST>
+static hipError_t launch_lds_v(const GemvArgs &a, int gx, int P, const LdsPlan &lp, hipStream_t stream)
 {
     static LdsFlags done;
-    const hipError_t attr = allow_dynamic_lds(reinterpret_cast<const void *>(&gemv_q4g128_lds<RD, PARTS, ACT, RL>),
-                                              (int)(kBalMaxLds - (lp.total - lp.lds)), done);
+    const void *k = reinterpret_cast<const void *>(&gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST>);
+    const hipError_t attr = allow_dynamic_lds(k, (int)(kBalMaxLds - (lp.total - lp.lds)), done);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemv_q4g128_lds<RD, PARTS, ACT, RL>), dim3((unsigned)gx, 1, 1), dim3(kBalThreads, 1, 1),
-                       lp.lds, stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.act, P, lp.nps, lp.nblm,
-                       burst ? 1 : 0);
+    hipLaunchKernelGGL((gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST>), dim3((unsigned)gx, 1, 1),
+                       dim3(kBalThreads, 1, 1), lp.lds, stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.act,
+                       P, lp.nps, lp.nblm);
     return hipGetLastError();
 }
 
-template <int RD, bool PARTS, bool ACT>
-static hipError_t launch_lds_rl(const GemvArgs &a, int gx, int P, bool burst, hipStream_t stream)
+template <int RD, bool PARTS, bool ACT, bool BURST>
+static hipError_t launch_lds_rl(const GemvArgs &a, int gx, int P, hipStream_t stream)
 {
-    const LdsPlan lp = lds_plan(a.M, a.K, a.N, gx, P, ACT, RD);
-    if (a.M <= 4) return launch_lds_v<RD, PARTS, ACT, 1>(a, gx, P, lp, burst, stream);
-    if (a.M <= 8) return launch_lds_v<RD, PARTS, ACT, 2>(a, gx, P, lp, burst, stream);
-    if (a.M <= 12) return launch_lds_v<RD, PARTS, ACT, 3>(a, gx, P, lp, burst, stream);
-    return launch_lds_v<RD, PARTS, ACT, 4>(a, gx, P, lp, burst, stream);
+    const LdsPlan lp = lds_plan(a.M, a.K, a.N, gx, P, ACT, RD, BURST);
+    if (!lp.fits) return hipErrorInvalidValue;
+    if (a.M <= 4) return launch_lds_v<RD, PARTS, ACT, 1, BURST>(a, gx, P, lp, stream);
+    if (a.M <= 8) return launch_lds_v<RD, PARTS, ACT, 2, BURST>(a, gx, P, lp, stream);
+    if (a.M <= 12) return launch_lds_v<RD, PARTS, ACT, 3, BURST>(a, gx, P, lp, stream);
+    return launch_lds_v<RD, PARTS, ACT, 4, BURST>(a, gx, P, lp, stream);
 }
 
-template <bool PARTS, bool ACT>
-static hipError_t launch_lds_rd(const GemvArgs &a, int gx, int P, int rd, bool burst, hipStream_t stream)
-{
-    return rd > 2 ? launch_lds_rl<4, PARTS, ACT>(a, gx, P, burst, stream)
-                  : launch_lds_rl<2, PARTS, ACT>(a, gx, P, burst, stream);
-}
-
+// Variants built: ring 2 without burst (any shape, the fused SwiGLU too), and
+// burst with rings of 2 or 4 (plain product only).
 hipError_t launch_gemv_lds(const GemvArgs &a, int gx, int P, int rd, bool burst, hipStream_t stream)
 {
     if (a.S != 1) return hipErrorInvalidValue;
-    if (a.act)
-        return P > 1 ? launch_lds_rd<true, true>(a, gx, P, rd, burst, stream)
-                     : launch_lds_rd<false, true>(a, gx, 1, rd, burst, stream);
-    return P > 1 ? launch_lds_rd<true, false>(a, gx, P, rd, burst, stream)
-                 : launch_lds_rd<false, false>(a, gx, 1, rd, burst, stream);
+    if (a.act) {
+        if (burst || rd != 2) return hipErrorInvalidValue;
+        return P > 1 ? launch_lds_rl<2, true, true, false>(a, gx, P, stream)
+                     : launch_lds_rl<2, false, true, false>(a, gx, 1, stream);
+    }
+    if (!burst) {
+        if (rd != 2) return hipErrorInvalidValue;
+        return P > 1 ? launch_lds_rl<2, true, false, false>(a, gx, P, stream)
+                     : launch_lds_rl<2, false, false, false>(a, gx, 1, stream);
+    }
+    if (rd > 2)
+        return P > 1 ? launch_lds_rl<4, true, false, true>(a, gx, P, stream)
+                     : launch_lds_rl<4, false, false, true>(a, gx, 1, stream);
+    return P > 1 ? launch_lds_rl<2, true, false, true>(a, gx, P, stream)
+                 : launch_lds_rl<2, false, false, true>(a, gx, 1, stream);
 }
 
 hipError_t launch_gemv_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)

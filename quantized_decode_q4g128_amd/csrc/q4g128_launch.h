@@ -126,7 +126,6 @@ constexpr int kBalMinTiles = 8;             // fewer tiles per workgroup: cut ea
 #define Q4G128_BAL_MINPART 24
 #endif
 constexpr int kBalMinPart = Q4G128_BAL_MINPART;   // groups per K part, at least
-constexpr int kBalShortK = 8192;            // K up to which partial-tile shapes get whole tiles and 1-block parts
 constexpr size_t kBalMaxLds = 160 * 1024;
 
 // Launch geometry of the balanced kernel for M rows, S K splits, gx
@@ -147,14 +146,16 @@ hipError_t launch_gemv_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)
 // The balanced kernel's work split and arithmetic (same bits) with codes and
 // scales/minimums brought into LDS by direct-to-LDS loads: a ring of rd (2 or
 // 4) group pairs per wave; `burst` requests the first unit's weights before x.
-// Needs S == 1, K % 1024 == 0, 16-byte aligned scale/min, and total <= 160 KiB.
+// Needs S == 1, K % 1024 == 0, 16-byte aligned scale/min, and lds_plan().fits;
+// built variants: rd 2 (plain or fused SwiGLU), burst with rd 2 or 4 (plain).
 struct LdsPlan {
     size_t lds;     // dynamic LDS bytes
-    size_t total;   // dynamic + the rings' static LDS
+    size_t total;   // dynamic + the static LDS (rings; burst: scale/minimum areas)
     int nblm;       // most 8-group blocks of one unit
     int nps;        // part-sum slots (P > 1)
+    bool fits;      // total <= 160 KiB, and (burst) units of at most 4 blocks
 };
-LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd);
+LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd, bool burst);
 hipError_t launch_gemv_lds(const GemvArgs &a, int gx, int P, int rd, bool burst, hipStream_t stream);
 
 // ---- work-balanced (stream-K) kernel ----------------------------------------
