@@ -365,8 +365,9 @@ def measure_epilogues(torch, q, steps, warmup):
     h = torch.empty((dn.M, dn.N), dtype=torch.float32, device=dev)
     xo = torch.empty((dn.M, dn.N), dtype=torch.int16, device=dev)
     S = q.q4g128_splitk_default_splits(dn.K, dn.N)
-    wsb = q.q4g128_splitk_workspace_bytes(dn.M, dn.N, S)
-    ws = torch.empty(max(wsb, 4) // 4, dtype=torch.float32, device=dev)
+    ws = q.q4g128_rmsnorm_workspace(dn.M, dn.N, S, dev)
+    wsb = ws.numel() * 4
+    one_launch = 1 < S == q.q4g128_gemm_parts(dn.K, dn.N) and dn.M == 1      # the one-launch form's condition
     calls = [lambda st, a=(x.data_ptr(), dn.M, dn.K, W.data_ptr(), sc.data_ptr(), mn.data_ptr(), dn.N, r.data_ptr(),
                            gamma.data_ptr(), 1e-6, h.data_ptr(), xo.data_ptr(), S, ws.data_ptr(), wsb):
              L.q4g128_gemm_rmsnorm(*a, st) for W, sc, mn in sets]
@@ -374,7 +375,7 @@ def measure_epilogues(torch, q, steps, warmup):
     t = timed_calls(torch, calls, reps, 1) * 1e-3 / (reps * len(calls))
     Bo = B + 4 * dn.M * dn.N + 2 * dn.N + 2 * dn.M * dn.N       # + residual in, gamma, bf16 x_out
     out["down_rmsnorm_M1"] = {"us_per_call": round(t * 1e6, 3), "GBps": round(Bo / t / 1e9, 1),
-                              "bytes_per_call": Bo, "splits": S, "launches_per_call": 2}
+                              "bytes_per_call": Bo, "splits": S, "launches_per_call": 1 if one_launch else 2}
     del sets
     torch.cuda.empty_cache()
     return out
@@ -416,6 +417,8 @@ def measure_chain(torch, q, reps=5):
     g_d = torch.from_numpy(synth.to_bf16_bits(1.0 + 0.1 * rng.standard_normal(d)).view(np.int16)).to(dev)
     S_o = q.q4g128_splitk_default_splits(6144, d)
     S_d = q.q4g128_splitk_default_splits(17408, d)
+    wsn = q.q4g128_rmsnorm_workspace(1, d, max(S_o, S_d), dev)       # control block zero: the norms' own
+    wsnb = wsn.numel() * 4
     wsb = max(q.q4g128_splitk_workspace_bytes(1, d, S_o), q.q4g128_splitk_workspace_bytes(1, d, S_d),
               q.q4g128_swiglu_workspace_bytes(1, 5120, 34816))
     ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
@@ -428,13 +431,13 @@ def measure_chain(torch, q, reps=5):
         seq.append(lambda st, A=(x.data_ptr(), 1, 5120, Wq.data_ptr(), sq.data_ptr(), mq.data_ptr(), 12288,
                                  qkv.data_ptr()): L.q4g128_gemm(*A, st))
         seq.append(lambda st, A=(a.data_ptr(), 1, 6144, Wo.data_ptr(), so.data_ptr(), mo.data_ptr(), d, h.data_ptr(),
-                                 g_o.data_ptr(), 1e-6, h.data_ptr(), xm.data_ptr(), S_o, ws.data_ptr(), wsb):
+                                 g_o.data_ptr(), 1e-6, h.data_ptr(), xm.data_ptr(), S_o, wsn.data_ptr(), wsnb):
                    L.q4g128_gemm_rmsnorm(*A, st))
         seq.append(lambda st, A=(xm.data_ptr(), 1, 5120, Wg.data_ptr(), sg.data_ptr(), mg.data_ptr(), 34816,
                                  act.data_ptr(), ws.data_ptr(), wsb): L.q4g128_gemm_swiglu(*A, st))
         seq.append(lambda st, A=(act.data_ptr(), 1, 17408, Wd.data_ptr(), sd.data_ptr(), md.data_ptr(), d,
-                                 h.data_ptr(), g_d.data_ptr(), 1e-6, h.data_ptr(), x.data_ptr(), S_d, ws.data_ptr(),
-                                 wsb): L.q4g128_gemm_rmsnorm(*A, st))
+                                 h.data_ptr(), g_d.data_ptr(), 1e-6, h.data_ptr(), x.data_ptr(), S_d, wsn.data_ptr(),
+                                 wsnb): L.q4g128_gemm_rmsnorm(*A, st))
     Wh, sh, mh = head
     seq.append(lambda st, A=(x.data_ptr(), 1, 5120, Wh.data_ptr(), sh.data_ptr(), mh.data_ptr(), 131072,
                              logits.data_ptr()): L.q4g128_gemm(*A, st))

@@ -197,6 +197,11 @@ q4g128_status q4g128_gemm_swiglu(const void *x, int M, int K,
                                  int N, void *act, float *workspace, size_t workspace_bytes,
                                  void *stream);
 
+/* Bytes of workspace q4g128_gemm_rmsnorm needs: 256 (a control block) +
+ * q4g128_splitk_workspace_bytes(M, N, splits).  Returns 0 for invalid
+ * arguments. */
+size_t q4g128_rmsnorm_workspace_bytes(int M, int N, int splits);
+
 /* The product followed by a residual add and RMSNorm, with the split-K
  * partial sums added inside the norm (Token Rush README, steps table rows
  * 8-9: a split-K GEMV whose partials are summed in the norm):
@@ -208,15 +213,29 @@ q4g128_status q4g128_gemm_swiglu(const void *x, int M, int K,
  * y is the product with K cut into `splits` ranges exactly as in
  * q4g128_gemm_splitk (splits == 1: not cut), its partials summed in
  * ascending split order, so h equals fp32(residual + y_splitk) bit for bit.
- * The sum of squares is taken in a fixed order (per thread of a
- * 1024-thread workgroup per row, then a fixed tree), the square root and
- * division correctly rounded.  residual and h fp32 [M][N] (h may be the
- * residual itself, updated in place; 4-byte aligned); gamma bf16 [N];
- * x_out bf16 [M][N] (the next product's input; 2-byte aligned); eps >= 0.
- * The RMSNorm formula is the usual one of the model family the pages run;
- * the pages do not spell it out.  Workspace: at least
- * q4g128_splitk_workspace_bytes(M, N, splits) bytes, for splits == 1 too.
- * Rows are bit-identical across M; results deterministic. */
+ * The sum of squares is taken in a fixed order: 256 partial sums, partial p
+ * the fused multiply-add chain over the columns n = p, p+256, p+512, ...
+ * (n < N) in ascending n; then a fixed tree over the 256.  The square root and division are correctly rounded.
+ * residual and h fp32 [M][N] (h may be the residual itself, updated in
+ * place; 4-byte aligned); gamma bf16 [N]; x_out bf16 [M][N] (the next
+ * product's input; 2-byte aligned); eps >= 0.  The RMSNorm formula is the
+ * usual one of the model family the pages run; the pages do not spell it
+ * out.  Rows are bit-identical across M; results deterministic.
+ *
+ * When `splits` equals q4g128_gemm_parts(K, N) > 1 and the M rows fit that
+ * launch's LDS (M <= 8; x for all of K is held there, so 17408 -> 5120 takes
+ * one row), the whole call is one launch: each workgroup adds the
+ * residual to its own columns, and the workgroup that finishes last (found
+ * by a counter) normalises the rows.  Otherwise the partials go to the
+ * workspace and a second launch sums them and normalises.  Both give the
+ * same bits.
+ *
+ * Workspace: at least q4g128_rmsnorm_workspace_bytes(M, N, splits) bytes,
+ * 4-byte aligned.  Its first 256 bytes are a control block that must hold
+ * zeros when the workspace is first given to this function (clear it once,
+ * e.g. with hipMemset); every call that completes leaves them zero again.
+ * No other call may write them in between, and calls in flight must not
+ * share a workspace. */
 q4g128_status q4g128_gemm_rmsnorm(const void *x, int M, int K,
                                   const uint32_t *W, const void *scale, const void *min,
                                   int N, const float *residual, const void *gamma, float eps,

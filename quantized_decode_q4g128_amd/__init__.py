@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.q4g128_quantize.restype = ci
         L.q4g128_splitk_workspace_bytes.argtypes = [ci, ci, ci]
         L.q4g128_splitk_workspace_bytes.restype = sz
+        L.q4g128_rmsnorm_workspace_bytes.argtypes = [ci, ci, ci]
+        L.q4g128_rmsnorm_workspace_bytes.restype = sz
         L.q4g128_gemm_parts.argtypes = [ci, ci]
         L.q4g128_gemm_parts.restype = ci
         L.q4g128_splitk_default_splits.argtypes = [ci, ci]
@@ -96,6 +98,20 @@ def q4g128_last_error() -> str:
 
 def q4g128_splitk_workspace_bytes(M: int, N: int, splits: int) -> int:
     return int(lib().q4g128_splitk_workspace_bytes(int(M), int(N), int(splits)))
+
+
+def q4g128_rmsnorm_workspace_bytes(M: int, N: int, splits: int) -> int:
+    return int(lib().q4g128_rmsnorm_workspace_bytes(int(M), int(N), int(splits)))
+
+
+def q4g128_rmsnorm_workspace(M: int, N: int, splits: int, device) -> torch.Tensor:
+    """A zero-filled workspace for q4g128_gemm_rmsnorm on (M, N, splits);
+    reusable by later calls of that size or smaller (they leave its control
+    block zero) as long as nothing else writes it."""
+    nbytes = q4g128_rmsnorm_workspace_bytes(M, N, splits)
+    if nbytes == 0:
+        raise ValueError(f"invalid rmsnorm workspace request M={M} N={N} splits={splits}")
+    return torch.zeros((nbytes // 4,), dtype=torch.float32, device=device)
 
 
 def q4g128_splitk_default_splits(K: int, N: int) -> int:
@@ -301,7 +317,10 @@ def q4g128_gemm_rmsnorm(x, W, scale, min, residual, gamma, eps: float = 1e-6, sp
                         workspace=None, stream=None):
     """(h, x_out): h = residual + x . dequant(W) (fp32 [M][N]; pass h=residual
     to update it in place), x_out = bf16(h / sqrt(mean(h^2) + eps) * gamma),
-    the split-K partials (default split count) summed inside the norm."""
+    the split-K partials (default split count) summed inside the norm.
+    A given `workspace` must come from q4g128_rmsnorm_workspace (its first
+    256 bytes zero; every call leaves them so) and must not be written by
+    other calls in between."""
     x, W, scale, min, M, K, N = _operands(x, W, scale, min)
     residual = _dev(residual, "residual", (torch.float32,))
     gamma = _dev(gamma, "gamma", _HALF, ndim=1)
@@ -313,8 +332,9 @@ def q4g128_gemm_rmsnorm(x, W, scale, min, residual, gamma, eps: float = 1e-6, sp
     x_out = _half_out(x_out, "x_out", (M, N), x.device)
     if splits is None:
         splits = q4g128_splitk_default_splits(K, N)
-    need = q4g128_splitk_workspace_bytes(M, N, splits) if splits >= 1 else 0
-    workspace = _workspace(workspace, need, x.device)
+    if workspace is None and splits >= 1:
+        workspace = q4g128_rmsnorm_workspace(M, N, splits, x.device)
+    workspace = _workspace(workspace, 0, x.device)
     st = lib().q4g128_gemm_rmsnorm(x.data_ptr(), M, K, W.data_ptr(), scale.data_ptr(), min.data_ptr(), N,
                                    residual.data_ptr(), gamma.data_ptr(), float(eps), h.data_ptr(), x_out.data_ptr(),
                                    int(splits), workspace.data_ptr(), workspace.numel() * 4,
@@ -355,7 +375,8 @@ def q4g128_quantize(w, ncand: int = 9, W=None, scale=None, min=None, err=None, s
 
 
 __all__ = ["q4g128_gemm", "q4g128_quantize", "q4g128_gemm_swiglu", "q4g128_swiglu_workspace_bytes",
-           "q4g128_gemm_rmsnorm", "q4g128_gemm_splitk", "q4g128_gemm_splitk_noalloc", "q4g128_gemm_streamk", "q4g128_streamk_workspace",
+           "q4g128_gemm_rmsnorm", "q4g128_rmsnorm_workspace", "q4g128_rmsnorm_workspace_bytes",
+           "q4g128_gemm_splitk", "q4g128_gemm_splitk_noalloc", "q4g128_gemm_streamk", "q4g128_streamk_workspace",
            "q4g128_streamk_workspace_bytes", "q4g128_dequant", "q4g128_splitk_workspace_bytes",
            "q4g128_splitk_default_splits", "q4g128_gemm_parts", "q4g128_status_string", "q4g128_last_error",
            "q4g128_abi_version", "Q4G128Error", "lib", "LIB_PATH"]

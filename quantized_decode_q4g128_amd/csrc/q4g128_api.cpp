@@ -26,6 +26,10 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 constexpr int kMaxK = 1 << 24;
 constexpr int kMaxN = 1 << 28;
 constexpr int kMaxSplits = 65535;
+// q4g128_gemm_rmsnorm's workspace starts with a control block (word 0: the
+// one-launch form's arrival counter, zero between calls); its split-K
+// partials follow.
+constexpr size_t kNormCtlBytes = 256;
 
 bool shape_ok(int M, int K, int N)
 {
@@ -567,6 +571,12 @@ q4g128_status q4g128_gemm_swiglu(const void *x, int M, int K, const uint32_t *W,
                       static_cast<hipStream_t>(stream));
 }
 
+size_t q4g128_rmsnorm_workspace_bytes(int M, int N, int splits)
+{
+    const size_t b = q4g128_splitk_workspace_bytes(M, N, splits);
+    return b ? b + kNormCtlBytes : 0;
+}
+
 q4g128_status q4g128_gemm_rmsnorm(const void *x, int M, int K, const uint32_t *W, const void *scale, const void *min,
                                   int N, const float *residual, const void *gamma, float eps, float *h, void *x_out,
                                   int splits, float *workspace, size_t workspace_bytes, void *stream)
@@ -577,12 +587,31 @@ q4g128_status q4g128_gemm_rmsnorm(const void *x, int M, int K, const uint32_t *W
     if (!(eps >= 0.0f) || eps > 3.0e38f) return Q4G128_EINVAL;
     if (splits < 1 || splits > max_splits(K) || splits > kMaxSplits) return Q4G128_EINVAL;
     if (!workspace || !aligned(workspace, 4)) return Q4G128_EINVAL;
-    if (workspace_bytes < q4g128_splitk_workspace_bytes(M, N, splits)) return Q4G128_EWORKSPACE;
+    if (workspace_bytes < q4g128_rmsnorm_workspace_bytes(M, N, splits)) return Q4G128_EWORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    clear_pending_error();
+    // One launch when the splits are the balanced kernel's K parts and the
+    // rows fit it: each workgroup adds the residual to its own columns and
+    // the last one to finish normalises the rows (same bits as below).
+    if (splits > 1) {
+        const BalChoice bc = plan_bal(M, K, N, scale, min);
+        if (bc.gx > 0 && bc.P == splits && M <= bc.rb && q4g128::lds_norm_fits(M, K, N, bc.gx, bc.P)) {
+            const q4g128::GemvArgs a = gemv_args(x, M, K, W, scale, min, N, h, 1);
+            const q4g128::NormArgs na = {residual, static_cast<const uint16_t *>(gamma), eps,
+                                         static_cast<uint16_t *>(x_out), reinterpret_cast<uint32_t *>(workspace)};
+            const hipError_t e = q4g128::launch_gemv_lds_norm(a, bc.gx, bc.P, na, st);
+            if (e != hipSuccess) {
+                set_error("gemv+rmsnorm launch", e);
+                return Q4G128_EHIP;
+            }
+            return Q4G128_OK;
+        }
+    }
+    float *ws = workspace + kNormCtlBytes / sizeof(float);   // the control block stays untouched
     int slices = 0;
-    q4g128_status rc = run_split(x, M, K, W, scale, min, N, splits, workspace, workspace, &slices, st);
+    q4g128_status rc = run_split(x, M, K, W, scale, min, N, splits, ws, ws, &slices, st);
     if (rc != Q4G128_OK) return rc;
-    hipError_t e = q4g128::launch_sum_residual_rmsnorm(workspace, slices, M, N, residual,
+    hipError_t e = q4g128::launch_sum_residual_rmsnorm(ws, slices, M, N, residual,
                                                        static_cast<const uint16_t *>(gamma), eps, h,
                                                        static_cast<uint16_t *>(x_out), st);
     if (e != hipSuccess) {

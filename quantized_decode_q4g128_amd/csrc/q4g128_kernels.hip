@@ -414,6 +414,48 @@ __device__ __forceinline__ uint16_t swiglu_bf16(float g, float u)
     return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
 }
 
+__device__ __forceinline__ uint16_t bf16_rne(float a)
+{
+    const uint32_t b = __float_as_uint(a);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+    return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+// Sum of squares of one row's h values, in the one order every kernel that
+// normalises uses (so a row's output does not depend on which kernel served
+// it): 256 partial sums, partial p the fmaf chain over n = p, p + 256,
+// p + 512, ... (n < N) in ascending n; then a butterfly over each wave's 64
+// partials (lane-independent: every lane adds the same pairs) and the 4 wave
+// totals added in wave order.  Threads 0..255 (waves 0-3, fully active) form
+// the partials, their reads batched 8 at a time (all issued before the
+// first is used); every thread of the workgroup calls it and gets the total.
+// hrow(n) yields h[n]; red: 4 floats of LDS.
+template <class H>
+__device__ __forceinline__ float row_sumsq(const H &hrow, int N, int tid, float *red)
+{
+    if (tid < 256) {
+        float ss = 0.0f;
+        int n = tid;
+        for (; n + 7 * 256 < N; n += 8 * 256) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = hrow(n + j * 256);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
+        }
+        for (; n < N; n += 256) {
+            const float v = hrow(n);
+            ss = fmaf(v, v, ss);
+        }
+        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+        if ((tid & 63) == 0) red[tid >> 6] = ss;
+    }
+    __syncthreads();
+    const float tot = ((red[0] + red[1]) + red[2]) + red[3];
+    __syncthreads();                                      // red may be reused
+    return tot;
+}
+
 // ---- balanced kernel: one workgroup per compute unit ---------------------------
 //
 // A stream only reaches full rate when every compute unit moves about the
@@ -735,6 +777,9 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
 
 constexpr int kLdsSlotU4 = 128;            // u32x4 per wave and ring slot: one group pair of a 16-column tile
 constexpr int kLdsBurstBlocks = 4;         // BURST: blocks of 8 groups per unit, at most
+// Cache-policy bits of a buffer access: system coherence (sc0 | sc1): loads
+// miss every cache, stores write through to memory.
+constexpr int kSysCoherent = 17;
 
 // Waits until the loads of a ring slot have landed, given how many later
 // pairs (two loads each) this wave has requested since (0 .. 3).  Vector
@@ -771,14 +816,17 @@ __device__ __forceinline__ void group_fma(const u32x4 (&a)[4], const f32x4 &xsum
     }
 }
 
-template <int RD, bool PARTS, bool ACT, int RL, bool BURST>
+template <int RD, bool PARTS, bool ACT, int RL, bool BURST, bool NORM>
 __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ mn, int N,
-    float *__restrict__ out, uint16_t *__restrict__ act, int P, int nps, int nblm)
+    float *__restrict__ out, uint16_t *__restrict__ act, int P, int nps, int nblm, NormArgs na)
 {
     static_assert(RD == 2 || RD == 4, "ring depth: units are whole blocks of 4 pairs");
+    static_assert(!NORM || (PARTS && !ACT), "the norm epilogue follows the K-part reduce of the plain product");
     constexpr bool burst = BURST;
+    __shared__ float red[NORM ? 4 : 1];
+    __shared__ uint32_t last_wg;
     __shared__ __attribute__((aligned(16))) u32x4 ring0[kBalWaves * kLdsSlotU4];
     __shared__ __attribute__((aligned(16))) u32x4 ring1[kBalWaves * kLdsSlotU4];
     __shared__ __attribute__((aligned(16))) u32x4 ring2[RD > 2 ? kBalWaves * kLdsSlotU4 : 1];
@@ -1007,15 +1055,87 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
                     }
                 }
             } else if (i < cw) {
+                // NORM: out is h, and this workgroup's columns of h =
+                // residual + y are stored at once (write-through); the
+                // residual loads go out before any store.
+                float rv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = kRowPerm ? rowof(4 * h + r) : 4 * h + r;
-                    if (row < M)
-                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[r]), ry,
-                                                              (uint32_t)(row * N + cb + i) * 4, 0, 0);
+                    rv[r] = NORM && row < M ? na.r[(size_t)row * N + cb + i] : 0.0f;
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = kRowPerm ? rowof(4 * h + r) : 4 * h + r;
+                    if (row < M) {
+                        const float hv = NORM ? rv[r] + v[r] : v[r];
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, hv), ry,
+                                                              (uint32_t)(row * N + cb + i) * 4, 0,
+                                                              NORM ? kSysCoherent : 0);
+                    }
                 }
             }
         }
+    }
+    if (NORM) {
+        // RMSNorm of the whole rows, done by the workgroup that finishes last.
+        // Ordering: h was stored system-coherent (written through to memory,
+        // acknowledged only once there); each workgroup waits for its stores'
+        // acknowledgements before it counts itself in a system-scope atomic;
+        // the atomics are ordered at memory, so the workgroup that reads the
+        // count gx - 1 is the last and every h store is complete.  Its h loads
+        // are issued only after that count has come back (a branch on it) and
+        // bypass the caches (system-coherent), so they read the stored values.
+        // The counter is left at zero for the next call.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t old = __hip_atomic_fetch_add(na.cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            last_wg = old == (uint32_t)gx - 1 ? 1u : 0u;
+        }
+        __syncthreads();
+        if (!last_wg) return;
+        // Loads in batches of 8 per thread, all issued before the first is
+        // used (one memory round trip per batch, not per element).
+        constexpr int kB = 8;
+        float *hl = reinterpret_cast<float *>(xs);        // one row of h (x is no longer needed)
+        // gamma of the thread's first batch of columns, requested before h
+        // (indexes clamped into [0, N), so every load is issued unconditionally)
+        uint32_t g0[kB];
+#pragma unroll
+        for (int j = 0; j < kB; ++j) g0[j] = na.gamma[min(tid + j * kBalThreads, N - 1)];
+        for (int m = 0; m < M; ++m) {
+            const uint32_t row = (uint32_t)(m * N);
+            for (int n0 = tid; n0 < N; n0 += kB * kBalThreads) {
+                float t[kB];
+#pragma unroll
+                for (int j = 0; j < kB; ++j) {
+                    const int n = n0 + j * kBalThreads;
+                    t[j] = n < N ? __uint_as_float(
+                                       __builtin_amdgcn_raw_buffer_load_b32(ry, (row + n) * 4, 0, kSysCoherent))
+                                 : 0.0f;
+                }
+#pragma unroll
+                for (int j = 0; j < kB; ++j)
+                    if (n0 + j * kBalThreads < N) hl[n0 + j * kBalThreads] = t[j];
+            }
+            __syncthreads();
+            const float tot = row_sumsq([&](int n) { return hl[n]; }, N, tid, red);
+            const float inv = 1.0f / sqrtf(tot / (float)N + na.eps);
+            for (int n0 = tid; n0 < N; n0 += kB * kBalThreads) {
+                uint32_t g[kB];
+#pragma unroll
+                for (int j = 0; j < kB; ++j)
+                    g[j] = n0 == tid ? g0[j] : na.gamma[min(n0 + j * kBalThreads, N - 1)];
+#pragma unroll
+                for (int j = 0; j < kB; ++j) {
+                    const int n = n0 + j * kBalThreads;
+                    if (n < N) na.xo[row + n] = bf16_rne((hl[n] * inv) * __uint_as_float(g[j] << 16));
+                }
+            }
+            __syncthreads();                              // hl is reused by the next row
+        }
+        if (tid == 0) __hip_atomic_store(na.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 }
 
@@ -1085,22 +1205,15 @@ __global__ __launch_bounds__(256) void sum_swiglu(const float *__restrict__ P, i
 // Residual add + RMSNorm with the split-K partial sums added inside the norm
 // (Token Rush README, steps table rows 8-9).  One workgroup of 1024 threads
 // per row m: thread t takes n = t, t + 1024, ...; y = sum_s P[s] in ascending
-// s, h = r + y (written to h, which may be r itself), ss = sum of h*h (each
-// thread's terms in order by fmaf, then a butterfly within the wave, then the
-// 16 wave sums in order), inv = 1 / sqrt(ss / N + eps) (correctly rounded),
+// s, h = r + y (written to h, which may be r itself), ss = sum of h*h in the
+// order of row_sumsq, inv = 1 / sqrt(ss / N + eps) (correctly rounded),
 // x_out = bf16((h * inv) * gamma).  PT > 0: the thread's h values stay in
-// registers (N <= 1024 PT); PT == 0: they are read back from h.
+// registers (N <= 1024 PT) and the row is also put in LDS (N floats of
+// dynamic LDS) for the sum of squares; PT == 0: it is read back from h.
 #ifndef Q4G128_NORM_THREADS
 #define Q4G128_NORM_THREADS 1024
 #endif
 constexpr int kNormThreads = Q4G128_NORM_THREADS;
-
-__device__ __forceinline__ uint16_t bf16_rne(float a)
-{
-    const uint32_t b = __float_as_uint(a);
-    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
-    return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
-}
 
 template <int PT>
 __global__ __launch_bounds__(kNormThreads) void sum_residual_rmsnorm(const float *__restrict__ P, int S, int M,
@@ -1108,14 +1221,14 @@ __global__ __launch_bounds__(kNormThreads) void sum_residual_rmsnorm(const float
                                                                      const uint16_t *__restrict__ gamma, float eps,
                                                                      float *h, uint16_t *__restrict__ xo)
 {
-    __shared__ float wsum[kNormThreads / 64];
+    __shared__ float red[4];
+    extern __shared__ float hl[];
     const int m = blockIdx.x;
     const int tid = threadIdx.x;
     const size_t MN = (size_t)M * N;
     const size_t row = (size_t)m * N;
     constexpr int R = PT > 0 ? PT : 1;
     float hv[R];
-    float ss = 0.0f;
     const int passes = PT > 0 ? PT : (N + kNormThreads - 1) / kNormThreads;
     if (PT > 0) {
         // Every load first (r and h may be the same array, so a store to h
@@ -1135,9 +1248,11 @@ __global__ __launch_bounds__(kNormThreads) void sum_residual_rmsnorm(const float
         for (int j = 0; j < R; ++j) {
             const int n = tid + j * kNormThreads;
             const float v = rv[j] + hv[j];
-            if (n < N) h[row + n] = v;
+            if (n < N) {
+                h[row + n] = v;
+                hl[n] = v;
+            }
             hv[j] = v;
-            ss = fmaf(v, v, ss);
         }
     } else {
         // Wide rows: the same steps on chunks of 8 of the thread's elements
@@ -1158,15 +1273,16 @@ __global__ __launch_bounds__(kNormThreads) void sum_residual_rmsnorm(const float
             for (int j = 0; j < 8; ++j) {
                 const float v = rv[j] + t[j];
                 if (ok[j]) h[e[j]] = v;
-                ss = fmaf(ok[j] ? v : 0.0f, ok[j] ? v : 0.0f, ss);
             }
         }
     }
-    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-    if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+    // The row's h for the sum of squares in the shared order: from LDS, or
+    // (PT == 0) read back from h, just written by this workgroup (the
+    // barrier makes the writes visible).
     __syncthreads();
-    float tot = wsum[0];
-    for (int w = 1; w < kNormThreads / 64; ++w) tot += wsum[w];
+    const float *hr = h + row;
+    const float tot = PT > 0 ? row_sumsq([&](int n) { return hl[n]; }, N, tid, red)
+                             : row_sumsq([&](int n) { return hr[n]; }, N, tid, red);
     const float inv = 1.0f / sqrtf(tot / (float)N + eps);
     for (int j = 0; j < passes; ++j) {
         const int n = tid + j * kNormThreads;
@@ -1379,16 +1495,17 @@ LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd, bool burs
     return lp;
 }
 
-template <int RD, bool PARTS, bool ACT, int RL, bool BURST>
-static hipError_t launch_lds_v(const GemvArgs &a, int gx, int P, const LdsPlan &lp, hipStream_t stream)
+template <int RD, bool PARTS, bool ACT, int RL, bool BURST, bool NORM = false>
+static hipError_t launch_lds_v(const GemvArgs &a, int gx, int P, const LdsPlan &lp, const NormArgs &na,
+                               hipStream_t stream)
 {
     static LdsFlags done;
-    const void *k = reinterpret_cast<const void *>(&gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST>);
+    const void *k = reinterpret_cast<const void *>(&gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST, NORM>);
     const hipError_t attr = allow_dynamic_lds(k, (int)(kBalMaxLds - (lp.total - lp.lds)), done);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST>), dim3((unsigned)gx, 1, 1),
+    hipLaunchKernelGGL((gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST, NORM>), dim3((unsigned)gx, 1, 1),
                        dim3(kBalThreads, 1, 1), lp.lds, stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.act,
-                       P, lp.nps, lp.nblm);
+                       P, lp.nps, lp.nblm, na);
     return hipGetLastError();
 }
 
@@ -1397,10 +1514,25 @@ static hipError_t launch_lds_rl(const GemvArgs &a, int gx, int P, hipStream_t st
 {
     const LdsPlan lp = lds_plan(a.M, a.K, a.N, gx, P, ACT, RD, BURST);
     if (!lp.fits) return hipErrorInvalidValue;
-    if (a.M <= 4) return launch_lds_v<RD, PARTS, ACT, 1, BURST>(a, gx, P, lp, stream);
-    if (a.M <= 8) return launch_lds_v<RD, PARTS, ACT, 2, BURST>(a, gx, P, lp, stream);
-    if (a.M <= 12) return launch_lds_v<RD, PARTS, ACT, 3, BURST>(a, gx, P, lp, stream);
-    return launch_lds_v<RD, PARTS, ACT, 4, BURST>(a, gx, P, lp, stream);
+    const NormArgs na{};
+    if (a.M <= 4) return launch_lds_v<RD, PARTS, ACT, 1, BURST>(a, gx, P, lp, na, stream);
+    if (a.M <= 8) return launch_lds_v<RD, PARTS, ACT, 2, BURST>(a, gx, P, lp, na, stream);
+    if (a.M <= 12) return launch_lds_v<RD, PARTS, ACT, 3, BURST>(a, gx, P, lp, na, stream);
+    return launch_lds_v<RD, PARTS, ACT, 4, BURST>(a, gx, P, lp, na, stream);
+}
+
+bool lds_norm_fits(int M, int K, int N, int gx, int P)
+{
+    const LdsPlan lp = lds_plan(M, K, N, gx, P, false, 2, true);
+    return P > 1 && M <= 8 && lp.fits && lp.lds >= (size_t)N * 4;
+}
+
+hipError_t launch_gemv_lds_norm(const GemvArgs &a, int gx, int P, const NormArgs &na, hipStream_t stream)
+{
+    if (a.S != 1 || a.act || !lds_norm_fits(a.M, a.K, a.N, gx, P)) return hipErrorInvalidValue;
+    const LdsPlan lp = lds_plan(a.M, a.K, a.N, gx, P, false, 2, true);
+    if (a.M <= 4) return launch_lds_v<2, true, false, 1, true, true>(a, gx, P, lp, na, stream);
+    return launch_lds_v<2, true, false, 2, true, true>(a, gx, P, lp, na, stream);
 }
 
 // Variants built: ring 2 without burst (any shape, the fused SwiGLU too), and
@@ -1454,13 +1586,14 @@ hipError_t launch_sum_residual_rmsnorm(const float *P, int S, int M, int N, cons
 {
     const dim3 grid((unsigned)M, 1, 1), block(kNormThreads, 1, 1);
     const int pt = (N + kNormThreads - 1) / kNormThreads;
+    const size_t lds = (size_t)N * sizeof(float);           // PT > 0 only: at most 64 KB
     if (pt <= 2)
-        hipLaunchKernelGGL(sum_residual_rmsnorm<2>, grid, block, 0, stream, P, S, M, N, r, gamma, eps, h, xo);
+        hipLaunchKernelGGL(sum_residual_rmsnorm<2>, grid, block, lds, stream, P, S, M, N, r, gamma, eps, h, xo);
     else if (pt <= 8)
-        hipLaunchKernelGGL(sum_residual_rmsnorm<8>, grid, block, 0, stream, P, S, M, N, r, gamma, eps, h, xo);
+        hipLaunchKernelGGL(sum_residual_rmsnorm<8>, grid, block, lds, stream, P, S, M, N, r, gamma, eps, h, xo);
     else if (pt <= 16 && kNormPt16)
-        hipLaunchKernelGGL(sum_residual_rmsnorm<kNormPt16 ? 16 : 8>, grid, block, 0, stream, P, S, M, N, r, gamma, eps, h,
-                           xo);
+        hipLaunchKernelGGL(sum_residual_rmsnorm<kNormPt16 ? 16 : 8>, grid, block, lds, stream, P, S, M, N, r, gamma,
+                           eps, h, xo);
     else
         hipLaunchKernelGGL(sum_residual_rmsnorm<0>, grid, block, 0, stream, P, S, M, N, r, gamma, eps, h, xo);
     return hipGetLastError();

@@ -158,6 +158,23 @@ struct LdsPlan {
 LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd, bool burst);
 hipError_t launch_gemv_lds(const GemvArgs &a, int gx, int P, int rd, bool burst, hipStream_t stream);
 
+// Residual add + RMSNorm inside the K-part launch (ring 2, burst): every
+// workgroup stores its columns of h = r + y to a.out (h; may be r itself),
+// and the workgroup that finishes last computes x_out = bf16(h / sqrt(mean(h^2)
+// + eps) * gamma) for whole rows.  cnt: a word of the caller's workspace that
+// holds zero, counted up by every workgroup and left at zero again.
+// lds_norm_fits: the shape takes it (K parts, M <= 8, one row of h fitting
+// the dynamic LDS).
+struct NormArgs {
+    const float *r;
+    const uint16_t *gamma;
+    float eps;
+    uint16_t *xo;
+    uint32_t *cnt;
+};
+bool lds_norm_fits(int M, int K, int N, int gx, int P);
+hipError_t launch_gemv_lds_norm(const GemvArgs &a, int gx, int P, const NormArgs &na, hipStream_t stream);
+
 // ---- work-balanced (stream-K) kernel ----------------------------------------
 constexpr int kSkWaves = 8;                 // waves per workgroup, one workgroup per CU
 constexpr int kSkThreads = 64 * kSkWaves;

@@ -172,7 +172,11 @@ def test_epilogue_rejects(L):
     assert f(*ok, 64, FAKE, FAKE, need - 4, None) == q.Q4G128_EWORKSPACE
     g = L.q4g128_gemm_rmsnorm
     base = [FAKE, 1, 1024, FAKE, FAKE, FAKE, 64]
-    wsb = q.q4g128_splitk_workspace_bytes(1, 64, 1)
+    wsb = q.q4g128_rmsnorm_workspace_bytes(1, 64, 1)
+    assert wsb == 256 + 64 * 4                                          # control block + partials
+    assert q.q4g128_rmsnorm_workspace_bytes(2, 64, 3) == 256 + 3 * 2 * 64 * 4
+    assert q.q4g128_rmsnorm_workspace_bytes(0, 64, 1) == 0
+    assert g(*base, FAKE, FAKE, 1e-6, FAKE, FAKE, 1, FAKE, wsb - 256, None) == q.Q4G128_EWORKSPACE
     assert g(*base, None, FAKE, 1e-6, FAKE, FAKE, 1, FAKE, wsb, None) == q.Q4G128_EINVAL    # no residual
     assert g(*base, FAKE, None, 1e-6, FAKE, FAKE, 1, FAKE, wsb, None) == q.Q4G128_EINVAL    # no gamma
     assert g(*base, FAKE, FAKE, -1.0, FAKE, FAKE, 1, FAKE, wsb, None) == q.Q4G128_EINVAL    # eps < 0

@@ -13,11 +13,15 @@ Residual add + RMSNorm with split-K partials summed in the norm
   * h equals fp32(residual + y) bit for bit, y the split-K product with the
     same splits (q4g128_gemm_splitk);
   * x_out within a tolerance derived from h's bound (product bound plus one
-    fp32 rounding), the fp32 sum of squares (at most ceil(N/1024) + 22
-    sequential roundings) and the correctly rounded sqrt and divide, plus
+    fp32 rounding), the fp32 sum of squares (at most ceil(N/256) + 9
+    sequential roundings: a chain over ceil(N/256) columns, 6 butterfly adds,
+    3 adds of wave totals) and the correctly rounded sqrt and divide, plus
     2^-8 relative for the fp32 products and the bf16 rounding;
   * in place (h = residual) gives the same results; rows bit-identical
-    across M; repeated calls identical.
+    across M; repeated calls identical;
+  * the one-launch form (splits = the K parts, the last workgroup
+    normalising) gives the bits of the two-launch form, and leaves the
+    workspace's control block zero, call after call.
 """
 import numpy as np
 import pytest
@@ -127,7 +131,7 @@ def rms_tolerance(y_ref, a_ref, r, gamma_bits, eps, out_ref):
     h = r.astype(np.float64) + y_ref
     th = tau + 2.0 ** -24 * (np.abs(h) + tau)
     ss = np.sum(h * h, axis=1, keepdims=True)
-    L = -(-N // 1024) + 22
+    L = -(-N // 256) + 9
     dss = np.sum(2 * np.abs(h) * th + th * th, axis=1, keepdims=True) + (L + 3) * 2.0 ** -24 * ss
     inv = 1.0 / np.sqrt(ss / N + eps)
     d = 1.01 * 0.5 * dss / (ss + N * eps) + 4 * 2.0 ** -24
@@ -197,3 +201,68 @@ def test_rmsnorm_rows_identical_across_M(K, N, seed):
         h, xo = q.q4g128_gemm_rmsnorm(x8[:M].contiguous(), W, s, m, torch.from_numpy(r[:M].copy()).to(DEV), gt)
         assert np.array_equal(host_f32(h).view(np.uint32), hf[:M].view(np.uint32)), M
         assert np.array_equal(host_bf16(xo), xf[:M]), M
+
+
+def rms_two_launch(x, W, s, m, r, g, S):
+    """The two-launch form on the same operands: scale/min copied to
+    addresses that are not 16-byte aligned, which the one-launch kernel does
+    not take (same values, so the same split-K partials)."""
+    return q.q4g128_gemm_rmsnorm(x, W, misaligned(s), misaligned(m), r, g, 1e-6, splits=S)
+
+
+@pytest.mark.parametrize("name,M,K,N,seed", [("down", None, None, None, None), (None, 1, 6144, 5120, 103),
+                                             (None, 4, 6144, 5120, 104), (None, 8, 6144, 5120, 105)])
+def test_rmsnorm_one_launch_equals_two_launch(name, M, K, N, seed):
+    case = rms_case(name, M, K, N, seed)
+    P = q.q4g128_gemm_parts(case.K, case.N)
+    assert P > 1, "a shape the one-launch form serves"
+    r, gamma = rms_inputs(case, 9)
+    x = dev_x(case.x)
+    W, s, m = dev_weights(case.weights)
+    rt = torch.from_numpy(r).to(DEV)
+    gt = torch.from_numpy(gamma.view(np.int16)).to(DEV)
+    ws = q.q4g128_rmsnorm_workspace(case.M, case.N, P, DEV)
+    ws[64:].fill_(-7.0)                         # the partials area: untouched by the one-launch form
+    h1, x1 = q.q4g128_gemm_rmsnorm(x, W, s, m, rt, gt, 1e-6, splits=P, workspace=ws)
+    h1, x1 = host_f32(h1), host_bf16(x1)
+    one_launch = bool((ws[64:] == -7.0).all().item())
+    if case.M == 1:
+        assert one_launch, "M = 1 on a K-part shape runs as one launch"
+    print(f"rmsnorm {case.name} M={case.M} P={P}: {'one launch' if one_launch else 'two launches'}")
+    h2, x2 = rms_two_launch(x, W, s, m, rt, gt, P)
+    assert np.array_equal(h1.view(np.uint32), host_f32(h2).view(np.uint32))
+    assert np.array_equal(x1, host_bf16(x2))
+    # the counter in the control block is back at zero, and a reused
+    # workspace gives the same bits (also in place, h = residual)
+    assert not ws[:64].view(torch.int32).any().item()
+    for _ in range(3):
+        res = torch.from_numpy(r.copy()).to(DEV)
+        h3, x3 = q.q4g128_gemm_rmsnorm(x, W, s, m, res, gt, 1e-6, splits=P, h=res, workspace=ws)
+        assert np.array_equal(host_f32(h3).view(np.uint32), h1.view(np.uint32))
+        assert np.array_equal(host_bf16(x3), x1)
+    assert not ws[:64].view(torch.int32).any().item()
+
+
+def test_rmsnorm_one_launch_shared_workspace_across_shapes():
+    """One workspace serving the one-launch form and the two-launch form in
+    turn (down projection at M = 1, then at M = 2, which its LDS does not
+    hold): the two-launch form leaves the control block alone."""
+    case = synth.make_random(2, 17408, 5120, 106)
+    P = q.q4g128_gemm_parts(case.K, case.N)
+    r, gamma = rms_inputs(case, 10)
+    x = dev_x(case.x)
+    W, s, m = dev_weights(case.weights)
+    rt = torch.from_numpy(r).to(DEV)
+    gt = torch.from_numpy(gamma.view(np.int16)).to(DEV)
+    ws = q.q4g128_rmsnorm_workspace(2, case.N, P, DEV)
+    ref = []
+    for M in (1, 2, 1, 2):
+        ws[64:].fill_(-7.0)
+        h, xo = q.q4g128_gemm_rmsnorm(x[:M].contiguous(), W, s, m, rt[:M].contiguous(), gt, 1e-6, splits=P,
+                                      workspace=ws)
+        ref.append((host_f32(h).view(np.uint32), host_bf16(xo)))
+        assert not ws[:64].view(torch.int32).any().item(), M
+        assert bool((ws[64:] == -7.0).all().item()) == (M == 1), M      # M = 2: partials written
+    assert np.array_equal(ref[0][0], ref[2][0]) and np.array_equal(ref[0][1], ref[2][1])
+    assert np.array_equal(ref[1][0], ref[3][0]) and np.array_equal(ref[1][1], ref[3][1])
+    assert np.array_equal(ref[1][0][:1], ref[0][0]) and np.array_equal(ref[1][1][:1], ref[0][1])

@@ -70,7 +70,7 @@ def test_graph_replay_of_fused_epilogues_equals_eager():
     S = q.q4g128_splitk_default_splits(dn.K, dn.N)
     h = r0.clone()
     xo = torch.empty((dn.M, dn.N), dtype=torch.bfloat16, device=DEV)
-    wsd = torch.empty(max(4, q.q4g128_splitk_workspace_bytes(dn.M, dn.N, S)) // 4, dtype=torch.float32, device=DEV)
+    wsd = q.q4g128_rmsnorm_workspace(dn.M, dn.N, S, DEV)
 
     def run_all(stream=None):
         for _, x, W, s, m, act, ws in ops:
