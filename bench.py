@@ -376,25 +376,78 @@ def measure_epilogues(torch, q, steps, warmup):
     Bo = B + 4 * dn.M * dn.N + 2 * dn.N + 2 * dn.M * dn.N       # + residual in, gamma, bf16 x_out
     out["down_rmsnorm_M1"] = {"us_per_call": round(t * 1e6, 3), "GBps": round(Bo / t / 1e9, 1),
                               "bytes_per_call": Bo, "splits": S, "launches_per_call": 1 if one_launch else 2}
+    # The residual add alone (x_out NULL): the norm is left to the next product.
+    calls = [lambda st, a=(x.data_ptr(), dn.M, dn.K, W.data_ptr(), sc.data_ptr(), mn.data_ptr(), dn.N, r.data_ptr(),
+                           None, 1e-6, h.data_ptr(), None, S, ws.data_ptr(), wsb):
+             L.q4g128_gemm_rmsnorm(*a, st) for W, sc, mn in sets]
+    t = timed_calls(torch, calls, reps, 1) * 1e-3 / (reps * len(calls))
+    Bo = B + 4 * dn.M * dn.N                                    # + residual in
+    out["down_residual_M1"] = {"us_per_call": round(t * 1e6, 3), "GBps": round(Bo / t / 1e9, 1),
+                               "bytes_per_call": Bo, "splits": S, "launches_per_call": 1 if one_launch else 2}
     del sets
     torch.cuda.empty_cache()
+    # The norm inside the consuming product: q/k/v and gate/up + SwiGLU made
+    # from fp32 h, against the same products on a ready bf16 x.
+    hrow = torch.from_numpy((rng.standard_normal((1, 5120)) * 0.5).astype(np.float32)).to(dev)
+    g5 = torch.from_numpy(synth.to_bf16_bits(1.0 + 0.1 * rng.standard_normal(5120)).view(np.int16)).to(dev)
+    x5 = torch.from_numpy(synth.to_bf16_bits(rng.standard_normal((1, 5120))).view(np.int16)).to(dev)
+    for name, (K, N), sw in (("qkv", (5120, 12288), False), ("gateup_swiglu", (5120, 34816), True)):
+        case = synth.make_random(1, K, N, 70 + N % 13)
+        B = synth.algorithmic_bytes(1, K, N)
+        sets = dev_copies(torch, case, max(2, math.ceil(ROTATE_BYTES / B)))
+        o = torch.empty((1, N // 2), dtype=torch.int16, device=dev) if sw else \
+            torch.empty((1, N), dtype=torch.float32, device=dev)
+        wpb = q.q4g128_prenorm_workspace_bytes(1, K, N, sw)
+        wsp = torch.empty(max(wpb, q.q4g128_swiglu_workspace_bytes(1, K, N) if sw else 0, 256) // 4,
+                          dtype=torch.float32, device=dev)
+        wpb = wsp.numel() * 4
+        if sw:
+            plain = [lambda st, a=(x5.data_ptr(), 1, K, W.data_ptr(), sc.data_ptr(), mn.data_ptr(), N, o.data_ptr(),
+                                   wsp.data_ptr(), wpb): L.q4g128_gemm_swiglu(*a, st) for W, sc, mn in sets]
+            pre = [lambda st, a=(hrow.data_ptr(), g5.data_ptr(), 1e-6, 1, K, W.data_ptr(), sc.data_ptr(),
+                                 mn.data_ptr(), N, o.data_ptr(), wsp.data_ptr(), wpb):
+                   L.q4g128_gemm_swiglu_prenorm(*a, st) for W, sc, mn in sets]
+        else:
+            plain = [lambda st, a=(x5.data_ptr(), 1, K, W.data_ptr(), sc.data_ptr(), mn.data_ptr(), N, o.data_ptr()):
+                     L.q4g128_gemm(*a, st) for W, sc, mn in sets]
+            pre = [lambda st, a=(hrow.data_ptr(), g5.data_ptr(), 1e-6, 1, K, W.data_ptr(), sc.data_ptr(),
+                                 mn.data_ptr(), N, o.data_ptr(), wsp.data_ptr(), wpb):
+                   L.q4g128_gemm_prenorm(*a, st) for W, sc, mn in sets]
+        reps = max(1, steps // len(plain))
+        res = {}
+        for _ in range(2):                                      # interleaved, best of two
+            for key, calls in (("plain", plain), ("prenorm", pre)):
+                t = timed_calls(torch, calls, reps, 1) * 1e-3 / (reps * len(calls))
+                res[key] = min(res.get(key, t), t)
+        out[name + "_prenorm_M1"] = {"us_per_call": round(res["prenorm"] * 1e6, 3),
+                                     "us_per_call_on_ready_x": round(res["plain"] * 1e6, 3),
+                                     "extra_us": round((res["prenorm"] - res["plain"]) * 1e6, 3),
+                                     "launches_per_call": 1}
+        del sets, plain, pre
+        torch.cuda.empty_cache()
     return out
 
 
-def measure_chain(torch, q, reps=5):
+def measure_chain(torch, q, reps=5, prenorm=True):
     """A decode step whose products feed each other as in a transformer layer
-    (attention itself out of scope): per layer, with h the fp32 residual
-    stream and x the bf16 normalised input,
-        qkv   = x . W_qkv                       (5120 -> 12288)
-        h    += a . W_o;  x' = RMSNorm(h)       (6144 -> 5120, a a fixed stand-in
-                                                 for the attention output)
-        act   = silu(gate) * up of x' . W_gu    (5120 -> 2 x 17408)
-        h    += act . W_down;  x = RMSNorm(h)   (17408 -> 5120, split-K partials
-                                                 summed in the norm)
+    (attention itself out of scope), with h the fp32 residual stream.
+    prenorm (each norm made inside the product that consumes it):
+        qkv   = RMSNorm(h) . W_qkv                 (5120 -> 12288)
+        h    += a . W_o                             (6144 -> 5120, a a fixed
+                                                     stand-in for the attention output)
+        act   = silu(gate) * up of RMSNorm(h) . W_gu   (5120 -> 2 x 17408)
+        h    += act . W_down                        (17408 -> 5120)
+      then logits = RMSNorm(h) . W_head.
+    postnorm (the norm after the product, split-K partials summed in it):
+        qkv   = x . W_qkv
+        h    += a . W_o;  x' = RMSNorm(h)
+        act   = silu(gate) * up of x' . W_gu
+        h    += act . W_down;  x = RMSNorm(h)
+      then logits = x . W_head.
     64 layers, every layer on its own weight copies, then the 5120 -> 131072
-    output projection: 385 launches.  Timed eager and as one replayed HIP
-    graph; each replay starts from the same residual and must reproduce the
-    eager outputs bit for bit."""
+    output projection.  Timed eager and as one replayed HIP graph; each replay
+    starts from the same residual and must reproduce the eager outputs bit for
+    bit."""
     L = q.lib()
     dev = torch.device("cuda:0")
     shapes = synth.stream_shapes()
@@ -415,19 +468,33 @@ def measure_chain(torch, q, reps=5):
     logits = torch.empty((1, 131072), dtype=torch.float32, device=dev)
     g_o = torch.from_numpy(synth.to_bf16_bits(1.0 + 0.1 * rng.standard_normal(d)).view(np.int16)).to(dev)
     g_d = torch.from_numpy(synth.to_bf16_bits(1.0 + 0.1 * rng.standard_normal(d)).view(np.int16)).to(dev)
+    g_h = torch.from_numpy(synth.to_bf16_bits(1.0 + 0.1 * rng.standard_normal(d)).view(np.int16)).to(dev)
     S_o = q.q4g128_splitk_default_splits(6144, d)
     S_d = q.q4g128_splitk_default_splits(17408, d)
     wsn = q.q4g128_rmsnorm_workspace(1, d, max(S_o, S_d), dev)       # control block zero: the norms' own
     wsnb = wsn.numel() * 4
     wsb = max(q.q4g128_splitk_workspace_bytes(1, d, S_o), q.q4g128_splitk_workspace_bytes(1, d, S_d),
-              q.q4g128_swiglu_workspace_bytes(1, 5120, 34816))
+              q.q4g128_swiglu_workspace_bytes(1, 5120, 34816),
+              q.q4g128_prenorm_workspace_bytes(1, 5120, 12288), q.q4g128_prenorm_workspace_bytes(1, 5120, 34816, True),
+              q.q4g128_prenorm_workspace_bytes(1, 5120, 131072))
     ws = torch.empty(wsb // 4, dtype=torch.float32, device=dev)
+    hp, gp = h.data_ptr(), None
     seq = []
     for l in range(layers):
         Wq, sq, mq = w[0][l]
         Wo, so, mo = w[1][l]
         Wg, sg, mg = w[2][l]
         Wd, sd, md = w[3][l]
+        if prenorm:
+            seq.append(lambda st, A=(hp, g_d.data_ptr(), 1e-6, 1, 5120, Wq.data_ptr(), sq.data_ptr(), mq.data_ptr(),
+                                     12288, qkv.data_ptr(), ws.data_ptr(), wsb): L.q4g128_gemm_prenorm(*A, st))
+            seq.append(lambda st, A=(a.data_ptr(), 1, 6144, Wo.data_ptr(), so.data_ptr(), mo.data_ptr(), d, hp, gp,
+                                     1e-6, hp, None, S_o, wsn.data_ptr(), wsnb): L.q4g128_gemm_rmsnorm(*A, st))
+            seq.append(lambda st, A=(hp, g_o.data_ptr(), 1e-6, 1, 5120, Wg.data_ptr(), sg.data_ptr(), mg.data_ptr(),
+                                     34816, act.data_ptr(), ws.data_ptr(), wsb): L.q4g128_gemm_swiglu_prenorm(*A, st))
+            seq.append(lambda st, A=(act.data_ptr(), 1, 17408, Wd.data_ptr(), sd.data_ptr(), md.data_ptr(), d, hp,
+                                     gp, 1e-6, hp, None, S_d, wsn.data_ptr(), wsnb): L.q4g128_gemm_rmsnorm(*A, st))
+            continue
         seq.append(lambda st, A=(x.data_ptr(), 1, 5120, Wq.data_ptr(), sq.data_ptr(), mq.data_ptr(), 12288,
                                  qkv.data_ptr()): L.q4g128_gemm(*A, st))
         seq.append(lambda st, A=(a.data_ptr(), 1, 6144, Wo.data_ptr(), so.data_ptr(), mo.data_ptr(), d, h.data_ptr(),
@@ -439,8 +506,12 @@ def measure_chain(torch, q, reps=5):
                                  h.data_ptr(), g_d.data_ptr(), 1e-6, h.data_ptr(), x.data_ptr(), S_d, wsn.data_ptr(),
                                  wsnb): L.q4g128_gemm_rmsnorm(*A, st))
     Wh, sh, mh = head
-    seq.append(lambda st, A=(x.data_ptr(), 1, 5120, Wh.data_ptr(), sh.data_ptr(), mh.data_ptr(), 131072,
-                             logits.data_ptr()): L.q4g128_gemm(*A, st))
+    if prenorm:
+        seq.append(lambda st, A=(hp, g_h.data_ptr(), 1e-6, 1, 5120, Wh.data_ptr(), sh.data_ptr(), mh.data_ptr(),
+                                 131072, logits.data_ptr(), ws.data_ptr(), wsb): L.q4g128_gemm_prenorm(*A, st))
+    else:
+        seq.append(lambda st, A=(x.data_ptr(), 1, 5120, Wh.data_ptr(), sh.data_ptr(), mh.data_ptr(), 131072,
+                                 logits.data_ptr()): L.q4g128_gemm(*A, st))
     B = layers * sum(synth.algorithmic_bytes(1, K, N) for K, N, _ in shapes[:4]) + \
         synth.algorithmic_bytes(1, *shapes[4][:2])
     stream = torch.cuda.current_stream()
@@ -489,12 +560,17 @@ def measure_chain(torch, q, reps=5):
         ms += t0.elapsed_time(t1)
         same = same and torch.equal(logits, ref[0]) and torch.equal(h, ref[1])
     t_graph = ms * 1e-3 / reps
-    out = {"launches_per_step": len(seq) + 2 * layers, "bytes_per_step": B,
+    # Kernels per call: the fused forms are one launch on these shapes at
+    # M = 1 (splits = the one-launch form's K parts; the prenorm staging).
+    one = S_o == q.q4g128_gemm_parts(6144, d) > 1 and S_d == q.q4g128_gemm_parts(17408, d) > 1
+    out = {"calls_per_step": len(seq), "launches_per_step": len(seq) + (0 if one else 2 * layers),
+           "norm": "prenorm (in the consuming product)" if prenorm else "postnorm (after the product)",
+           "bytes_per_step": B,
            "ms_per_step": round(t_eager * 1e3, 4), "GBps_wall": round(B / t_eager / 1e9, 1),
            "graph": {"ms_per_step": round(t_graph * 1e3, 4), "GBps_wall": round(B / t_graph / 1e9, 1),
                      "replay_equals_eager": bool(same)},
            "outputs_finite": finite,
-           "note": "products chained through the fused epilogues; weight bytes as the plain stream"}
+           "note": "products chained through the fused norms; weight bytes as the plain stream"}
     del w, head, g
     torch.cuda.empty_cache()
     return out
@@ -1001,6 +1077,7 @@ def main():
     stream_step = measure_stream(torch, q) if not args.no_stream else None
     epilogues = None if args.no_epilogues else measure_epilogues(torch, q, args.steps, args.warmup)
     chain = measure_chain(torch, q) if not (args.no_stream or args.no_epilogues) else None
+    chain_post = measure_chain(torch, q, prenorm=False) if chain is not None else None
     quant, quant_out = (None, None) if args.no_quantize else measure_quantize(torch, q)
     env = env_info(torch)            # after every GPU leg: rocm-smi leaves the GPU idle for a second or two
 
@@ -1043,6 +1120,7 @@ def main():
         "decode_step_stream": stream_step,
         "epilogues": epilogues,
         "decode_step_chain": chain,
+        "decode_step_chain_postnorm": chain_post,
         "quantize": quant,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),

@@ -218,9 +218,11 @@ size_t q4g128_rmsnorm_workspace_bytes(int M, int N, int splits);
  * (n < N) in ascending n; then a fixed tree over the 256.  The square root and division are correctly rounded.
  * residual and h fp32 [M][N] (h may be the residual itself, updated in
  * place; 4-byte aligned); gamma bf16 [N]; x_out bf16 [M][N] (the next
- * product's input; 2-byte aligned); eps >= 0.  The RMSNorm formula is the
- * usual one of the model family the pages run; the pages do not spell it
- * out.  Rows are bit-identical across M; results deterministic.
+ * product's input; 2-byte aligned); eps >= 0.  x_out == NULL: the residual
+ * add alone (h only; gamma and eps are not read), for a caller that lets the
+ * next product normalise h itself (q4g128_gemm_prenorm).  The RMSNorm
+ * formula is the usual one of the model family the pages run; the pages do
+ * not spell it out.  Rows are bit-identical across M; results deterministic.
  *
  * When `splits` equals q4g128_gemm_parts(K, N) > 1 and the M rows fit that
  * launch's LDS (M <= 8; x for all of K is held there, so 17408 -> 5120 takes
@@ -228,7 +230,9 @@ size_t q4g128_rmsnorm_workspace_bytes(int M, int N, int splits);
  * residual to its own columns, and the workgroup that finishes last (found
  * by a counter) normalises the rows.  Otherwise the partials go to the
  * workspace and a second launch sums them and normalises.  Both give the
- * same bits.
+ * same bits.  (The last workgroup's pass over the rows costs about 3 us on
+ * 17408 -> 5120; moving the norm into the next product, q4g128_gemm_prenorm
+ * with x_out == NULL here, costs about 0.1 us here.)
  *
  * Workspace: at least q4g128_rmsnorm_workspace_bytes(M, N, splits) bytes,
  * 4-byte aligned.  Its first 256 bytes are a control block that must hold
@@ -241,6 +245,44 @@ q4g128_status q4g128_gemm_rmsnorm(const void *x, int M, int K,
                                   int N, const float *residual, const void *gamma, float eps,
                                   float *h, void *x_out, int splits,
                                   float *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace q4g128_gemm_prenorm (swiglu == 0) or
+ * q4g128_gemm_swiglu_prenorm (swiglu != 0) needs: M*K*2 rounded up to 256
+ * (x, when it is made in a launch of its own), plus for swiglu
+ * q4g128_swiglu_workspace_bytes(M, K, N).  Returns 0 for invalid arguments. */
+size_t q4g128_prenorm_workspace_bytes(int M, int K, int N, int swiglu);
+
+/* The product of a normalised input: with fp32 rows h [M][K],
+ *
+ *     x[m][k] = bf16( h[m][k] * inv[m] * gamma[k] ),
+ *     inv[m]  = 1 / sqrt( (sum over k of h[m][k]^2) / K + eps ),
+ *     y       = x . dequant(W)                          (as q4g128_gemm)
+ *
+ * x is bit for bit the x_out q4g128_gemm_rmsnorm gives for rows h (same sum
+ * of squares order), and y bit for bit q4g128_gemm on that x.  This is the
+ * decoder's pre-norm: the residual stream h (q4g128_gemm_rmsnorm with
+ * x_out == NULL keeps it) is normalised inside the product that consumes it
+ * (the q/k/v projection, the gate/up projection, the output head) instead of
+ * in a launch of its own (Token Rush README, steps table: norm, then the
+ * projections).  One launch when the shape's one-launch plan takes it (M <=
+ * 8; h and gamma 16-byte aligned, scale and min too): every workgroup reads
+ * the whole rows of h and gamma while it stages x.  Otherwise x goes to the
+ * workspace first.  h fp32 [M][K] (4-byte aligned), gamma bf16 [K] (2-byte
+ * aligned), eps >= 0, y fp32 [M][N]; workspace: at least
+ * q4g128_prenorm_workspace_bytes(M, K, N, 0) bytes, 256-byte aligned, not
+ * shared by calls in flight.  Other requirements as q4g128_gemm. */
+q4g128_status q4g128_gemm_prenorm(const float *h, const void *gamma, float eps, int M, int K,
+                                  const uint32_t *W, const void *scale, const void *min,
+                                  int N, float *y, float *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+/* q4g128_gemm_swiglu on x = the normalised h above: act [M][N/2] =
+ * bf16(silu(gate) * up), bit for bit q4g128_gemm_swiglu on that x.
+ * Workspace: q4g128_prenorm_workspace_bytes(M, K, N, 1). */
+q4g128_status q4g128_gemm_swiglu_prenorm(const float *h, const void *gamma, float eps, int M, int K,
+                                         const uint32_t *W, const void *scale, const void *min,
+                                         int N, void *act, float *workspace, size_t workspace_bytes,
+                                         void *stream);
 
 /* Decoded weights w_out[n][k] = fp32(q*s + m), rounded once (fma), laid out
  * fp32 [N][K].  Uses the same device unpacking as the product; it exists so

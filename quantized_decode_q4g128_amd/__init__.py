@@ -70,6 +70,12 @@ def lib() -> ctypes.CDLL:
         L.q4g128_splitk_workspace_bytes.restype = sz
         L.q4g128_rmsnorm_workspace_bytes.argtypes = [ci, ci, ci]
         L.q4g128_rmsnorm_workspace_bytes.restype = sz
+        L.q4g128_prenorm_workspace_bytes.argtypes = [ci, ci, ci, ci]
+        L.q4g128_prenorm_workspace_bytes.restype = sz
+        L.q4g128_gemm_prenorm.argtypes = [vp, vp, ctypes.c_float, ci, ci, vp, vp, vp, ci, vp, vp, sz, vp]
+        L.q4g128_gemm_prenorm.restype = ci
+        L.q4g128_gemm_swiglu_prenorm.argtypes = [vp, vp, ctypes.c_float, ci, ci, vp, vp, vp, ci, vp, vp, sz, vp]
+        L.q4g128_gemm_swiglu_prenorm.restype = ci
         L.q4g128_gemm_parts.argtypes = [ci, ci]
         L.q4g128_gemm_parts.restype = ci
         L.q4g128_splitk_default_splits.argtypes = [ci, ci]
@@ -314,33 +320,98 @@ def q4g128_gemm_swiglu(x, W, scale, min, act=None, workspace=None, stream=None) 
 
 
 def q4g128_gemm_rmsnorm(x, W, scale, min, residual, gamma, eps: float = 1e-6, splits=None, h=None, x_out=None,
-                        workspace=None, stream=None):
+                        workspace=None, stream=None, norm: bool = True):
     """(h, x_out): h = residual + x . dequant(W) (fp32 [M][N]; pass h=residual
     to update it in place), x_out = bf16(h / sqrt(mean(h^2) + eps) * gamma),
     the split-K partials (default split count) summed inside the norm.
+    norm=False: the residual add alone, returns (h, None) (gamma unused: the
+    next product normalises h itself, q4g128_gemm_prenorm).
     A given `workspace` must come from q4g128_rmsnorm_workspace (its first
     256 bytes zero; every call leaves them so) and must not be written by
     other calls in between."""
     x, W, scale, min, M, K, N = _operands(x, W, scale, min)
     residual = _dev(residual, "residual", (torch.float32,))
-    gamma = _dev(gamma, "gamma", _HALF, ndim=1)
-    if tuple(residual.shape) != (M, N) or tuple(gamma.shape) != (N,):
-        raise ValueError(f"residual must be [M][N] = {(M, N)} and gamma [N]")
-    if residual.device != x.device or gamma.device != x.device:
-        raise ValueError("all operands must be on the same device")
+    if tuple(residual.shape) != (M, N) or residual.device != x.device:
+        raise ValueError(f"residual must be [M][N] = {(M, N)} on the operands' device")
+    if norm:
+        gamma = _dev(gamma, "gamma", _HALF, ndim=1)
+        if tuple(gamma.shape) != (N,) or gamma.device != x.device:
+            raise ValueError(f"gamma must be [N] = ({N},) on the operands' device")
     h = _out(h, M, N, x.device)
-    x_out = _half_out(x_out, "x_out", (M, N), x.device)
+    x_out = _half_out(x_out, "x_out", (M, N), x.device) if norm else None
     if splits is None:
         splits = q4g128_splitk_default_splits(K, N)
     if workspace is None and splits >= 1:
         workspace = q4g128_rmsnorm_workspace(M, N, splits, x.device)
     workspace = _workspace(workspace, 0, x.device)
     st = lib().q4g128_gemm_rmsnorm(x.data_ptr(), M, K, W.data_ptr(), scale.data_ptr(), min.data_ptr(), N,
-                                   residual.data_ptr(), gamma.data_ptr(), float(eps), h.data_ptr(), x_out.data_ptr(),
-                                   int(splits), workspace.data_ptr(), workspace.numel() * 4,
-                                   _stream(stream, x.device))
+                                   residual.data_ptr(), gamma.data_ptr() if norm else None, float(eps), h.data_ptr(),
+                                   x_out.data_ptr() if norm else None, int(splits), workspace.data_ptr(),
+                                   workspace.numel() * 4, _stream(stream, x.device))
     _check(st, "q4g128_gemm_rmsnorm")
     return h, x_out
+
+
+def q4g128_prenorm_workspace_bytes(M: int, K: int, N: int, swiglu: bool = False) -> int:
+    return int(lib().q4g128_prenorm_workspace_bytes(int(M), int(K), int(N), 1 if swiglu else 0))
+
+
+def _prenorm_operands(h, gamma, W, scale, min):
+    h = _dev(h, "h", (torch.float32,))
+    gamma = _dev(gamma, "gamma", _HALF, ndim=1)
+    W = _dev(W, "W", _WORD)
+    scale = _dev(scale, "scale", _HALF)
+    min = _dev(min, "min", _HALF)
+    M, K = h.shape
+    N = W.shape[0]
+    if W.shape[1] * 8 != K or tuple(gamma.shape) != (K,):
+        raise ValueError(f"W must be [N][K/8] and gamma [K] for h of K={K}")
+    if K % GROUP or tuple(scale.shape) != (N, K // GROUP) or tuple(min.shape) != (N, K // GROUP):
+        raise ValueError(f"scale/min must be [N][K/128] = {(N, K // GROUP)}")
+    for t in (gamma, W, scale, min):
+        if t.device != h.device:
+            raise ValueError("all operands must be on the same device")
+    return h, gamma, W, scale, min, M, K, N
+
+
+def _ws256(ws, need, device):
+    """A 256-byte aligned workspace of at least `need` bytes."""
+    if ws is None:
+        ws = torch.empty((max(need, 256) // 4,), dtype=torch.float32, device=device)
+    ws = _workspace(ws, need, device)
+    if ws.data_ptr() % 256:
+        raise ValueError("workspace must be 256-byte aligned")
+    return ws
+
+
+def q4g128_gemm_prenorm(h, gamma, W, scale, min, eps: float = 1e-6, y=None, workspace=None,
+                        stream=None) -> torch.Tensor:
+    """y = x . dequant(W) with x = bf16(h / sqrt(mean(h^2) + eps) * gamma)
+    made from fp32 rows h inside the product (the x_out q4g128_gemm_rmsnorm
+    would give for h, bit for bit)."""
+    h, gamma, W, scale, min, M, K, N = _prenorm_operands(h, gamma, W, scale, min)
+    y = _out(y, M, N, h.device)
+    workspace = _ws256(workspace, q4g128_prenorm_workspace_bytes(M, K, N), h.device)
+    st = lib().q4g128_gemm_prenorm(h.data_ptr(), gamma.data_ptr(), float(eps), M, K, W.data_ptr(), scale.data_ptr(),
+                                   min.data_ptr(), N, y.data_ptr(), workspace.data_ptr(), workspace.numel() * 4,
+                                   _stream(stream, h.device))
+    _check(st, "q4g128_gemm_prenorm")
+    return y
+
+
+def q4g128_gemm_swiglu_prenorm(h, gamma, W, scale, min, eps: float = 1e-6, act=None, workspace=None,
+                               stream=None) -> torch.Tensor:
+    """q4g128_gemm_swiglu on x = the normalised h (as q4g128_gemm_prenorm)."""
+    h, gamma, W, scale, min, M, K, N = _prenorm_operands(h, gamma, W, scale, min)
+    if N % 2:
+        raise ValueError(f"N={N} must be even (gate and up halves)")
+    act = _half_out(act, "act", (M, N // 2), h.device)
+    workspace = _ws256(workspace, q4g128_prenorm_workspace_bytes(M, K, N, True), h.device)
+    st = lib().q4g128_gemm_swiglu_prenorm(h.data_ptr(), gamma.data_ptr(), float(eps), M, K, W.data_ptr(),
+                                          scale.data_ptr(), min.data_ptr(), N, act.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel() * 4, _stream(stream, h.device))
+    _check(st, "q4g128_gemm_swiglu_prenorm")
+    return act
 
 
 def q4g128_quantize(w, ncand: int = 9, W=None, scale=None, min=None, err=None, stream=None):
@@ -376,6 +447,7 @@ def q4g128_quantize(w, ncand: int = 9, W=None, scale=None, min=None, err=None, s
 
 __all__ = ["q4g128_gemm", "q4g128_quantize", "q4g128_gemm_swiglu", "q4g128_swiglu_workspace_bytes",
            "q4g128_gemm_rmsnorm", "q4g128_rmsnorm_workspace", "q4g128_rmsnorm_workspace_bytes",
+           "q4g128_gemm_prenorm", "q4g128_gemm_swiglu_prenorm", "q4g128_prenorm_workspace_bytes",
            "q4g128_gemm_splitk", "q4g128_gemm_splitk_noalloc", "q4g128_gemm_streamk", "q4g128_streamk_workspace",
            "q4g128_streamk_workspace_bytes", "q4g128_dequant", "q4g128_splitk_workspace_bytes",
            "q4g128_splitk_default_splits", "q4g128_gemm_parts", "q4g128_status_string", "q4g128_last_error",

@@ -205,14 +205,17 @@ BalChoice plan_bal(int M, int K, int N, const void *scale, const void *min, bool
 #ifndef Q4G128_LDS_MODE
 #define Q4G128_LDS_MODE -1
 #endif
+int balanced_mode(int N, bool act, int gx, int P)
+{
+    const int tiles = act ? (((N / 2 + 3) / 4 + gx - 1) / gx * 4 + 7) / 8 : bal_tiles(N, gx);
+    return P > 1 ? (act ? 1 : 2) : tiles >= q4g128::kBalMinTiles ? 1 : 0;
+}
+
 hipError_t launch_balanced(const q4g128::GemvArgs &a, int gx, int P, hipStream_t stream)
 {
     using namespace q4g128;
     int mode = Q4G128_LDS_MODE;                 // 0: register ring; 1-4: LDS-fed (rd 2/2/4/4, burst on 2 and 4)
-    if (mode < 0) {
-        const int tiles = a.act ? (((a.N / 2 + 3) / 4 + gx - 1) / gx * 4 + 7) / 8 : bal_tiles(a.N, gx);
-        mode = P > 1 ? (a.act ? 1 : 2) : tiles >= kBalMinTiles ? 1 : 0;
-    }
+    if (mode < 0) mode = balanced_mode(a.N, a.act != nullptr, gx, P);
     if (mode > 0) {
         const int rd = mode >= 3 ? 4 : 2;
         const bool burst = mode == 2 || mode == 4;
@@ -582,26 +585,29 @@ q4g128_status q4g128_gemm_rmsnorm(const void *x, int M, int K, const uint32_t *W
                                   int splits, float *workspace, size_t workspace_bytes, void *stream)
 {
     if (!shape_ok(M, K, N) || !operands_ok(x, W, scale, min, h)) return Q4G128_EINVAL;
-    if (!residual || !gamma || !x_out || !aligned(residual, 4) || !aligned(gamma, 2) || !aligned(x_out, 2))
-        return Q4G128_EINVAL;
-    if (!(eps >= 0.0f) || eps > 3.0e38f) return Q4G128_EINVAL;
+    if (!residual || !aligned(residual, 4)) return Q4G128_EINVAL;
+    const bool norm = x_out != nullptr;          // else the residual add alone
+    if (norm && (!gamma || !aligned(gamma, 2) || !aligned(x_out, 2))) return Q4G128_EINVAL;
+    if (norm && (!(eps >= 0.0f) || eps > 3.0e38f)) return Q4G128_EINVAL;
     if (splits < 1 || splits > max_splits(K) || splits > kMaxSplits) return Q4G128_EINVAL;
     if (!workspace || !aligned(workspace, 4)) return Q4G128_EINVAL;
     if (workspace_bytes < q4g128_rmsnorm_workspace_bytes(M, N, splits)) return Q4G128_EWORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     clear_pending_error();
     // One launch when the splits are the balanced kernel's K parts and the
-    // rows fit it: each workgroup adds the residual to its own columns and
-    // the last one to finish normalises the rows (same bits as below).
+    // rows fit it: each workgroup adds the residual to its own columns (and
+    // with the norm, the last one to finish normalises the rows).  Same bits
+    // as below.
     if (splits > 1) {
+        const int epi = norm ? 2 : 1;
         const BalChoice bc = plan_bal(M, K, N, scale, min);
-        if (bc.gx > 0 && bc.P == splits && M <= bc.rb && q4g128::lds_norm_fits(M, K, N, bc.gx, bc.P)) {
+        if (bc.gx > 0 && bc.P == splits && M <= bc.rb && q4g128::lds_epi_fits(M, K, N, bc.gx, bc.P, epi)) {
             const q4g128::GemvArgs a = gemv_args(x, M, K, W, scale, min, N, h, 1);
             const q4g128::NormArgs na = {residual, static_cast<const uint16_t *>(gamma), eps,
                                          static_cast<uint16_t *>(x_out), reinterpret_cast<uint32_t *>(workspace)};
-            const hipError_t e = q4g128::launch_gemv_lds_norm(a, bc.gx, bc.P, na, st);
+            const hipError_t e = q4g128::launch_gemv_lds_epi(a, bc.gx, bc.P, epi, na, st);
             if (e != hipSuccess) {
-                set_error("gemv+rmsnorm launch", e);
+                set_error(norm ? "gemv+rmsnorm launch" : "gemv+residual launch", e);
                 return Q4G128_EHIP;
             }
             return Q4G128_OK;
@@ -615,10 +621,82 @@ q4g128_status q4g128_gemm_rmsnorm(const void *x, int M, int K, const uint32_t *W
                                                        static_cast<const uint16_t *>(gamma), eps, h,
                                                        static_cast<uint16_t *>(x_out), st);
     if (e != hipSuccess) {
-        set_error("rmsnorm launch", e);
+        set_error(norm ? "rmsnorm launch" : "residual launch", e);
         return Q4G128_EHIP;
     }
     return Q4G128_OK;
+}
+
+size_t q4g128_prenorm_workspace_bytes(int M, int K, int N, int swiglu)
+{
+    if (M < 1 || M > Q4G128_MAX_M || K <= 0 || K % Q4G128_GROUP != 0 || K > kMaxK || N < 1 || N > kMaxN) return 0;
+    if (swiglu && (N < 2 || N % 2)) return 0;
+    const size_t xb = ((size_t)M * (size_t)K * 2 + 255) / 256 * 256;
+    return xb + (swiglu ? q4g128_swiglu_workspace_bytes(M, K, N) : 0);
+}
+
+// The product of x = RMSNorm(h) * gamma: in one launch when the shape's
+// balanced plan takes the normalising staging (whole rows, M <= 8, operands
+// 16-byte aligned), else x into the workspace and the product on it.  The
+// same bits either way, and those of the product called on that x.
+q4g128_status run_prenorm(const float *h, const void *gamma, float eps, int M, int K, const uint32_t *W,
+                          const void *scale, const void *min, int N, float *y, uint16_t *act, float *workspace,
+                          hipStream_t st)
+{
+    clear_pending_error();
+    const bool sw = act != nullptr;
+    const BalChoice bc = plan_bal(M, K, N, scale, min, sw);
+    if (bc.gx > 0 && M <= 8 && (bc.P == 1 || M <= bc.rb) && aligned(h, 16) && aligned(gamma, 16)) {
+        const int mode = balanced_mode(N, sw, bc.gx, bc.P);
+        bool lds = mode > 0;
+        if (!q4g128::xn_fits(M, K, N, bc.gx, bc.P, sw, lds)) lds = !lds;
+        if (q4g128::xn_fits(M, K, N, bc.gx, bc.P, sw, lds)) {
+            q4g128::GemvArgs a = gemv_args(h, M, K, W, scale, min, N, y, 1);
+            a.act = act;
+            const q4g128::NormArgs na = {nullptr, static_cast<const uint16_t *>(gamma), eps, nullptr, nullptr};
+            const hipError_t e = q4g128::launch_gemv_xn(a, bc.gx, bc.P, lds, na, st);
+            if (e != hipSuccess) {
+                set_error("rmsnorm+gemv launch", e);
+                return Q4G128_EHIP;
+            }
+            return Q4G128_OK;
+        }
+    }
+    uint16_t *xb = reinterpret_cast<uint16_t *>(workspace);
+    hipError_t e = q4g128::launch_rmsnorm(h, M, K, static_cast<const uint16_t *>(gamma), eps, xb, st);
+    if (e != hipSuccess) {
+        set_error("rmsnorm launch", e);
+        return Q4G128_EHIP;
+    }
+    float *rest = workspace + ((size_t)M * (size_t)K * 2 + 255) / 256 * 64;
+    return sw ? run_swiglu(xb, M, K, W, scale, min, N, act, rest, st) : run_gemv(xb, M, K, W, scale, min, N, y, 1, st);
+}
+
+q4g128_status q4g128_gemm_prenorm(const float *h, const void *gamma, float eps, int M, int K, const uint32_t *W,
+                                  const void *scale, const void *min, int N, float *y, float *workspace,
+                                  size_t workspace_bytes, void *stream)
+{
+    if (!shape_ok(M, K, N) || !h || !gamma || !aligned(h, 4) || !aligned(gamma, 2)) return Q4G128_EINVAL;
+    if (!W || !scale || !min || !y || !aligned(W, 16) || !aligned(scale, 2) || !aligned(min, 2) || !aligned(y, 4))
+        return Q4G128_EINVAL;
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return Q4G128_EINVAL;
+    if (!workspace || !aligned(workspace, 256)) return Q4G128_EINVAL;
+    if (workspace_bytes < q4g128_prenorm_workspace_bytes(M, K, N, 0)) return Q4G128_EWORKSPACE;
+    return run_prenorm(h, gamma, eps, M, K, W, scale, min, N, y, nullptr, workspace, static_cast<hipStream_t>(stream));
+}
+
+q4g128_status q4g128_gemm_swiglu_prenorm(const float *h, const void *gamma, float eps, int M, int K,
+                                         const uint32_t *W, const void *scale, const void *min, int N, void *act,
+                                         float *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!shape_ok(M, K, N) || N % 2 || !h || !gamma || !aligned(h, 4) || !aligned(gamma, 2)) return Q4G128_EINVAL;
+    if (!W || !scale || !min || !act || !aligned(W, 16) || !aligned(scale, 2) || !aligned(min, 2) || !aligned(act, 2))
+        return Q4G128_EINVAL;
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return Q4G128_EINVAL;
+    if (!workspace || !aligned(workspace, 256)) return Q4G128_EINVAL;
+    if (workspace_bytes < q4g128_prenorm_workspace_bytes(M, K, N, 1)) return Q4G128_EWORKSPACE;
+    return run_prenorm(h, gamma, eps, M, K, W, scale, min, N, nullptr, static_cast<uint16_t *>(act), workspace,
+                       static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

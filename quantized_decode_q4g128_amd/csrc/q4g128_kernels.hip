@@ -414,48 +414,6 @@ __device__ __forceinline__ uint16_t swiglu_bf16(float g, float u)
     return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
 }
 
-__device__ __forceinline__ uint16_t bf16_rne(float a)
-{
-    const uint32_t b = __float_as_uint(a);
-    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
-    return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
-}
-
-// Sum of squares of one row's h values, in the one order every kernel that
-// normalises uses (so a row's output does not depend on which kernel served
-// it): 256 partial sums, partial p the fmaf chain over n = p, p + 256,
-// p + 512, ... (n < N) in ascending n; then a butterfly over each wave's 64
-// partials (lane-independent: every lane adds the same pairs) and the 4 wave
-// totals added in wave order.  Threads 0..255 (waves 0-3, fully active) form
-// the partials, their reads batched 8 at a time (all issued before the
-// first is used); every thread of the workgroup calls it and gets the total.
-// hrow(n) yields h[n]; red: 4 floats of LDS.
-template <class H>
-__device__ __forceinline__ float row_sumsq(const H &hrow, int N, int tid, float *red)
-{
-    if (tid < 256) {
-        float ss = 0.0f;
-        int n = tid;
-        for (; n + 7 * 256 < N; n += 8 * 256) {
-            float v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = hrow(n + j * 256);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
-        }
-        for (; n < N; n += 256) {
-            const float v = hrow(n);
-            ss = fmaf(v, v, ss);
-        }
-        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-        if ((tid & 63) == 0) red[tid >> 6] = ss;
-    }
-    __syncthreads();
-    const float tot = ((red[0] + red[1]) + red[2]) + red[3];
-    __syncthreads();                                      // red may be reused
-    return tot;
-}
-
 // ---- balanced kernel: one workgroup per compute unit ---------------------------
 //
 // A stream only reaches full rate when every compute unit moves about the
@@ -602,11 +560,13 @@ struct BalTile : Tile<1, true, RING, SML, PAD, PAIR, RL, kPairCpol> {
 // workgroups of 4 or more units, where it streams faster, and leaves it off
 // for 3 or fewer tiles per CU, where it streamed slower.  It never changes a
 // bit.
-template <int RING, bool SML, bool PARTS, bool ACT, int RL, bool PAIR>
+// XN: x is the RMSNorm of fp32 rows h (x points to h) times na.gamma, made
+// while staging (S == 1: whole rows).
+template <int RING, bool SML, bool PARTS, bool ACT, int RL, bool PAIR, bool XN>
 __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ mn, int N,
-    float *__restrict__ out, uint16_t *__restrict__ act, int S, int nblp, int P, int nps)
+    float *__restrict__ out, uint16_t *__restrict__ act, int S, int nblp, int P, int nps, NormArgs na)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
 
@@ -623,8 +583,11 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
     // the workgroup's x is in LDS.  Issued together, its few kilobytes queue
     // behind megabytes of weight requests from all CUs, and the barrier waits
     // for the slowest wave's x.  Its loads go out before any other set-up.
-    XStage<kBalThreads, kBalStage, kRowPerm> xst;
-    xst.load(x, M, K, gs, ge);
+    XStage<kBalThreads, kBalStage, kRowPerm, XN> xst;
+    if constexpr (XN)
+        xst.load_norm(reinterpret_cast<const float *>(x), na.gamma, M, K);
+    else
+        xst.load(x, M, K, gs, ge);
     const int gx = gridDim.x;
     // Workgroups are dealt to the 8 XCDs in turn (c -> XCD c % 8); numbering
     // them XCD by XCD before cutting the column range gives every XCD the same
@@ -689,6 +652,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
         cs = PARTS ? gs + ((p * (ng >> 3)) / P) * 8 : gs;
         ce = PARTS ? gs + (((p + 1) * (ng >> 3)) / P) * 8 : ge;
     };
+    if constexpr (XN) xst.norm(xs, M, K, na.eps);
     xst.store(xs, M, gs, ge);
     lds_barrier();
     if (!PARTS && !active) return;
@@ -816,16 +780,20 @@ __device__ __forceinline__ void group_fma(const u32x4 (&a)[4], const f32x4 &xsum
     }
 }
 
-template <int RD, bool PARTS, bool ACT, int RL, bool BURST, bool NORM>
+// EPI (K parts, plain product): 1 stores h = r + y instead of y (out is h);
+// 2 also normalises the rows in the workgroup that finishes last.  XN: x is
+// the RMSNorm of fp32 rows h (x points to h) times gamma, made while staging.
+template <int RD, bool PARTS, bool ACT, int RL, bool BURST, int EPI, bool XN>
 __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ mn, int N,
     float *__restrict__ out, uint16_t *__restrict__ act, int P, int nps, int nblm, NormArgs na)
 {
     static_assert(RD == 2 || RD == 4, "ring depth: units are whole blocks of 4 pairs");
-    static_assert(!NORM || (PARTS && !ACT), "the norm epilogue follows the K-part reduce of the plain product");
+    static_assert(EPI == 0 || (PARTS && !ACT), "the residual epilogue follows the K-part reduce of the plain product");
+    static_assert(!XN || !BURST, "x is made before any weight load is issued");
     constexpr bool burst = BURST;
-    __shared__ float red[NORM ? 4 : 1];
+    constexpr bool NORM = EPI == 2;
     __shared__ uint32_t last_wg;
     __shared__ __attribute__((aligned(16))) u32x4 ring0[kBalWaves * kLdsSlotU4];
     __shared__ __attribute__((aligned(16))) u32x4 ring1[kBalWaves * kLdsSlotU4];
@@ -949,9 +917,14 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
         for (int r = 0; r < RD; ++r) fill(r, min(r, unp - 1));
     };
 
-    XStage<kBalThreads, kBalStage, kRowPerm> xst;
+    XStage<kBalThreads, kBalStage, kRowPerm, XN> xst;
     if (burst) setup_unit(wave, active);
-    xst.load(x, M, K, 0, G);
+    if constexpr (XN) {
+        xst.load_norm(reinterpret_cast<const float *>(x), na.gamma, M, K);
+        xst.norm(xs, M, K, na.eps);
+    } else {
+        xst.load(x, M, K, 0, G);
+    }
     if (burst) prime();                           // after x: x's loads stay the oldest of the wave
     xst.store(xs, M, 0, G);
     lds_barrier();
@@ -1055,20 +1028,20 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
                     }
                 }
             } else if (i < cw) {
-                // NORM: out is h, and this workgroup's columns of h =
-                // residual + y are stored at once (write-through); the
-                // residual loads go out before any store.
+                // EPI: out is h, and this workgroup's columns of h =
+                // residual + y are stored at once (EPI 2: written through);
+                // the residual loads go out before any store.
                 float rv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = kRowPerm ? rowof(4 * h + r) : 4 * h + r;
-                    rv[r] = NORM && row < M ? na.r[(size_t)row * N + cb + i] : 0.0f;
+                    rv[r] = EPI && row < M ? na.r[(size_t)row * N + cb + i] : 0.0f;
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = kRowPerm ? rowof(4 * h + r) : 4 * h + r;
                     if (row < M) {
-                        const float hv = NORM ? rv[r] + v[r] : v[r];
+                        const float hv = EPI ? rv[r] + v[r] : v[r];
                         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, hv), ry,
                                                               (uint32_t)(row * N + cb + i) * 4, 0,
                                                               NORM ? kSysCoherent : 0);
@@ -1098,7 +1071,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
         // Loads in batches of 8 per thread, all issued before the first is
         // used (one memory round trip per batch, not per element).
         constexpr int kB = 8;
-        float *hl = reinterpret_cast<float *>(xs);        // one row of h (x is no longer needed)
+        float *hl = reinterpret_cast<float *>(xs);        // one row of h, then its group sums (x is done)
         // gamma of the thread's first batch of columns, requested before h
         // (indexes clamped into [0, N), so every load is issued unconditionally)
         uint32_t g0[kB];
@@ -1120,8 +1093,8 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
                     if (n0 + j * kBalThreads < N) hl[n0 + j * kBalThreads] = t[j];
             }
             __syncthreads();
-            const float tot = row_sumsq([&](int n) { return hl[n]; }, N, tid, red);
-            const float inv = 1.0f / sqrtf(tot / (float)N + na.eps);
+            const float tot = row_total<kBalThreads>([&](int n) { return hl[n]; }, N, hl + N);
+            const float inv = rms_inv(tot, N, na.eps);
             for (int n0 = tid; n0 < N; n0 += kB * kBalThreads) {
                 uint32_t g[kB];
 #pragma unroll
@@ -1205,23 +1178,25 @@ __global__ __launch_bounds__(256) void sum_swiglu(const float *__restrict__ P, i
 // Residual add + RMSNorm with the split-K partial sums added inside the norm
 // (Token Rush README, steps table rows 8-9).  One workgroup of 1024 threads
 // per row m: thread t takes n = t, t + 1024, ...; y = sum_s P[s] in ascending
-// s, h = r + y (written to h, which may be r itself), ss = sum of h*h in the
-// order of row_sumsq, inv = 1 / sqrt(ss / N + eps) (correctly rounded),
-// x_out = bf16((h * inv) * gamma).  PT > 0: the thread's h values stay in
-// registers (N <= 1024 PT) and the row is also put in LDS (N floats of
-// dynamic LDS) for the sum of squares; PT == 0: it is read back from h.
+// s, h = r + y (written to h, which may be r itself); the row's sum of squares
+// in the shared order (row_total), inv = 1 / sqrt(ss / N + eps) (correctly
+// rounded), x_out = bf16((h * inv) * gamma).
+//   MODE 0: h and x_out.  MODE 1: h only (gamma, xo unused).  MODE 2: no
+//   product: h is r itself (read only, P and S unused), x_out only.
+// PT > 0: the thread's h values stay in registers (N <= 1024 PT) and the row
+// is also put in LDS for the sum of squares; PT == 0: it is read back from h
+// (r for MODE 2).  Dynamic LDS: (PT > 0 ? N : 0) + ceil(N/128) floats.
 #ifndef Q4G128_NORM_THREADS
 #define Q4G128_NORM_THREADS 1024
 #endif
 constexpr int kNormThreads = Q4G128_NORM_THREADS;
 
-template <int PT>
+template <int MODE, int PT>
 __global__ __launch_bounds__(kNormThreads) void sum_residual_rmsnorm(const float *__restrict__ P, int S, int M,
                                                                      int N, const float *r,
                                                                      const uint16_t *__restrict__ gamma, float eps,
                                                                      float *h, uint16_t *__restrict__ xo)
 {
-    __shared__ float red[4];
     extern __shared__ float hl[];
     const int m = blockIdx.x;
     const int tid = threadIdx.x;
@@ -1243,18 +1218,18 @@ __global__ __launch_bounds__(kNormThreads) void sum_residual_rmsnorm(const float
             ok[j] = n < N;
             rv[j] = ok[j] ? r[e[j]] : 0.0f;
         }
-        sum_partials<R>(P, S, MN, e, ok, hv);
+        if (MODE != 2) sum_partials<R>(P, S, MN, e, ok, hv);
 #pragma unroll
         for (int j = 0; j < R; ++j) {
             const int n = tid + j * kNormThreads;
-            const float v = rv[j] + hv[j];
+            const float v = MODE == 2 ? rv[j] : rv[j] + hv[j];
             if (n < N) {
-                h[row + n] = v;
-                hl[n] = v;
+                if (MODE != 2) h[row + n] = v;
+                if (MODE != 1) hl[n] = v;
             }
             hv[j] = v;
         }
-    } else {
+    } else if (MODE != 2) {
         // Wide rows: the same steps on chunks of 8 of the thread's elements
         // (loads of a chunk batched), h read back afterwards.
         for (int j0 = 0; j0 < passes; j0 += 8) {
@@ -1276,18 +1251,20 @@ __global__ __launch_bounds__(kNormThreads) void sum_residual_rmsnorm(const float
             }
         }
     }
-    // The row's h for the sum of squares in the shared order: from LDS, or
-    // (PT == 0) read back from h, just written by this workgroup (the
-    // barrier makes the writes visible).
+    if (MODE == 1) return;
+    // The row's sum of squares in the shared order: from LDS, or (PT == 0)
+    // read back from h, just written by this workgroup (the barrier makes the
+    // writes visible), or from r (MODE 2).
     __syncthreads();
-    const float *hr = h + row;
-    const float tot = PT > 0 ? row_sumsq([&](int n) { return hl[n]; }, N, tid, red)
-                             : row_sumsq([&](int n) { return hr[n]; }, N, tid, red);
-    const float inv = 1.0f / sqrtf(tot / (float)N + eps);
+    const float *hr = (MODE == 2 ? r : h) + row;
+    float *gsum = hl + (PT > 0 ? N : 0);
+    const float tot = PT > 0 ? row_total<kNormThreads>([&](int n) { return hl[n]; }, N, gsum)
+                             : row_total<kNormThreads>([&](int n) { return hr[n]; }, N, gsum);
+    const float inv = rms_inv(tot, N, eps);
     for (int j = 0; j < passes; ++j) {
         const int n = tid + j * kNormThreads;
         if (n < N) {
-            const float v = PT > 0 ? hv[PT > 0 ? j : 0] : h[row + n];   // PT == 0: this thread's own h
+            const float v = PT > 0 ? hv[PT > 0 ? j : 0] : hr[n];   // PT == 0: this thread's own h
             const float gm = __uint_as_float((uint32_t)gamma[n] << 16);
             xo[row + n] = bf16_rne((v * inv) * gm);
         }
@@ -1436,36 +1413,47 @@ BalPlan bal_plan(int M, int K, int N, int S, int gx, int P, bool act)
     return bp;
 }
 
-template <bool PARTS, bool ACT, int RL, bool PAIR>
-static hipError_t launch_bal_v(const GemvArgs &a, int gx, int P, const BalPlan &bp, hipStream_t stream)
+template <bool PARTS, bool ACT, int RL, bool PAIR, bool XN>
+static hipError_t launch_bal_v(const GemvArgs &a, int gx, int P, const BalPlan &bp, const NormArgs &na,
+                               hipStream_t stream)
 {
     static LdsFlags done;
     const hipError_t attr = allow_dynamic_lds(
-        reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT, RL, PAIR>), (int)kBalMaxLds,
-        done);
+        reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT, RL, PAIR, XN>),
+        (int)kBalMaxLds, done);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT, RL, PAIR>),
+    hipLaunchKernelGGL((gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT, RL, PAIR, XN>),
                        dim3((unsigned)gx, (unsigned)a.S, 1), dim3(kBalThreads, 1, 1), bp.lds, stream, a.x, a.M, a.K,
-                       a.W, a.scale, a.mn, a.N, a.out, a.act, a.S, bp.nblp, P, bp.nps);
+                       a.W, a.scale, a.mn, a.N, a.out, a.act, a.S, bp.nblp, P, bp.nps, na);
     return hipGetLastError();
 }
 
-template <bool PARTS, bool ACT, int RL>
-static hipError_t launch_bal_rl(const GemvArgs &a, int gx, int P, hipStream_t stream)
+template <bool PARTS, bool ACT, int RL, bool XN = false>
+static hipError_t launch_bal_rl(const GemvArgs &a, int gx, int P, const NormArgs &na, hipStream_t stream)
 {
     const BalPlan bp = bal_plan(a.M, a.K, a.N, a.S, gx, P, ACT);
-    return bp.pair ? launch_bal_v<PARTS, ACT, RL, true>(a, gx, P, bp, stream)
-                   : launch_bal_v<PARTS, ACT, RL, false>(a, gx, P, bp, stream);
+    return bp.pair ? launch_bal_v<PARTS, ACT, RL, true, XN>(a, gx, P, bp, na, stream)
+                   : launch_bal_v<PARTS, ACT, RL, false, XN>(a, gx, P, bp, na, stream);
 }
 
 // Rows accumulate ceil(M/4) D rows per lane (rowpos).
 template <bool PARTS, bool ACT>
 static hipError_t launch_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)
 {
-    if (kBalOneRow && (a.M == 1 || (kRowPerm && a.M <= 4))) return launch_bal_rl<PARTS, ACT, 1>(a, gx, P, stream);
-    if (kRowPerm && a.M <= 8) return launch_bal_rl<PARTS, ACT, 2>(a, gx, P, stream);
-    if (kRowPerm && a.M <= 12) return launch_bal_rl<PARTS, ACT, 3>(a, gx, P, stream);
-    return launch_bal_rl<PARTS, ACT, 4>(a, gx, P, stream);
+    const NormArgs na{};
+    if (kBalOneRow && (a.M == 1 || (kRowPerm && a.M <= 4))) return launch_bal_rl<PARTS, ACT, 1>(a, gx, P, na, stream);
+    if (kRowPerm && a.M <= 8) return launch_bal_rl<PARTS, ACT, 2>(a, gx, P, na, stream);
+    if (kRowPerm && a.M <= 12) return launch_bal_rl<PARTS, ACT, 3>(a, gx, P, na, stream);
+    return launch_bal_rl<PARTS, ACT, 4>(a, gx, P, na, stream);
+}
+
+// XN on the register-ring kernel: S == 1, M <= 8.
+template <bool PARTS, bool ACT>
+static hipError_t launch_bal_xn(const GemvArgs &a, int gx, int P, const NormArgs &na, hipStream_t stream)
+{
+    if (a.S != 1 || a.M > 8 || !kRowPerm || !kBalOneRow) return hipErrorInvalidValue;
+    return a.M <= 4 ? launch_bal_rl<PARTS, ACT, 1, true>(a, gx, P, na, stream)
+                    : launch_bal_rl<PARTS, ACT, 2, true>(a, gx, P, na, stream);
 }
 
 LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd, bool burst)
@@ -1495,15 +1483,15 @@ LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd, bool burs
     return lp;
 }
 
-template <int RD, bool PARTS, bool ACT, int RL, bool BURST, bool NORM = false>
+template <int RD, bool PARTS, bool ACT, int RL, bool BURST, int EPI = 0, bool XN = false>
 static hipError_t launch_lds_v(const GemvArgs &a, int gx, int P, const LdsPlan &lp, const NormArgs &na,
                                hipStream_t stream)
 {
     static LdsFlags done;
-    const void *k = reinterpret_cast<const void *>(&gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST, NORM>);
+    const void *k = reinterpret_cast<const void *>(&gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST, EPI, XN>);
     const hipError_t attr = allow_dynamic_lds(k, (int)(kBalMaxLds - (lp.total - lp.lds)), done);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST, NORM>), dim3((unsigned)gx, 1, 1),
+    hipLaunchKernelGGL((gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST, EPI, XN>), dim3((unsigned)gx, 1, 1),
                        dim3(kBalThreads, 1, 1), lp.lds, stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.act,
                        P, lp.nps, lp.nblm, na);
     return hipGetLastError();
@@ -1521,22 +1509,54 @@ static hipError_t launch_lds_rl(const GemvArgs &a, int gx, int P, hipStream_t st
     return launch_lds_v<RD, PARTS, ACT, 4, BURST>(a, gx, P, lp, na, stream);
 }
 
-bool lds_norm_fits(int M, int K, int N, int gx, int P)
+bool lds_epi_fits(int M, int K, int N, int gx, int P, int epi)
 {
     const LdsPlan lp = lds_plan(M, K, N, gx, P, false, 2, true);
-    return P > 1 && M <= 8 && lp.fits && lp.lds >= (size_t)N * 4;
+    const size_t tail = epi == 2 ? (size_t)(N + (N + 127) / 128) * sizeof(float) : 0;
+    return P > 1 && M <= 8 && lp.fits && lp.lds >= tail;
 }
 
-hipError_t launch_gemv_lds_norm(const GemvArgs &a, int gx, int P, const NormArgs &na, hipStream_t stream)
+hipError_t launch_gemv_lds_epi(const GemvArgs &a, int gx, int P, int epi, const NormArgs &na, hipStream_t stream)
 {
-    if (a.S != 1 || a.act || !lds_norm_fits(a.M, a.K, a.N, gx, P)) return hipErrorInvalidValue;
+    if (a.S != 1 || a.act || (epi != 1 && epi != 2) || !lds_epi_fits(a.M, a.K, a.N, gx, P, epi))
+        return hipErrorInvalidValue;
     const LdsPlan lp = lds_plan(a.M, a.K, a.N, gx, P, false, 2, true);
-    if (a.M <= 4) return launch_lds_v<2, true, false, 1, true, true>(a, gx, P, lp, na, stream);
-    return launch_lds_v<2, true, false, 2, true, true>(a, gx, P, lp, na, stream);
+    if (epi == 1)
+        return a.M <= 4 ? launch_lds_v<2, true, false, 1, true, 1>(a, gx, P, lp, na, stream)
+                        : launch_lds_v<2, true, false, 2, true, 1>(a, gx, P, lp, na, stream);
+    return a.M <= 4 ? launch_lds_v<2, true, false, 1, true, 2>(a, gx, P, lp, na, stream)
+                    : launch_lds_v<2, true, false, 2, true, 2>(a, gx, P, lp, na, stream);
 }
 
-// Variants built: ring 2 without burst (any shape, the fused SwiGLU too), and
-// burst with rings of 2 or 4 (plain product only).
+// XN on the LDS-fed kernel, ring 2 without burst (x is made before any
+// weight load).
+template <bool PARTS, bool ACT>
+static hipError_t launch_lds_xn(const GemvArgs &a, int gx, int P, const NormArgs &na, hipStream_t stream)
+{
+    const LdsPlan lp = lds_plan(a.M, a.K, a.N, gx, P, ACT, 2, false);
+    if (!lp.fits || a.M > 8) return hipErrorInvalidValue;
+    return a.M <= 4 ? launch_lds_v<2, PARTS, ACT, 1, false, 0, true>(a, gx, P, lp, na, stream)
+                    : launch_lds_v<2, PARTS, ACT, 2, false, 0, true>(a, gx, P, lp, na, stream);
+}
+
+hipError_t launch_gemv_xn(const GemvArgs &a, int gx, int P, bool lds, const NormArgs &na, hipStream_t stream)
+{
+    if (a.S != 1 || a.M > 8) return hipErrorInvalidValue;
+    if (lds) {
+        if (P > 1) return a.act ? hipErrorInvalidValue : launch_lds_xn<true, false>(a, gx, P, na, stream);
+        return a.act ? launch_lds_xn<false, true>(a, gx, 1, na, stream) : launch_lds_xn<false, false>(a, gx, 1, na, stream);
+    }
+    if (P > 1) return hipErrorInvalidValue;
+    return a.act ? launch_bal_xn<false, true>(a, gx, 1, na, stream) : launch_bal_xn<false, false>(a, gx, 1, na, stream);
+}
+
+bool xn_fits(int M, int K, int N, int gx, int P, bool act, bool lds)
+{
+    if (M > 8) return false;
+    if (lds) return (P == 1 || !act) && lds_plan(M, K, N, gx, P, act, 2, false).fits;
+    return P == 1;
+}
+
 hipError_t launch_gemv_lds(const GemvArgs &a, int gx, int P, int rd, bool burst, hipStream_t stream)
 {
     if (a.S != 1) return hipErrorInvalidValue;
@@ -1581,22 +1601,39 @@ hipError_t launch_sum_swiglu(const float *P, int S, int M, int N, uint16_t *act,
 // 16 elements per thread in registers only while the batched loads fit too.
 constexpr bool kNormPt16 = kSumBatch * 16 <= 64;
 
-hipError_t launch_sum_residual_rmsnorm(const float *P, int S, int M, int N, const float *r, const uint16_t *gamma,
-                                       float eps, float *h, uint16_t *xo, hipStream_t stream)
+template <int MODE>
+static hipError_t launch_srn(const float *P, int S, int M, int N, const float *r, const uint16_t *gamma, float eps,
+                             float *h, uint16_t *xo, hipStream_t stream)
 {
     const dim3 grid((unsigned)M, 1, 1), block(kNormThreads, 1, 1);
     const int pt = (N + kNormThreads - 1) / kNormThreads;
-    const size_t lds = (size_t)N * sizeof(float);           // PT > 0 only: at most 64 KB
-    if (pt <= 2)
-        hipLaunchKernelGGL(sum_residual_rmsnorm<2>, grid, block, lds, stream, P, S, M, N, r, gamma, eps, h, xo);
+    const size_t gl = (size_t)((N + 127) / 128) * sizeof(float);
+    const size_t lds = (size_t)N * sizeof(float) + gl;
+    if (lds > 64 * 1024)                                       // the row does not fit the default LDS limit
+        hipLaunchKernelGGL((sum_residual_rmsnorm<MODE, 0>), grid, block, gl, stream, P, S, M, N, r, gamma, eps, h, xo);
+    else if (pt <= 2)
+        hipLaunchKernelGGL((sum_residual_rmsnorm<MODE, 2>), grid, block, lds, stream, P, S, M, N, r, gamma, eps, h, xo);
     else if (pt <= 8)
-        hipLaunchKernelGGL(sum_residual_rmsnorm<8>, grid, block, lds, stream, P, S, M, N, r, gamma, eps, h, xo);
+        hipLaunchKernelGGL((sum_residual_rmsnorm<MODE, 8>), grid, block, lds, stream, P, S, M, N, r, gamma, eps, h, xo);
     else if (pt <= 16 && kNormPt16)
-        hipLaunchKernelGGL(sum_residual_rmsnorm<kNormPt16 ? 16 : 8>, grid, block, lds, stream, P, S, M, N, r, gamma,
-                           eps, h, xo);
+        hipLaunchKernelGGL((sum_residual_rmsnorm<MODE, kNormPt16 ? 16 : 8>), grid, block, lds, stream, P, S, M, N, r,
+                           gamma, eps, h, xo);
     else
-        hipLaunchKernelGGL(sum_residual_rmsnorm<0>, grid, block, 0, stream, P, S, M, N, r, gamma, eps, h, xo);
+        hipLaunchKernelGGL((sum_residual_rmsnorm<MODE, 0>), grid, block, gl, stream, P, S, M, N, r, gamma, eps, h, xo);
     return hipGetLastError();
+}
+
+hipError_t launch_sum_residual_rmsnorm(const float *P, int S, int M, int N, const float *r, const uint16_t *gamma,
+                                       float eps, float *h, uint16_t *xo, hipStream_t stream)
+{
+    if (!xo) return launch_srn<1>(P, S, M, N, r, nullptr, 0.0f, h, nullptr, stream);
+    return launch_srn<0>(P, S, M, N, r, gamma, eps, h, xo, stream);
+}
+
+hipError_t launch_rmsnorm(const float *h, int M, int N, const uint16_t *gamma, float eps, uint16_t *xo,
+                          hipStream_t stream)
+{
+    return launch_srn<2>(nullptr, 0, M, N, h, gamma, eps, nullptr, xo, stream);
 }
 
 hipError_t launch_dequant(const uint32_t *W, const uint16_t *scale, const uint16_t *mn, int K, int N,

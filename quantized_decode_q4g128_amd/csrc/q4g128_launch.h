@@ -158,13 +158,20 @@ struct LdsPlan {
 LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd, bool burst);
 hipError_t launch_gemv_lds(const GemvArgs &a, int gx, int P, int rd, bool burst, hipStream_t stream);
 
-// Residual add + RMSNorm inside the K-part launch (ring 2, burst): every
-// workgroup stores its columns of h = r + y to a.out (h; may be r itself),
-// and the workgroup that finishes last computes x_out = bf16(h / sqrt(mean(h^2)
-// + eps) * gamma) for whole rows.  cnt: a word of the caller's workspace that
-// holds zero, counted up by every workgroup and left at zero again.
-// lds_norm_fits: the shape takes it (K parts, M <= 8, one row of h fitting
-// the dynamic LDS).
+// RMSNorm around the balanced kernels.
+//
+// Epilogue (K-part launch of the LDS-fed kernel, ring 2, burst): every
+// workgroup stores its columns of h = r + y to a.out (h; may be r itself);
+// epi 2: the workgroup that finishes last also computes x_out = bf16(h /
+// sqrt(mean(h^2) + eps) * gamma) for whole rows.  cnt: a word of the
+// caller's workspace that holds zero, counted up by every workgroup and left
+// at zero again.  lds_epi_fits: the shape takes it (K parts, M <= 8, epi 2:
+// one row of h and its group sums fitting the dynamic LDS).
+//
+// Prologue (xn): x = bf16(h / sqrt(mean(h^2) + eps) * gamma) made from fp32
+// rows h (a.x points to h) while staging, then the product as usual: the LDS-
+// fed kernel without burst (lds) or the register-ring kernel; M <= 8, S == 1.
+// xn_fits: the plan (gx, P, kernel) takes it.
 struct NormArgs {
     const float *r;
     const uint16_t *gamma;
@@ -172,8 +179,10 @@ struct NormArgs {
     uint16_t *xo;
     uint32_t *cnt;
 };
-bool lds_norm_fits(int M, int K, int N, int gx, int P);
-hipError_t launch_gemv_lds_norm(const GemvArgs &a, int gx, int P, const NormArgs &na, hipStream_t stream);
+bool lds_epi_fits(int M, int K, int N, int gx, int P, int epi);
+hipError_t launch_gemv_lds_epi(const GemvArgs &a, int gx, int P, int epi, const NormArgs &na, hipStream_t stream);
+bool xn_fits(int M, int K, int N, int gx, int P, bool act, bool lds);
+hipError_t launch_gemv_xn(const GemvArgs &a, int gx, int P, bool lds, const NormArgs &na, hipStream_t stream);
 
 // ---- work-balanced (stream-K) kernel ----------------------------------------
 constexpr int kSkWaves = 8;                 // waves per workgroup, one workgroup per CU
@@ -219,10 +228,13 @@ hipError_t launch_dequant(const uint32_t *W, const uint16_t *scale, const uint16
 
 // Epilogues over partial sums P [S][M][N] (summed in ascending s first):
 // act [M][N/2] = bf16(silu(gate) * up) of the gate/up halves; and
-// h = r + y, x_out = bf16(h / sqrt(mean(h^2) + eps) * gamma) per row (h may be r).
+// h = r + y, x_out = bf16(h / sqrt(mean(h^2) + eps) * gamma) per row (h may be
+// r; xo == nullptr: h only).  launch_rmsnorm: x_out of given rows h alone.
 hipError_t launch_sum_swiglu(const float *P, int S, int M, int N, uint16_t *act, hipStream_t stream);
 hipError_t launch_sum_residual_rmsnorm(const float *P, int S, int M, int N, const float *r, const uint16_t *gamma,
                                        float eps, float *h, uint16_t *xo, hipStream_t stream);
+hipError_t launch_rmsnorm(const float *h, int M, int N, const uint16_t *gamma, float eps, uint16_t *xo,
+                          hipStream_t stream);
 
 // Quantizer (q4g128_quant.hip): groups staged per workgroup for `ncand`, and
 // the launch over `ngroups` consecutive 128-weight groups of w.

@@ -181,7 +181,7 @@ def test_epilogue_rejects(L):
     assert g(*base, FAKE, None, 1e-6, FAKE, FAKE, 1, FAKE, wsb, None) == q.Q4G128_EINVAL    # no gamma
     assert g(*base, FAKE, FAKE, -1.0, FAKE, FAKE, 1, FAKE, wsb, None) == q.Q4G128_EINVAL    # eps < 0
     assert g(*base, FAKE, FAKE, float("nan"), FAKE, FAKE, 1, FAKE, wsb, None) == q.Q4G128_EINVAL
-    assert g(*base, FAKE, FAKE, 1e-6, FAKE, None, 1, FAKE, wsb, None) == q.Q4G128_EINVAL    # no x_out
+    # (x_out NULL is the residual-only form: a valid call, launched only by the GPU tests)
     assert g(*base, FAKE, FAKE, 1e-6, FAKE, FAKE, 0, FAKE, wsb, None) == q.Q4G128_EINVAL    # splits 0
     assert g(*base, FAKE, FAKE, 1e-6, FAKE, FAKE, 9, FAKE, 10 ** 6, None) == q.Q4G128_EINVAL   # > K/128
     assert g(*base, FAKE, FAKE, 1e-6, FAKE, FAKE, 1, FAKE, wsb - 4, None) == q.Q4G128_EWORKSPACE
@@ -196,3 +196,36 @@ def test_splitk_noalloc_rejects_before_launch(L):
     # 136 splits x 16 rows x 5120 columns x 4 bytes = 44.6 MB > the 8 MiB scratch
     assert f(FAKE, 16, 17408, FAKE, FAKE, FAKE, 5120, FAKE, 136, None) == q.Q4G128_EWORKSPACE
     assert b"exceeds the library scratch" in L.q4g128_last_error()
+
+
+def test_prenorm_workspace_and_rejects(L):
+    assert q.q4g128_prenorm_workspace_bytes(1, 5120, 12288) == 10240
+    assert q.q4g128_prenorm_workspace_bytes(3, 128, 2, True) == 768 + q.q4g128_swiglu_workspace_bytes(3, 128, 2)
+    for bad in ((0, 1024, 16, 0), (17, 1024, 16, 0), (1, 100, 16, 0), (1, 1024, 0, 0), (1, 1024, 3, 1)):
+        assert q.q4g128_prenorm_workspace_bytes(*bad) == 0
+    f, g = L.q4g128_gemm_prenorm, L.q4g128_gemm_swiglu_prenorm
+    need = q.q4g128_prenorm_workspace_bytes(1, 1024, 64)
+
+    def call(fn, h=FAKE, gamma=FAKE, eps=1e-6, M=1, K=1024, W=FAKE, s=FAKE, m=FAKE, N=64, out=FAKE, ws=FAKE,
+             nb=None):
+        return fn(h, gamma, eps, M, K, W, s, m, N, out, ws, need if nb is None else nb, None)
+
+    for fn in (f, g):
+        for kw in (dict(h=None), dict(gamma=None), dict(W=None), dict(s=None), dict(m=None), dict(out=None),
+                   dict(h=FAKE + 2), dict(gamma=FAKE + 1), dict(W=FAKE + 4), dict(eps=-1.0),
+                   dict(eps=float("nan")), dict(M=0), dict(M=17), dict(K=100), dict(N=0), dict(ws=None),
+                   dict(ws=FAKE + 16)):
+            assert call(fn, **kw) == q.Q4G128_EINVAL, (fn, kw)
+    assert call(f, nb=need - 4) == q.Q4G128_EWORKSPACE
+    assert call(g, N=63) == q.Q4G128_EINVAL                                  # odd N
+    assert call(g, nb=q.q4g128_prenorm_workspace_bytes(1, 1024, 64, True) - 4) == q.Q4G128_EWORKSPACE
+
+
+def test_rmsnorm_residual_only_arguments(L):
+    g = L.q4g128_gemm_rmsnorm
+    base = [FAKE, 1, 1024, FAKE, FAKE, FAKE, 64]
+    wsb = q.q4g128_rmsnorm_workspace_bytes(1, 64, 1)
+    # x_out NULL: gamma and eps are not read (so bad values do not reject) ...
+    assert g(*base, None, None, -1.0, FAKE, None, 1, FAKE, wsb, None) == q.Q4G128_EINVAL   # ... residual still
+    assert g(*base, FAKE + 2, None, -1.0, FAKE, None, 1, FAKE, wsb, None) == q.Q4G128_EINVAL
+    assert g(*base, FAKE, None, -1.0, FAKE, None, 1, FAKE, wsb - 4, None) == q.Q4G128_EWORKSPACE

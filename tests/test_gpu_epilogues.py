@@ -13,10 +13,11 @@ Residual add + RMSNorm with split-K partials summed in the norm
   * h equals fp32(residual + y) bit for bit, y the split-K product with the
     same splits (q4g128_gemm_splitk);
   * x_out within a tolerance derived from h's bound (product bound plus one
-    fp32 rounding), the fp32 sum of squares (at most ceil(N/256) + 9
-    sequential roundings: a chain over ceil(N/256) columns, 6 butterfly adds,
-    3 adds of wave totals) and the correctly rounded sqrt and divide, plus
-    2^-8 relative for the fp32 products and the bf16 rounding;
+    fp32 rounding), the fp32 sum of squares (at most ceil(N/8192) + 18
+    sequential roundings: 8 in a block's chain, 4 in a group's tree,
+    ceil(N/8192) in a lane's chain of group sums, 6 in the butterfly) and the
+    correctly rounded sqrt and divide, plus 2^-8 relative for the fp32
+    products and the bf16 rounding;
   * in place (h = residual) gives the same results; rows bit-identical
     across M; repeated calls identical;
   * the one-launch form (splits = the K parts, the last workgroup
@@ -131,7 +132,7 @@ def rms_tolerance(y_ref, a_ref, r, gamma_bits, eps, out_ref):
     h = r.astype(np.float64) + y_ref
     th = tau + 2.0 ** -24 * (np.abs(h) + tau)
     ss = np.sum(h * h, axis=1, keepdims=True)
-    L = -(-N // 256) + 9
+    L = -(-N // 8192) + 18
     dss = np.sum(2 * np.abs(h) * th + th * th, axis=1, keepdims=True) + (L + 3) * 2.0 ** -24 * ss
     inv = 1.0 / np.sqrt(ss / N + eps)
     d = 1.01 * 0.5 * dss / (ss + N * eps) + 4 * 2.0 ** -24
