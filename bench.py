@@ -262,19 +262,33 @@ def trace_reading(kernel_prefix):
             "file": os.path.relpath(TRACE_SUMMARY, ROOT)}
 
 
-def measure_wide_verify(torch, q, raw, t_dec, steps, warmup):
-    """Verify steps wider than the 7-row one on the gate/up shape: M = 9 (a
-    draft of 8 tokens plus the next) and M = 16 (the MFMA tile's rows), each
-    timed like M = 7 and given as a ratio to the M = 1 call."""
-    out = {}
+def measure_verify_ratios(torch, raw, dec_calls, ver_calls, ver_bytes, steps, warmup, passes=3):
+    """Verify steps against the decode step on the gate/up shape: M = 7 (the
+    verify workload), M = 9 (a draft of 8 tokens plus the next) and M = 16
+    (the MFMA tile's rows), each `steps` launches on rotating weight copies,
+    timed in `passes` interleaved passes together with M = 1; each ratio is
+    of medians taken in the same passes, so box-to-box and drift effects
+    cancel."""
+    sets = {1: (dec_calls, None)}
+    if ver_calls:
+        sets[7] = (ver_calls, ver_bytes)
     for M in (9, 16):
         case = synth.make_random(M, 5120, 34816, 80 + M)
         B = synth.algorithmic_bytes(M, case.K, case.N)
-        calls, _ = raw.prepare(case, max(2, math.ceil(ROTATE_BYTES / B)), splits=1)
-        n = max(steps, len(calls))
-        t = timed_launches(torch, calls, n, warmup) * 1e-3 / n
-        out[f"M{M}"] = {"us_per_call": round(t * 1e6, 3), "GBps": round(B / t / 1e9, 1), "bytes_per_call": B,
-                        "time_ratio_vs_M1": round(t / t_dec, 4)}
+        sets[M] = (raw.prepare(case, max(2, math.ceil(ROTATE_BYTES / B)), splits=1)[0], B)
+    t = {M: [] for M in sets}
+    for _ in range(passes):
+        for M, (calls, _) in sets.items():
+            n = max(steps, len(calls))
+            t[M].append(timed_launches(torch, calls, n, warmup) * 1e-3 / n)
+    med = {M: sorted(v)[len(v) // 2] for M, v in t.items()}
+    out = {}
+    for M, (_, B) in sets.items():
+        if M == 1:
+            continue
+        out[M] = {"us_per_call": round(med[M] * 1e6, 3), "GBps": round(B / med[M] / 1e9, 1), "bytes_per_call": B,
+                  "time_ratio_vs_M1": round(med[M] / med[1], 4), "M1_us_same_passes": round(med[1] * 1e6, 3),
+                  "passes": passes}
     return out
 
 
@@ -1061,14 +1075,11 @@ def main():
     gbps = B_dec * n_dec / (wall_d * 1e-3) / 1e9
     achieved = B_dec / t_dec / 1e9
     dist = per_call_distribution(torch, dec_calls, max(DIST_CALLS, args.steps))
-    verify = None
+    verify, wider = None, None
     if ver_calls:
-        n_ver = max(args.steps, len(ver_calls))
-        wall_v = timed_launches(torch, ver_calls, n_ver, args.warmup)
-        t_ver = wall_v * 1e-3 / n_ver
-        verify = {"GBps": round(B_ver / t_ver / 1e9, 1), "us_per_call": round(t_ver * 1e6, 3),
-                  "bytes_per_call": B_ver, "time_ratio_vs_M1": round(t_ver / t_dec, 4)}
-    wider = None if args.no_verify else measure_wide_verify(torch, q, raw, t_dec, args.steps, args.warmup)
+        vr = measure_verify_ratios(torch, raw, dec_calls, ver_calls, B_ver, args.steps, args.warmup)
+        verify = vr.pop(7)
+        wider = {f"M{M}": v for M, v in vr.items()}
     traffic = traffic_from_summary()
     ceiling = None if args.no_read_ceiling else measure_read_ceiling(torch, dec_case)
     if ceiling is not None:

@@ -181,7 +181,8 @@ BalChoice plan_bal(int M, int K, int N, const void *scale, const void *min, bool
     const int gx = act ? bal_gx(N, true, ncu) : pg.gx;
     const int P = pg.P;                                        // the plain product's parts, also for ACT
     if (P == 1) {
-        if (!bal_fits(M, K, N, gx, 1, act)) return no;
+        // Rows beyond what x staged whole allows: chunked x (M <= 16).
+        if (!bal_fits(M, K, N, gx, 1, act) && !(M > 8 && q4g128::lds_plan_xch(M, K, N, gx, act).fits)) return no;
         BalChoice c = {gx, 1, M};
         return c;
     }
@@ -222,6 +223,12 @@ hipError_t launch_balanced(const q4g128::GemvArgs &a, int gx, int P, hipStream_t
         if (lds_plan(a.M, a.K, a.N, gx, P, a.act != nullptr, rd, burst).fits)
             return launch_gemv_lds(a, gx, P, rd, burst, stream);
     }
+    // More rows than fit x whole (verify M = 9..16): chunked x, where the
+    // LDS-fed kernel is the faster one or the register-ring kernel cannot
+    // stage the rows.
+    if (a.M > 8 && P == 1 && (mode > 0 || !bal_fits(a.M, a.K, a.N, gx, 1, a.act != nullptr)) &&
+        lds_plan_xch(a.M, a.K, a.N, gx, a.act != nullptr).fits)
+        return launch_gemv_xch(a, gx, stream);
     return launch_gemv_bal(a, gx, P, stream);
 }
 

@@ -745,6 +745,35 @@ constexpr int kLdsBurstBlocks = 4;         // BURST: blocks of 8 groups per unit
 // miss every cache, stores write through to memory.
 constexpr int kSysCoherent = 17;
 
+// LDS counters shared by the waves of a workgroup, read and added to in
+// inline asm: the compiler takes any LDS access it sees as possibly aliasing
+// the direct-to-LDS loads in flight and would wait for all of them first
+// (draining the weight ring).  The read waits for its own result in the same
+// asm block.  f is an LDS address.
+__device__ __forceinline__ uint32_t lds_counter(const uint32_t *f)
+{
+    const uint32_t a = (uint32_t)(size_t)(const __attribute__((address_space(3))) uint32_t *)f;
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+    return v;
+}
+
+__device__ __forceinline__ void lds_count_up(uint32_t *f)
+{
+    const uint32_t a = (uint32_t)(size_t)(__attribute__((address_space(3))) uint32_t *)f;
+    asm volatile("ds_add_u32 %0, %1" : : "v"(a), "v"(1u) : "memory");
+}
+
+// Wait until the LDS counter *f reaches v.  Bounded (about a millisecond):
+// every wave leaves the kernel even if a count never arrives.
+__device__ __forceinline__ void lds_wait_geq(uint32_t *f, uint32_t v)
+{
+    for (int it = 0; it < (1 << 14); ++it) {
+        if (lds_counter(f) >= v) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
 // Waits until the loads of a ring slot have landed, given how many later
 // pairs (two loads each) this wave has requested since (0 .. 3).  Vector
 // memory loads complete in order, so "at most 2n outstanding" covers the
@@ -783,18 +812,25 @@ __device__ __forceinline__ void group_fma(const u32x4 (&a)[4], const f32x4 &xsum
 // EPI (K parts, plain product): 1 stores h = r + y instead of y (out is h);
 // 2 also normalises the rows in the workgroup that finishes last.  XN: x is
 // the RMSNorm of fp32 rows h (x points to h) times gamma, made while staging.
-template <int RD, bool PARTS, bool ACT, int RL, bool BURST, int EPI, bool XN>
+// XCH (rows that do not fit the LDS whole, every tile one wave's, at least
+// one wave without a tile): x is staged in chunks of xcg groups into two
+// buffers.  The waves without a tile load chunk c + 1 while the others run
+// chunk c; one workgroup barrier per chunk boundary hands the buffers over.
+// Every tile's sums run in the same order as with x staged whole.
+template <int RD, bool PARTS, bool ACT, int RL, bool BURST, int EPI, bool XN, bool XCH = false>
 __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ mn, int N,
-    float *__restrict__ out, uint16_t *__restrict__ act, int P, int nps, int nblm, NormArgs na)
+    float *__restrict__ out, uint16_t *__restrict__ act, int P, int nps, int nblm, NormArgs na, int xcg)
 {
     static_assert(RD == 2 || RD == 4, "ring depth: units are whole blocks of 4 pairs");
     static_assert(EPI == 0 || (PARTS && !ACT), "the residual epilogue follows the K-part reduce of the plain product");
     static_assert(!XN || !BURST, "x is made before any weight load is issued");
+    static_assert(!XCH || (!PARTS && !BURST && !XN && EPI == 0), "chunked x: whole-K tiles, x loaded as is");
     constexpr bool burst = BURST;
     constexpr bool NORM = EPI == 2;
     __shared__ uint32_t last_wg;
+    __shared__ uint32_t xflag[XCH ? 2 : 1];               // XCH: chunks staged, chunk completions
     __shared__ __attribute__((aligned(16))) u32x4 ring0[kBalWaves * kLdsSlotU4];
     __shared__ __attribute__((aligned(16))) u32x4 ring1[kBalWaves * kLdsSlotU4];
     __shared__ __attribute__((aligned(16))) u32x4 ring2[RD > 2 ? kBalWaves * kLdsSlotU4 : 1];
@@ -843,7 +879,9 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     // LDS: x [M][G*128] bf16, row sums [G][16] fp32, nps part slots of 256
     // fp32, then one scale/minimum area per wave: [scale, min][16 columns][nblm
     // blocks] of 16 bytes.
-    float *slots = reinterpret_cast<float *>(xs + M * G * 128 + G * kXsRows * 2);
+    const int xg = XCH ? xcg : G;                          // groups of x staged at once
+    const int xstride = M * xg * 128 + xg * kXsRows * 2;  // one x buffer (bf16 units)
+    float *slots = reinterpret_cast<float *>(xs + (XCH ? 2 : 1) * xstride);
     uint8_t *smarea = BURST ? smst + wave * (512 * kLdsBurstBlocks)
                             : reinterpret_cast<uint8_t *>(slots + nps * 256) + (size_t)wave * (512 * nblm);
 
@@ -862,14 +900,22 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
         return min(cc, cw - 1);
     };
     // Loads of ring slot r <- pair p of the current unit (two 1 KB loads).
-    auto fill = [&](int r, int p) {
+    // Pair p of the unit into ring slot r.  live == false: the same two loads
+    // from an empty descriptor (they read nothing and write zeros into the
+    // slot, which is not read again): the main loop refills unconditionally,
+    // so every pass issues the same loads and the compiler's count of loads
+    // in flight stays exact (a refill under a branch made it wait for every
+    // load before reading the second slot).
+    const __amdgpu_buffer_rsrc_t rnone = make_rsrc(W, 0u);
+    auto fill = [&](int r, int p, bool live = true) {
         u32x4 *dst = rings[r] + wave * kLdsSlotU4;
         // The slot's earlier reads are complete before the load may write it.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const uint32_t so = (uint32_t)(64 * ucs + 128 * p);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void *)dst, 16, voffA, so, 0,
+        const __amdgpu_buffer_rsrc_t src = live ? rw : rnone;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, voffA, so, 0,
                                                  kPairCpol);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void *)(dst + 64), 16, voffB,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void *)(dst + 64), 16, voffB,
                                                  so, 0, kPairCpol);
     };
     // Unit u: descriptors and its scale/minimum pieces into the wave's area.
@@ -923,17 +969,48 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
         xst.load_norm(reinterpret_cast<const float *>(x), na.gamma, M, K);
         xst.norm(xs, M, K, na.eps);
     } else {
-        xst.load(x, M, K, 0, G);
+        xst.load(x, M, K, 0, xg);
     }
     if (burst) prime();                           // after x: x's loads stay the oldest of the wave
-    xst.store(xs, M, 0, G);
+    xst.store(xs, M, 0, xg);
+    if (XCH && tid == 0) xflag[0] = xflag[1] = 0u;
     lds_barrier();
+    if (XCH && !active) {
+        // Loader: chunk c (>= 1) into buffer c % 2 once every tile wave is
+        // done with chunk c - 2 (xflag[1] counts (wave, chunk) completions),
+        // then counted in xflag[0] (one count per loader wave and chunk).
+        // The tile waves do not wait for one another, only for the chunk
+        // they need next: a workgroup barrier at each chunk end would hold
+        // every wave to the slowest one while its ring runs dry.
+        const int nchk = (G + xg - 1) / xg;
+        for (int c = 1; c < nchk; ++c) {
+            if (c >= 2) lds_wait_geq(&xflag[1], (uint32_t)(nunit * (c - 1)));
+            // Rounds of 8 pieces per thread where a chunk is more than 12
+            // per loader thread (M = 16 at 5120 -> 34816: 24.2 against
+            // 25.2 us), else of 4 (M = 9, 13: 0.3-0.6 us faster than 8).
+            const int cs = c * xg, ce = min((c + 1) * xg, G), lt = tid - 64 * nunit, nlt = 64 * (kBalWaves - nunit);
+            if (M * (ce - cs) * 16 > 12 * nlt)
+                stage_rounds<8, kRowPerm>(xs + (c & 1) * xstride, x, M, K, cs, ce, lt, nlt);
+            else
+                stage_rounds<4, kRowPerm>(xs + (c & 1) * xstride, x, M, K, cs, ce, lt, nlt);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");      // this wave's writes have landed
+            if (lane == 0) lds_count_up(&xflag[0]);
+        }
+        return;
+    }
     if (!PARTS && !active) return;
 
     const UnpackConsts uc = unpack_consts();
     const int arow = min(kRowPerm ? rowof(i) : i, M - 1);
-    const uint16_t *rbase = xs + arow * G * 128;
-    const float *xrow = reinterpret_cast<const float *>(xs + M * G * 128) + 4 * h;
+    // x of the current chunk [ccs, cce) (the whole of K without XCH): offsets
+    // of the row and of the row sums from xs, indexed by group - ccs.  (Kept
+    // as offsets from xs: a pointer that changes inside the loop hides from
+    // the compiler that x is not where the direct-to-LDS loads land, and it
+    // then waits for all of them before each read of x.)
+    int ccs = 0, cce = xg, chk = 0;
+    int rofs = arow * xg * 128;                           // bf16 units
+    int sofs = (M * xg * 128) / 2 + 4 * h;                // fp32 units
+    const float *xsf = reinterpret_cast<const float *>(xs);
     int aoff[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) aoff[t] = swz(4 * h + t, arow) * 8;
@@ -951,27 +1028,41 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
 #pragma unroll
                 for (int r = 0; r < RD; ++r) {
                     const int p = p0 + r;
-                    // Requested after pair p: pairs p+1 .. min(p+RD-1, unp-1).
-                    wait_ring(min(RD - 1, unp - 1 - p));
+                    if (XCH && ucs + 2 * p == cce) {
+                        // Chunk end: this wave is done with the buffer; wait
+                        // until the loaders have filled the next chunk.
+                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                        if (lane == 0) lds_count_up(&xflag[1]);
+                        ++chk;
+                        lds_wait_geq(&xflag[0], (uint32_t)((kBalWaves - nunit) * chk));
+                        ccs = cce;
+                        cce = min(ccs + xg, G);
+                        const int bo = (chk & 1) * xstride;
+                        rofs = bo + arow * (cce - ccs) * 128;
+                        sofs = (bo + M * (cce - ccs) * 128) / 2 + 4 * h;
+                    }
+                    // Requested after pair p: RD - 1 pairs (refills past the
+                    // last pair included).
+                    wait_ring(RD - 1);
                     const u32x4 *slot = rings[r] + wave * kLdsSlotU4;
                     const u32x4 c0 = slot[boff0];
                     const u32x4 c1 = slot[boff1];
                     const uint32_t sw = *reinterpret_cast<const uint32_t *>(sbase + 4 * p);
                     const uint32_t mw = *reinterpret_cast<const uint32_t *>(sbase + 256 * nblm + 4 * p);
-                    if (p + RD < unp) fill(r, p + RD);
+                    fill(r, p + RD, p + RD < unp);
                     __builtin_amdgcn_sched_barrier(0);
-                    const int g = ucs + 2 * p;
+                    const int g = ucs + 2 * p - ccs;              // group within the staged x
                     u32x4 a[4];
                     f32x4 xsum;
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u32x4 *>(rbase + g * 128 + aoff[t]);
-                    xsum = *reinterpret_cast<const f32x4 *>(xrow + g * kXsRows);
+                    for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u32x4 *>(xs + rofs + g * 128 + aoff[t]);
+                    xsum = *reinterpret_cast<const f32x4 *>(xsf + sofs + g * kXsRows);
                     group_fma<RL>(a, xsum, c0, bf16_lo(sw), bf16_lo(mw), acc, uc);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
-                        a[t] = *reinterpret_cast<const u32x4 *>(rbase + (g + 1) * 128 + aoff[t]);
-                    xsum = *reinterpret_cast<const f32x4 *>(xrow + (g + 1) * kXsRows);
+                        a[t] = *reinterpret_cast<const u32x4 *>(xs + rofs + (g + 1) * 128 + aoff[t]);
+                    xsum = *reinterpret_cast<const f32x4 *>(xsf + sofs + (g + 1) * kXsRows);
                     group_fma<RL>(a, xsum, c1, bf16_hi(sw), bf16_hi(mw), acc, uc);
                 }
             }
@@ -1483,18 +1574,65 @@ LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd, bool burs
     return lp;
 }
 
-template <int RD, bool PARTS, bool ACT, int RL, bool BURST, int EPI = 0, bool XN = false>
+template <int RD, bool PARTS, bool ACT, int RL, bool BURST, int EPI = 0, bool XN = false, bool XCH = false>
 static hipError_t launch_lds_v(const GemvArgs &a, int gx, int P, const LdsPlan &lp, const NormArgs &na,
                                hipStream_t stream)
 {
     static LdsFlags done;
-    const void *k = reinterpret_cast<const void *>(&gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST, EPI, XN>);
+    const void *k = reinterpret_cast<const void *>(&gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST, EPI, XN, XCH>);
     const hipError_t attr = allow_dynamic_lds(k, (int)(kBalMaxLds - (lp.total - lp.lds)), done);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST, EPI, XN>), dim3((unsigned)gx, 1, 1),
+    hipLaunchKernelGGL((gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST, EPI, XN, XCH>), dim3((unsigned)gx, 1, 1),
                        dim3(kBalThreads, 1, 1), lp.lds, stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.act,
-                       P, lp.nps, lp.nblm, na);
+                       P, lp.nps, lp.nblm, na, lp.xcg);
     return hipGetLastError();
+}
+
+LdsPlan lds_plan_xch(int M, int K, int N, int gx, bool act)
+{
+    LdsPlan lp = lds_plan(M, K, N, gx, 1, act, 2, false);
+    lp.fits = false;
+    const int G = K / 128;
+    int tiles;
+    if (act) {
+        const int NU = (N / 2 + 3) / 4;
+        tiles = ((NU + gx - 1) / gx * 4 + 7) / 8;
+    } else {
+        const int N4 = (N + 3) / 4;
+        tiles = ((N4 + gx - 1) / gx * 4 + 15) / 16;
+    }
+    if (M > 16 || tiles >= kBalWaves || G < 4) return lp;
+    const size_t stat = lp.total - lp.lds;
+    const size_t sm = (size_t)tiles * 512 * lp.nblm;          // the tile waves' scale/minimum areas
+    // The largest even chunk whose two buffers fit, then the most even cut
+    // into that many chunks; chunk 0 is staged by every thread (kBalStage
+    // pieces each at most).
+    int cg = 0;
+    for (int c = 2; c <= G && M * c * 16 <= kBalThreads * kBalStage; c += 2)
+        if (stat + 2 * ((size_t)M * c * 256 + (size_t)c * kXsRows * 4) + sm <= kBalMaxLds) cg = c;
+    if (cg == 0) return lp;
+    const int nch = (G + cg - 1) / cg;
+    if (nch < 2) return lp;                                    // fits whole: no chunks needed
+    cg = ((G + nch - 1) / nch + 1) & ~1;
+    lp.xcg = cg;
+    lp.nps = 0;
+    lp.lds = 2 * ((size_t)M * cg * 256 + (size_t)cg * kXsRows * 4) + sm;
+    if (lp.lds + stat < kBalOwnCu) lp.lds = kBalOwnCu - stat;
+    lp.total = lp.lds + stat;
+    lp.fits = lp.total <= kBalMaxLds;
+    return lp;
+}
+
+hipError_t launch_gemv_xch(const GemvArgs &a, int gx, hipStream_t stream)
+{
+    const LdsPlan lp = lds_plan_xch(a.M, a.K, a.N, gx, a.act != nullptr);
+    if (!lp.fits || a.S != 1 || a.M <= 8) return hipErrorInvalidValue;
+    const NormArgs na{};
+    if (a.act)
+        return a.M <= 12 ? launch_lds_v<2, false, true, 3, false, 0, false, true>(a, gx, 1, lp, na, stream)
+                         : launch_lds_v<2, false, true, 4, false, 0, false, true>(a, gx, 1, lp, na, stream);
+    return a.M <= 12 ? launch_lds_v<2, false, false, 3, false, 0, false, true>(a, gx, 1, lp, na, stream)
+                     : launch_lds_v<2, false, false, 4, false, 0, false, true>(a, gx, 1, lp, na, stream);
 }
 
 template <int RD, bool PARTS, bool ACT, bool BURST>

@@ -154,9 +154,16 @@ struct LdsPlan {
     int nblm;       // most 8-group blocks of one unit
     int nps;        // part-sum slots (P > 1)
     bool fits;      // total <= 160 KiB, and (burst) units of at most 4 blocks
+    int xcg = 0;    // chunked x (lds_plan_xch): groups per chunk
 };
 LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd, bool burst);
 hipError_t launch_gemv_lds(const GemvArgs &a, int gx, int P, int rd, bool burst, hipStream_t stream);
+
+// Chunked x on the LDS-fed kernel (ring 2, no burst, K not cut): for rows
+// whose x does not fit the LDS whole, when every tile is one wave's and at
+// least one wave has none (those load the chunks).  M <= 16.
+LdsPlan lds_plan_xch(int M, int K, int N, int gx, bool act);
+hipError_t launch_gemv_xch(const GemvArgs &a, int gx, hipStream_t stream);
 
 // RMSNorm around the balanced kernels.
 //

@@ -307,6 +307,47 @@ struct XStage {
     }
 };
 
+// Stage x[0..M)[cs*128 .. ce*128) into buf in XStage's layout (x rows of
+// (ce - cs)*16 swizzled 16-byte pieces in pair order, then the row sums), by
+// nt threads (a multiple of 64; this thread is number t) in rounds of R
+// pieces per thread, the loads of a round issued together.  Piece p = base +
+// t + j*nt of a round, so the 16 pieces of one (row, group) are one 16-lane
+// row, as in XStage, and the row sums come out bit for bit the same.
+template <int R, bool RP>
+__device__ __forceinline__ void stage_rounds(uint16_t *buf, const uint16_t *__restrict__ x, int M, int K, int cs,
+                                             int ce, int t, int nt)
+{
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    const int pr = (ce - cs) * 16;
+    const int pieces = M * pr;
+    float *Xs = reinterpret_cast<float *>(buf + M * (ce - cs) * 128);
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, kOnePair);
+    const int lane = (int)(threadIdx.x & 63);
+    for (int base = 0; base < pieces; base += R * nt) {
+        u32x4 st[R];
+        int rw[R], bk[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int pu = min(base + t + j * nt, pieces - 1);   // past the end: the last piece again
+            rw[j] = pu / pr;
+            bk[j] = pu - rw[j] * pr;
+            st[j] = *reinterpret_cast<const u32x4 *>(x + (size_t)rw[j] * K + (size_t)cs * 128 + bk[j] * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const int row = rw[j], blk = bk[j];
+            *reinterpret_cast<u32x4 *>(&buf[(row * pr + swz(blk, row)) * 8]) = pair_order(st[j]);
+            const uint32_t w0 = st[j].x, w1 = st[j].y, w2 = st[j].z, w3 = st[j].w;
+            float part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), ones, 0.0f, false);
+            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), ones, part, false);
+            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), ones, part, false);
+            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), ones, part, false);
+            const float tot = row16_sum(part);
+            if ((lane & 15) == 15 && base + t + j * nt < pieces) Xs[(blk >> 4) * kXsRows + (RP ? rowpos(row) : row)] = tot;
+        }
+    }
+}
+
 template <int NT, int SMAX>
 __device__ __forceinline__ void stage_x(uint16_t *xs, const uint16_t *__restrict__ x, int M, int K, int cs,
                                         int ce)

@@ -73,7 +73,7 @@ def misaligned(t: torch.Tensor) -> torch.Tensor:
 SWIGLU_CASES = [("gateup", None, None, None, None), ("verify", None, None, None, None),
                 (None, 3, 2048, 200, 81), (None, 1, 1024, 34, 82), (None, 2, 1024, 2, 83),
                 (None, 8, 640, 100, 84), (None, 5, 8192, 778, 85), (None, 1, 17408, 2 * 1000, 86),
-                (None, 9, 5120, 34816, 87), (None, 16, 2048, 2 * 1000, 88)]
+                (None, 9, 5120, 34816, 87), (None, 16, 2048, 2 * 1000, 88), (None, 13, 5120, 34816, 89)]
 
 
 def swiglu_case(name, M, K, N, seed):
@@ -106,6 +106,18 @@ def test_swiglu_paths_agree(name, M, K, N, seed):
     assert np.array_equal(fused, split)
     again = host_bf16(q.q4g128_gemm_swiglu(x, W, s, m))
     assert np.array_equal(fused, again)
+
+
+def test_swiglu_rows_identical_up_to_16_rows():
+    """Verify drafts of up to 15 tokens: gate/up + SwiGLU with x staged in
+    chunks (M >= 9) against x staged whole (M <= 8)."""
+    case = synth.make_random(16, 5120, 34816, 93)
+    x16 = dev_x(case.x)
+    W, s, m = dev_weights(case.weights)
+    full = host_bf16(q.q4g128_gemm_swiglu(x16, W, s, m))
+    for M in (1, 4, 8, 9, 12, 13, 15):
+        part = host_bf16(q.q4g128_gemm_swiglu(x16[:M].contiguous(), W, s, m))
+        assert np.array_equal(part, full[:M]), M
 
 
 @pytest.mark.parametrize("K,N,seed", [(5120, 34816, 3), (8192, 778, 91), (1024, 2, 92)])

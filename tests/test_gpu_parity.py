@@ -261,15 +261,16 @@ def test_rows_bit_identical_across_kernel_choice(K, N):
 
 # Verify wider than 8 rows (a draft of up to 15 tokens plus the next one):
 # rows of every M up to 16 equal the 16-row call's.  At K = 5120, N = 34816
-# the balanced kernel takes M <= 9 and the per-tile kernel M >= 10; at K =
+# the LDS-fed kernel takes M <= 8 with x staged whole and M >= 9 with x in
+# chunks (loaded by the waves without a tile); at K =
 # 8192, N = 777 the balanced kernel cuts K into 2 parts and holds 6 rows per
 # launch; 17408 -> 5120 (5 parts, 2 rows per launch) runs with its default
 # splits (one launch for M <= 2, 5 K splits beyond); 6144 -> 5120 (2 parts,
 # 8 rows per launch) without splits.  5120 -> 12288 (3 tiles per CU: the
 # balanced kernel loads one group per load) and 5120 -> 20480 (5 tiles per
-# CU: two groups per load) tie both load patterns of the balanced kernel to
-# the per-tile kernel's paired loads (M >= 10), and M = 3, 4, 5, 12, 13 cross
-# the 1-, 2-, 3- and 4-row accumulation of the balanced kernel.
+# CU: two groups per load) tie both load patterns of the register-ring kernel
+# (M <= 8, 9) to the chunked form (M >= 10), and M = 3, 4, 5, 12, 13 cross the
+# 1-, 2-, 3- and 4-row accumulation of the balanced kernels.
 @pytest.mark.parametrize("K,N,split", [(5120, 34816, False), (8192, 777, False), (17408, 5120, True),
                                        (6144, 5120, False), (5120, 12288, False), (5120, 20480, False)])
 def test_rows_bit_identical_up_to_16_rows(K, N, split):
