@@ -193,23 +193,25 @@ BalChoice plan_bal(int M, int K, int N, const void *scale, const void *min, bool
     return c;
 }
 
-// Which balanced kernel runs a planned launch.  Both give the same bits.
+// Which balanced kernel runs a planned launch.  All give the same bits.
 // Workgroups of many whole tiles (8 or more, K not cut: gate/up, the output
 // projection, their SwiGLU and verify forms) take the LDS-fed kernel with a
-// ring of 2 group pairs per wave: gate/up 19.7-20.6 -> 18.3-18.6 us, verify
-// M = 7 21.5 -> 20.6 us, SwiGLU 20.6 -> 18.7 us (one box, interleaved).  K-part
-// shapes take it with the weights requested before x (17408 -> 5120 in 6
-// parts: 13.4 against 14.7 us; 6144 -> 5120: even).  Deeper rings (4 pairs)
-// were slower on every shape.  Few whole tiles per CU without parts (5120 ->
-// 12288) stay on the register-ring kernel (10.3 against 10.6-13.1 us).  A
-// shape whose LDS does not fit the LDS-fed kernel takes the other one.
+// ring of 2 group pairs per wave, each wave's first tile requested before x
+// is staged (burst): gate/up 18.33 -> 17.76 us against x first, M = 7 20.0
+// -> 19.2 us, SwiGLU 18.34 -> 17.82 us (one box, interleaved); against the
+// register-ring kernel 19.7-20.6 us.  K-part shapes take it in burst form
+// too (17408 -> 5120 in 6 parts: 13.4 against 14.7 us; 6144 -> 5120: even),
+// with SwiGLU x first.  Deeper rings (4 pairs) were slower on every shape.
+// Few whole tiles per CU without parts (5120 -> 12288) stay on the
+// register-ring kernel (10.3 against 10.6-13.1 us).  A shape whose LDS does
+// not fit the burst form takes x first, then the register-ring kernel.
 #ifndef Q4G128_LDS_MODE
 #define Q4G128_LDS_MODE -1
 #endif
 int balanced_mode(int N, bool act, int gx, int P)
 {
     const int tiles = act ? (((N / 2 + 3) / 4 + gx - 1) / gx * 4 + 7) / 8 : bal_tiles(N, gx);
-    return P > 1 ? (act ? 1 : 2) : tiles >= q4g128::kBalMinTiles ? 1 : 0;
+    return P > 1 ? (act ? 1 : 2) : tiles >= q4g128::kBalMinTiles ? 2 : 0;
 }
 
 hipError_t launch_balanced(const q4g128::GemvArgs &a, int gx, int P, hipStream_t stream)
@@ -222,6 +224,8 @@ hipError_t launch_balanced(const q4g128::GemvArgs &a, int gx, int P, hipStream_t
         const bool burst = mode == 2 || mode == 4;
         if (lds_plan(a.M, a.K, a.N, gx, P, a.act != nullptr, rd, burst).fits)
             return launch_gemv_lds(a, gx, P, rd, burst, stream);
+        if (burst && lds_plan(a.M, a.K, a.N, gx, P, a.act != nullptr, 2, false).fits)
+            return launch_gemv_lds(a, gx, P, 2, false, stream);
     }
     // More rows than fit x whole (verify M = 9..16): chunked x, where the
     // LDS-fed kernel is the faster one or the register-ring kernel cannot

@@ -740,7 +740,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
 // between the kernels never changes a bit.
 
 constexpr int kLdsSlotU4 = 128;            // u32x4 per wave and ring slot: one group pair of a 16-column tile
-constexpr int kLdsBurstBlocks = 4;         // BURST: blocks of 8 groups per unit, at most
+constexpr int kLdsBurstBlocks = 5;         // BURST: blocks of 8 groups per unit, at most (whole K = 5120 too)
 // Cache-policy bits of a buffer access: system coherence (sc0 | sc1): loads
 // miss every cache, stores write through to memory.
 constexpr int kSysCoherent = 17;
@@ -1699,7 +1699,8 @@ hipError_t launch_gemv_lds(const GemvArgs &a, int gx, int P, int rd, bool burst,
 {
     if (a.S != 1) return hipErrorInvalidValue;
     if (a.act) {
-        if (burst || rd != 2) return hipErrorInvalidValue;
+        if (rd != 2 || (burst && P > 1)) return hipErrorInvalidValue;
+        if (burst) return launch_lds_rl<2, false, true, true>(a, gx, 1, stream);
         return P > 1 ? launch_lds_rl<2, true, true, false>(a, gx, P, stream)
                      : launch_lds_rl<2, false, true, false>(a, gx, 1, stream);
     }
