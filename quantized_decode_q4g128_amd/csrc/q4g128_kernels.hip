@@ -825,7 +825,6 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
 {
     static_assert(RD == 2 || RD == 4, "ring depth: units are whole blocks of 4 pairs");
     static_assert(EPI == 0 || (PARTS && !ACT), "the residual epilogue follows the K-part reduce of the plain product");
-    static_assert(!XN || !BURST, "x is made before any weight load is issued");
     static_assert(!XCH || (!PARTS && !BURST && !XN && EPI == 0), "chunked x: whole-K tiles, x loaded as is");
     constexpr bool burst = BURST;
     constexpr bool NORM = EPI == 2;
@@ -965,13 +964,12 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
 
     XStage<kBalThreads, kBalStage, kRowPerm, XN> xst;
     if (burst) setup_unit(wave, active);
-    if constexpr (XN) {
+    if constexpr (XN)
         xst.load_norm(reinterpret_cast<const float *>(x), na.gamma, M, K);
-        xst.norm(xs, M, K, na.eps);
-    } else {
+    else
         xst.load(x, M, K, 0, xg);
-    }
     if (burst) prime();                           // after x: x's loads stay the oldest of the wave
+    if constexpr (XN) xst.norm(xs, M, K, na.eps);
     xst.store(xs, M, 0, xg);
     if (XCH && tid == 0) xflag[0] = xflag[1] = 0u;
     lds_barrier();
@@ -1623,6 +1621,9 @@ LdsPlan lds_plan_xch(int M, int K, int N, int gx, bool act)
     return lp;
 }
 
+// Chunked x, x staged first (the burst order, each wave's first tile
+// requested before chunk 0, was slower here: M = 12 23.8 against 22.1 us,
+// M = 16 25.5 against 25.1 us, one box).
 hipError_t launch_gemv_xch(const GemvArgs &a, int gx, hipStream_t stream)
 {
     const LdsPlan lp = lds_plan_xch(a.M, a.K, a.N, gx, a.act != nullptr);
@@ -1666,13 +1667,19 @@ hipError_t launch_gemv_lds_epi(const GemvArgs &a, int gx, int P, int epi, const 
                     : launch_lds_v<2, true, false, 2, true, 2>(a, gx, P, lp, na, stream);
 }
 
-// XN on the LDS-fed kernel, ring 2 without burst (x is made before any
-// weight load).
+// XN on the LDS-fed kernel, ring 2: burst (each wave's first tile requested
+// before h and gamma, its ring primed before the norm) where it fits, else
+// x made first.
 template <bool PARTS, bool ACT>
 static hipError_t launch_lds_xn(const GemvArgs &a, int gx, int P, const NormArgs &na, hipStream_t stream)
 {
+    if (a.M > 8) return hipErrorInvalidValue;
+    const LdsPlan lb = lds_plan(a.M, a.K, a.N, gx, P, ACT, 2, true);
+    if (lb.fits)
+        return a.M <= 4 ? launch_lds_v<2, PARTS, ACT, 1, true, 0, true>(a, gx, P, lb, na, stream)
+                        : launch_lds_v<2, PARTS, ACT, 2, true, 0, true>(a, gx, P, lb, na, stream);
     const LdsPlan lp = lds_plan(a.M, a.K, a.N, gx, P, ACT, 2, false);
-    if (!lp.fits || a.M > 8) return hipErrorInvalidValue;
+    if (!lp.fits) return hipErrorInvalidValue;
     return a.M <= 4 ? launch_lds_v<2, PARTS, ACT, 1, false, 0, true>(a, gx, P, lp, na, stream)
                     : launch_lds_v<2, PARTS, ACT, 2, false, 0, true>(a, gx, P, lp, na, stream);
 }
