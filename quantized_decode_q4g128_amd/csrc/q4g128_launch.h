@@ -31,6 +31,7 @@ namespace q4g128 {
 constexpr int kMaxDevices = 64;
 typedef std::atomic<bool> LdsFlags[kMaxDevices];
 
+// `bytes` is capped at what the kernel's own static LDS leaves of 160 KiB.
 inline hipError_t allow_dynamic_lds(const void *kernel, int bytes, LdsFlags &done)
 {
     int dev = 0;
@@ -38,7 +39,11 @@ inline hipError_t allow_dynamic_lds(const void *kernel, int bytes, LdsFlags &don
     if (e != hipSuccess) return e;
     const bool cached = dev >= 0 && dev < kMaxDevices;
     if (cached && done[dev].load(std::memory_order_relaxed)) return hipSuccess;
-    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    hipFuncAttributes fa;
+    e = hipFuncGetAttributes(&fa, kernel);
+    if (e != hipSuccess) return e;
+    const int room = 160 * 1024 - (int)fa.sharedSizeBytes;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes < room ? bytes : room);
     if (e == hipSuccess && cached) done[dev].store(true, std::memory_order_relaxed);
     return e;
 }

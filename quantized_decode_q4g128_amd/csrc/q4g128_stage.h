@@ -237,8 +237,9 @@ struct XStage {
 
     // After load_norm: group sums of squares of every (row, group) into
     // Xs[g][row] (the 16 pieces of a (row, group) are one 16-lane row of a
-    // wave), a barrier, then every wave forms each row's total and lane r
-    // keeps row r's 1/rms; a barrier again before store() reuses Xs.
+    // wave), a barrier, then wave r forms row r's total (all rows at once,
+    // M <= NT/64) into an LDS slot; a barrier again, and every lane r takes
+    // row r's 1/rms from it before store() reuses Xs.
     __device__ __forceinline__ void norm(uint16_t *xs, int M, int K, float eps)
     {
         const int tid = threadIdx.x;
@@ -262,13 +263,15 @@ struct XStage {
             }
         }
         lds_barrier();
+        __shared__ float invs[kXsRows];
         const int lane = tid & 63;
-        inv_l = 0.0f;
-        for (int r = 0; r < M; ++r) {
-            const float t = groups_total([&](int g) { return Xs[g * kXsRows + r]; }, G);
-            if (lane == r) inv_l = rms_inv(t, K, eps);
+        const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        if (w < M) {
+            const float t = groups_total([&](int g) { return Xs[g * kXsRows + w]; }, G);
+            if (lane == 0) invs[w] = rms_inv(t, K, eps);
         }
         lds_barrier();
+        inv_l = lane < M ? invs[lane] : 0.0f;
     }
 
     __device__ __forceinline__ void store(uint16_t *xs, int M, int cs, int ce)
