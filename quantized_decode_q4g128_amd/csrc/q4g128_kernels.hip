@@ -962,13 +962,19 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
         for (int r = 0; r < RD; ++r) fill(r, min(r, unp - 1));
     };
 
+    // Burst: the first tile's scale/minimum requests, x, then the ring's
+    // first pairs; with K parts x goes first (its store then also waits for
+    // the scale/minimum loads: 17408 -> 5120 12.88 -> 12.59 us, 6144 -> 5120
+    // 7.53 -> 7.47; on whole-K shapes even or slower).
+    constexpr bool xfirst = BURST && PARTS;
     XStage<kBalThreads, kBalStage, kRowPerm, XN> xst;
-    if (burst) setup_unit(wave, active);
+    if (burst && !xfirst) setup_unit(wave, active);
     if constexpr (XN)
         xst.load_norm(reinterpret_cast<const float *>(x), na.gamma, M, K);
     else
         xst.load(x, M, K, 0, xg);
-    if (burst) prime();                           // after x: x's loads stay the oldest of the wave
+    if (burst && xfirst) setup_unit(wave, active);
+    if (burst) prime();                           // after x: x's loads stay older than the ring's
     if constexpr (XN) xst.norm(xs, M, K, na.eps);
     xst.store(xs, M, 0, xg);
     if (XCH && tid == 0) xflag[0] = xflag[1] = 0u;
