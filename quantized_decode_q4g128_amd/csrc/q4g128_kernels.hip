@@ -741,6 +741,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
 
 constexpr int kLdsSlotU4 = 128;            // u32x4 per wave and ring slot: one group pair of a 16-column tile
 constexpr int kLdsBurstBlocks = 5;         // BURST: blocks of 8 groups per unit, at most (whole K = 5120 too)
+constexpr int kDeepRing = 8;                // pairs in flight for the youngest tile wave (its slots + 3 idle waves')
 // Cache-policy bits of a buffer access: system coherence (sc0 | sc1): loads
 // miss every cache, stores write through to memory.
 constexpr int kSysCoherent = 17;
@@ -786,6 +787,28 @@ __device__ __forceinline__ void wait_ring(int newer)
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// A ring slot's two code pieces and the pair's scale/minimum words from the
+// burst form's area (the minima kLdsBurstBlocks * 256 bytes after the
+// scales), read and waited for in one block.  The compiler then adds no wait
+// of its own for direct-to-LDS loads it cannot tell apart from these
+// addresses (slots of other waves included); the outputs are early-clobber,
+// so no later read of the block can take its address from a register an
+// earlier read is still writing.
+__device__ __forceinline__ void pair_reads(const u32x4 *a0, const u32x4 *a1, const uint8_t *sp, u32x4 &c0, u32x4 &c1,
+                                           uint32_t &sw, uint32_t &mw)
+{
+    static_assert(kLdsBurstBlocks == 5, "the minima are read 5 * 256 bytes after the scales");
+    const uint32_t x0 = (uint32_t)(size_t)(const __attribute__((address_space(3))) u32x4 *)a0;
+    const uint32_t x1 = (uint32_t)(size_t)(const __attribute__((address_space(3))) u32x4 *)a1;
+    const uint32_t xq = (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t *)sp;
+    uint32_t __attribute__((ext_vector_type(2))) r;
+    asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read2st64_b32 %2, %5 offset1:5\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(c0), "=&v"(c1), "=&v"(r) : "v"(x0), "v"(x1), "v"(xq) : "memory");
+    sw = r.x;
+    mw = r.y;
+}
+
 // Per-group arithmetic shared by the LDS-fed kernel: D = x . (128 + q) by
 // four MFMAs, then acc = fma(s, D, acc), acc = fma(m - 128 s, X, acc) for
 // the RL accumulated D rows.  Identical to Tile::arith for one tile.
@@ -828,6 +851,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     static_assert(!XCH || (!PARTS && !BURST && !XN && EPI == 0), "chunked x: whole-K tiles, x loaded as is");
     constexpr bool burst = BURST;
     constexpr bool NORM = EPI == 2;
+    constexpr bool DEEP = RD == 2 && BURST && !PARTS && !XCH && RL == 1;
     __shared__ uint32_t last_wg;
     __shared__ uint32_t xflag[XCH ? 2 : 1];               // XCH: chunks staged, chunk completions
     __shared__ __attribute__((aligned(16))) u32x4 ring0[kBalWaves * kLdsSlotU4];
@@ -906,8 +930,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     // in flight stays exact (a refill under a branch made it wait for every
     // load before reading the second slot).
     const __amdgpu_buffer_rsrc_t rnone = make_rsrc(W, 0u);
-    auto fill = [&](int r, int p, bool live = true) {
-        u32x4 *dst = rings[r] + wave * kLdsSlotU4;
+    auto fill_at = [&](u32x4 *dst, int p, bool live) {
         // The slot's earlier reads are complete before the load may write it.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         const uint32_t so = (uint32_t)(64 * ucs + 128 * p);
@@ -917,6 +940,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
         __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void *)(dst + 64), 16, voffB,
                                                  so, 0, kPairCpol);
     };
+    auto fill = [&](int r, int p, bool live = true) { fill_at(rings[r] + wave * kLdsSlotU4, p, live); };
     // Unit u: descriptors and its scale/minimum pieces into the wave's area.
     // live == false (a wave without a unit, burst only): unit 0's geometry
     // with empty descriptors, so its loads read nothing and only fill its own
@@ -978,7 +1002,23 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     if constexpr (XN) xst.norm(xs, M, K, na.eps);
     xst.store(xs, M, 0, xg);
     if (XCH && tid == 0) xflag[0] = xflag[1] = 0u;
+    // Deep ring (whole-K burst form, one accumulated row): where at least
+    // three waves have no tile, the youngest tile wave also takes the ring
+    // slots of the three after it and keeps kDeepRing pairs in flight.
+    // Memory issue favours older waves, so the youngest ends last, waiting on
+    // its two-pair ring (gate/up, M = 1: 17.77 -> 17.12 us, interleaved,
+    // 2-4% on most boxes, even on one; M = 5-8: no gain, so not taken).  The
+    // idle waves' empty primes land before the barrier; the deep wave's
+    // pairs 2..7 are requested after it.
+    const bool deep_wg = DEEP && kBalWaves - nunit >= 3 && (G >> 1) >= kDeepRing;
+    const bool deep = deep_wg && wave == nunit - 1;
+    auto dslot = [&](int k) -> u32x4 * { return ((k & 1) ? ring1 : ring0) + (wave + (k >> 1)) * kLdsSlotU4; };
+    if (deep_wg && !active) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
+    if (deep) {
+#pragma unroll
+        for (int k = 2; k < kDeepRing; ++k) fill_at(dslot(k), k, true);
+    }
     if (XCH && !active) {
         // Loader: chunk c (>= 1) into buffer c % 2 once every tile wave is
         // done with chunk c - 2 (xflag[1] counts (wave, chunk) completions),
@@ -1028,46 +1068,70 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
             }
             float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             const uint8_t *sbase = smarea + i * unblk * 16;
-            for (int p0 = 0; p0 < unp; p0 += RD) {
+            // Pair p from `slot`; the slot is refilled with pair p + ahead.
+            auto pair = [&](int p, u32x4 *slot, int ahead) {
+                u32x4 c0, c1;
+                uint32_t sw, mw;
+                if constexpr (DEEP) {
+                    pair_reads(slot + boff0, slot + boff1, sbase + 4 * p, c0, c1, sw, mw);
+                } else {
+                    c0 = slot[boff0];
+                    c1 = slot[boff1];
+                    sw = *reinterpret_cast<const uint32_t *>(sbase + 4 * p);
+                    mw = *reinterpret_cast<const uint32_t *>(sbase + 256 * nblm + 4 * p);
+                }
+                fill_at(slot, p + ahead, p + ahead < unp);
+                __builtin_amdgcn_sched_barrier(0);
+                const int g = ucs + 2 * p - ccs;                  // group within the staged x
+                u32x4 a[4];
+                f32x4 xsum;
 #pragma unroll
-                for (int r = 0; r < RD; ++r) {
-                    const int p = p0 + r;
-                    if (XCH && ucs + 2 * p == cce) {
-                        // Chunk end: this wave is done with the buffer; wait
-                        // until the loaders have filled the next chunk.
-                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                        if (lane == 0) lds_count_up(&xflag[1]);
-                        ++chk;
-                        lds_wait_geq(&xflag[0], (uint32_t)((kBalWaves - nunit) * chk));
-                        ccs = cce;
-                        cce = min(ccs + xg, G);
-                        const int bo = (chk & 1) * xstride;
-                        rofs = bo + arow * (cce - ccs) * 128;
-                        sofs = (bo + M * (cce - ccs) * 128) / 2 + 4 * h;
+                for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u32x4 *>(xs + rofs + g * 128 + aoff[t]);
+                xsum = *reinterpret_cast<const f32x4 *>(xsf + sofs + g * kXsRows);
+                group_fma<RL>(a, xsum, c0, bf16_lo(sw), bf16_lo(mw), acc, uc);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    a[t] = *reinterpret_cast<const u32x4 *>(xs + rofs + (g + 1) * 128 + aoff[t]);
+                xsum = *reinterpret_cast<const f32x4 *>(xsf + sofs + (g + 1) * kXsRows);
+                group_fma<RL>(a, xsum, c1, bf16_hi(sw), bf16_hi(mw), acc, uc);
+            };
+            if (DEEP && deep) {
+                // Slot k: own slots 0, 1, then the lent waves' (k / 2 - 1 past this one).
+                for (int p0 = 0; p0 < unp; p0 += kDeepRing) {
+#pragma unroll
+                    for (int r = 0; r < kDeepRing; ++r) {
+                        const int p = p0 + r;
+                        if (p < unp) {
+                            static_assert(kDeepRing == 8, "vmcnt(14): the 7 later pairs, two loads each");
+                            asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+                            pair(p, dslot(r), kDeepRing);
+                        }
                     }
-                    // Requested after pair p: RD - 1 pairs (refills past the
-                    // last pair included).
-                    wait_ring(RD - 1);
-                    const u32x4 *slot = rings[r] + wave * kLdsSlotU4;
-                    const u32x4 c0 = slot[boff0];
-                    const u32x4 c1 = slot[boff1];
-                    const uint32_t sw = *reinterpret_cast<const uint32_t *>(sbase + 4 * p);
-                    const uint32_t mw = *reinterpret_cast<const uint32_t *>(sbase + 256 * nblm + 4 * p);
-                    fill(r, p + RD, p + RD < unp);
-                    __builtin_amdgcn_sched_barrier(0);
-                    const int g = ucs + 2 * p - ccs;              // group within the staged x
-                    u32x4 a[4];
-                    f32x4 xsum;
+                }
+            } else {
+                for (int p0 = 0; p0 < unp; p0 += RD) {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const u32x4 *>(xs + rofs + g * 128 + aoff[t]);
-                    xsum = *reinterpret_cast<const f32x4 *>(xsf + sofs + g * kXsRows);
-                    group_fma<RL>(a, xsum, c0, bf16_lo(sw), bf16_lo(mw), acc, uc);
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        a[t] = *reinterpret_cast<const u32x4 *>(xs + rofs + (g + 1) * 128 + aoff[t]);
-                    xsum = *reinterpret_cast<const f32x4 *>(xsf + sofs + (g + 1) * kXsRows);
-                    group_fma<RL>(a, xsum, c1, bf16_hi(sw), bf16_hi(mw), acc, uc);
+                    for (int r = 0; r < RD; ++r) {
+                        const int p = p0 + r;
+                        if (XCH && ucs + 2 * p == cce) {
+                            // Chunk end: this wave is done with the buffer; wait
+                            // until the loaders have filled the next chunk.
+                            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                            if (lane == 0) lds_count_up(&xflag[1]);
+                            ++chk;
+                            lds_wait_geq(&xflag[0], (uint32_t)((kBalWaves - nunit) * chk));
+                            ccs = cce;
+                            cce = min(ccs + xg, G);
+                            const int bo = (chk & 1) * xstride;
+                            rofs = bo + arow * (cce - ccs) * 128;
+                            sofs = (bo + M * (cce - ccs) * 128) / 2 + 4 * h;
+                        }
+                        // Requested after pair p: RD - 1 pairs (refills past the
+                        // last pair included).
+                        wait_ring(RD - 1);
+                        pair(p, rings[r] + wave * kLdsSlotU4, RD);
+                    }
                 }
             }
             if (!PARTS) {

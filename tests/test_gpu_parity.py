@@ -334,3 +334,25 @@ def test_k_parts_equal_split_k(K, N):
         plain = host_f32(q.q4g128_gemm(x, W, s, m))
         assert np.array_equal(bits(fast), bits(tile)), (M, "parts vs splits")
         assert np.array_equal(bits(fast), bits(plain)), (M, "splits vs no split")
+
+
+# Deep ring of the LDS-fed kernel's whole-K burst form (rows 1-4 only): with
+# 8 tiles per CU (4 waves without a tile) at K = 2048 the youngest tile
+# wave's 8-pair ring covers its unit exactly; 9 tiles at K = 3072 leave a
+# partial second pass (12 pairs); K = 1024 (4 pairs) is too short for it.
+# Rows 1-4 must equal the 5-row call's rows, which never takes the deep ring,
+# and the 4-row call must be within tolerance; the SwiGLU form alike.
+@pytest.mark.parametrize("K,N", [(2048, 32768), (3072, 34816), (1024, 34816)])
+def test_deep_ring_rows_equal_plain_ring(orc, K, N):
+    case = synth.make_random(5, K, N, 90 + K // 1024, outlier_frac=0.01)
+    wt = case.weights
+    W, s, m = dev_weights(wt)
+    x5 = dev_x(case.x)
+    y5 = host_f32(q.q4g128_gemm(x5, W, s, m))
+    a5 = q.q4g128_gemm_swiglu(x5, W, s, m).view(torch.int16).cpu().numpy()
+    for M in (1, 2, 3, 4):
+        xM = x5[:M].contiguous()
+        assert np.array_equal(bits(host_f32(q.q4g128_gemm(xM, W, s, m))), bits(y5[:M])), M
+        assert np.array_equal(q.q4g128_gemm_swiglu(xM, W, s, m).view(torch.int16).cpu().numpy(), a5[:M]), M
+    y_ref, a_ref = orc.gemm(case.x[:4], wt.W, wt.scale, wt.mn)
+    assert_within_tolerance(y5[:4], y_ref, a_ref, f"deep ring K={K} N={N}")
