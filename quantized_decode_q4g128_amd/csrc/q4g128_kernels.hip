@@ -1003,12 +1003,12 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     xst.store(xs, M, 0, xg);
     if (XCH && tid == 0) xflag[0] = xflag[1] = 0u;
     // Deep ring (whole-K burst form, one accumulated row): where at least
-    // three waves have no tile, the youngest tile wave also takes the ring
-    // slots of the three after it and keeps kDeepRing pairs in flight.
-    // Memory issue favours older waves, so the youngest ends last, waiting on
-    // its two-pair ring (gate/up, M = 1: 17.77 -> 17.12 us, interleaved,
-    // 2-4% on most boxes, even on one; M = 5-8: no gain, so not taken).  The
-    // idle waves' empty primes land before the barrier; the deep wave's
+    // three waves have no tile, the youngest tile wave (the last to end its
+    // loop) also takes the ring slots of the three after it and keeps
+    // kDeepRing pairs in flight.  Back-to-back gate/up launches at M = 1-4
+    // run 2-4% faster with it on most boxes (e.g. 18.01 -> 17.34 us) and up
+    // to 1% slower on some; M = 5-8 gain nothing, so they do not take it.
+    // The idle waves' empty primes land before the barrier; the deep wave's
     // pairs 2..7 are requested after it.
     const bool deep_wg = DEEP && kBalWaves - nunit >= 3 && (G >> 1) >= kDeepRing;
     const bool deep = deep_wg && wave == nunit - 1;
