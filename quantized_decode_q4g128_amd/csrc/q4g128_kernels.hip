@@ -1501,13 +1501,12 @@ int chunk_groups(int M)
 template <int TPW, bool CHUNKED, bool VSM, int WAVES>
 static hipError_t launch_one(const GemvArgs &a, dim3 grid, int cg, hipStream_t stream)
 {
-    // x for up to 16 rows of a chunk can pass 64 KiB (66.5 KiB at M = 16):
-    // allow the kernel the CU's whole LDS.
-    static LdsFlags done;
-    const hipError_t attr = allow_dynamic_lds(
-        reinterpret_cast<const void *>(&gemv_q4g128<TPW, CHUNKED, VSM, kRingDepth, WAVES>), (int)kBalMaxLds, done);
-    if (attr != hipSuccess) return attr;
+    // x for up to 16 rows of a chunk can pass 64 KiB (66.5 KiB at M = 16).
+    static LdsRoom room;
     const size_t lds = (size_t)a.M * (size_t)cg * 128 * 2 + (size_t)cg * kXsRows * 4;
+    const hipError_t attr = lds_launch_ok(
+        reinterpret_cast<const void *>(&gemv_q4g128<TPW, CHUNKED, VSM, kRingDepth, WAVES>), lds, room);
+    if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((gemv_q4g128<TPW, CHUNKED, VSM, kRingDepth, WAVES>), grid, dim3(64 * WAVES, 1, 1), lds,
                        stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.S, cg);
     return hipGetLastError();
@@ -1576,10 +1575,9 @@ template <bool PARTS, bool ACT, int RL, bool PAIR, bool XN>
 static hipError_t launch_bal_v(const GemvArgs &a, int gx, int P, const BalPlan &bp, const NormArgs &na,
                                hipStream_t stream)
 {
-    static LdsFlags done;
-    const hipError_t attr = allow_dynamic_lds(
-        reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT, RL, PAIR, XN>),
-        (int)kBalMaxLds, done);
+    static LdsRoom room;
+    const hipError_t attr = lds_launch_ok(
+        reinterpret_cast<const void *>(&gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT, RL, PAIR, XN>), bp.lds, room);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((gemv_q4g128_bal<kBalRing, kBalSml, PARTS, ACT, RL, PAIR, XN>),
                        dim3((unsigned)gx, (unsigned)a.S, 1), dim3(kBalThreads, 1, 1), bp.lds, stream, a.x, a.M, a.K,
@@ -1631,8 +1629,11 @@ LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd, bool burs
     const int nact = units < kBalWaves ? units : kBalWaves;
     lp.nblm = P > 1 ? (nb + P - 1) / P : nb;
     lp.nps = P > 1 ? units : 0;
+    // Static LDS: the rings, the burst area, and 256 bytes for the kernel's
+    // small arrays (counters, the 1/rms table); the launcher checks the
+    // kernel's actual static size too.
     const size_t stat = (size_t)(rd > 2 ? 4 : 2) * kBalWaves * kLdsSlotU4 * 16 + (rd > 2 ? 0 : 32) +
-                        (burst ? (size_t)kBalWaves * 512 * kLdsBurstBlocks : 16);
+                        (burst ? (size_t)kBalWaves * 512 * kLdsBurstBlocks : 16) + 256;
     lp.fits = !burst || lp.nblm <= kLdsBurstBlocks;
     lp.lds = (size_t)M * G * 256 + (size_t)G * kXsRows * 4 + (size_t)lp.nps * 1024 +
              (burst ? 0 : (size_t)nact * 512 * lp.nblm);
@@ -1646,9 +1647,9 @@ template <int RD, bool PARTS, bool ACT, int RL, bool BURST, int EPI = 0, bool XN
 static hipError_t launch_lds_v(const GemvArgs &a, int gx, int P, const LdsPlan &lp, const NormArgs &na,
                                hipStream_t stream)
 {
-    static LdsFlags done;
+    static LdsRoom room;
     const void *k = reinterpret_cast<const void *>(&gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST, EPI, XN, XCH>);
-    const hipError_t attr = allow_dynamic_lds(k, (int)(kBalMaxLds - (lp.total - lp.lds)), done);
+    const hipError_t attr = lds_launch_ok(k, lp.lds, room);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST, EPI, XN, XCH>), dim3((unsigned)gx, 1, 1),
                        dim3(kBalThreads, 1, 1), lp.lds, stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.act,

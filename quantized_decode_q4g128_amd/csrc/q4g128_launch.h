@@ -26,26 +26,35 @@ namespace q4g128 {
 #define Q4G128_STAGE 16
 #endif
 
-// Dynamic LDS above 64 KiB has to be allowed per kernel and per device; each
-// call site keeps one flag per device so the attribute is set once on each.
+// Dynamic LDS above 64 KiB has to be allowed per kernel and per device.
+// Each call site keeps, per device, the room its kernel's own static LDS
+// leaves of the CU's 160 KiB (0: not yet known), with the kernel's dynamic
+// limit raised to that room the first time.  A launch asking for more than
+// the room is refused here with hipErrorInvalidValue: the runtime does not
+// check static plus dynamic LDS against the CU and would dispatch it, and
+// the dispatch then fails as an invalid allocation that aborts the queue.
 constexpr int kMaxDevices = 64;
-typedef std::atomic<bool> LdsFlags[kMaxDevices];
+constexpr int kCuLds = 160 * 1024;
+typedef std::atomic<int> LdsRoom[kMaxDevices];
 
-// `bytes` is capped at what the kernel's own static LDS leaves of 160 KiB.
-inline hipError_t allow_dynamic_lds(const void *kernel, int bytes, LdsFlags &done)
+inline hipError_t lds_launch_ok(const void *kernel, size_t dyn, LdsRoom &room)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     const bool cached = dev >= 0 && dev < kMaxDevices;
-    if (cached && done[dev].load(std::memory_order_relaxed)) return hipSuccess;
-    hipFuncAttributes fa;
-    e = hipFuncGetAttributes(&fa, kernel);
-    if (e != hipSuccess) return e;
-    const int room = 160 * 1024 - (int)fa.sharedSizeBytes;
-    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes < room ? bytes : room);
-    if (e == hipSuccess && cached) done[dev].store(true, std::memory_order_relaxed);
-    return e;
+    int r = cached ? room[dev].load(std::memory_order_relaxed) : 0;
+    if (r <= 0) {
+        hipFuncAttributes fa;
+        e = hipFuncGetAttributes(&fa, kernel);
+        if (e != hipSuccess) return e;
+        r = kCuLds - (int)fa.sharedSizeBytes;
+        if (r <= 0) return hipErrorInvalidValue;
+        e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, r);
+        if (e != hipSuccess) return e;
+        if (cached) room[dev].store(r, std::memory_order_relaxed);
+    }
+    return dyn <= (size_t)r ? hipSuccess : hipErrorInvalidValue;
 }
 
 constexpr int kMaxM = 16;                  // rows of one MFMA tile

@@ -327,9 +327,9 @@ size_t streamk_lds_bytes(const SkShape &p, int M)
 hipError_t launch_gemv_streamk(const GemvArgs &a, const SkShape &p, float *parts, uint32_t *cnt,
                                hipStream_t stream)
 {
-    static LdsFlags done;
+    static LdsRoom room;
     const hipError_t attr =
-        allow_dynamic_lds(reinterpret_cast<const void *>(&gemv_q4g128_streamk), (int)kBalMaxLds, done);
+        lds_launch_ok(reinterpret_cast<const void *>(&gemv_q4g128_streamk), streamk_lds_bytes(p, a.M), room);
     if (attr != hipSuccess) return attr;
     dim3 grid((unsigned)(p.SK * (p.Wsl / kSkWaves)), 1, 1);
     hipLaunchKernelGGL(gemv_q4g128_streamk, grid, dim3(kSkThreads, 1, 1), streamk_lds_bytes(p, a.M), stream,
