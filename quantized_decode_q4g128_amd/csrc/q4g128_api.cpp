@@ -90,8 +90,9 @@ struct BalChoice {
     int rb;         // P > 1: rows one launch can hold (1..kBalRowBlock); P == 1: M
 };
 
-// K-part shapes stage x for at most this many rows per launch.
-constexpr int kBalRowBlock = 8;
+// K-part shapes stage x for at most this many rows per launch: 9, a draft
+// of 8 tokens plus the next one, fits at K <= 5120.
+constexpr int kBalRowBlock = 9;
 
 // Workgroups for N columns (ACT: N/2 pairs) shared out in units of 4.
 int bal_gx(int N, bool act, int ncu)
@@ -107,27 +108,50 @@ int bal_tiles(int N, int gx)
     return ((N4 + gx - 1) / gx * 4 + 15) / 16;
 }
 
-// K parts per tile: 1 when a workgroup has enough tiles for its waves, else
-// enough parts to occupy them, each part at least `minpart` groups long.
-int bal_parts(int K, int N, int gx, int minpart)
+// K parts per tile, cut at the 8-group blocks: 1 when a workgroup has enough
+// tiles for its waves (the many-tile shapes stream whole columns); else the
+// count whose busiest wave has the fewest blocks to stream, units (tile,
+// part) dealt to the waves in turn, and of those the one that keeps the
+// fewest waves busy.  Measured against the alternatives at M = 1 (one box,
+// interleaved): 5120 -> 12288 (3 tiles per CU) 3 parts 9.45 us against 10.28
+// whole-K on the register-ring kernel, 10.21 in 2 parts, 10.41 in 4, 10.03 in
+// 5; 5120 -> 8192 (2 tiles) 5 parts 0.80 of whole-K, 4 parts 0.89; 5120 ->
+// 16384 (4 tiles) 3 parts 0.90, 2 parts 0.97; 5120 -> 20480 and 5120 -> 24576
+// 2 parts 0.96 and 0.98; 17408 -> 5120 and 6144 -> 5120 (two whole tiles on
+// 160 workgroups) 6 parts, 3-5 parts 8-14% slower.  The sums of a tile do not
+// depend on M, so rows stay bit-identical across M; the price is in rows a
+// launch cannot hold: q4g128_gemm then runs row blocks of up to 9 rows, each
+// streaming the weights again (5120 -> 12288 at M = 10-16: 20.9-22.1 us
+// against 13.0-15.8 us whole-K with x in chunks; M = 7 10.8 against 11.6, M = 9
+// 11.7 against 12.2).
+int bal_parts(int K, int N, int gx)
 {
     using namespace q4g128;
     const int tiles = bal_tiles(N, gx);
     if (tiles >= kBalMinTiles) return 1;
-    int P = kBalWaves / tiles;
-    if (P > K / 128 / minpart) P = K / 128 / minpart;
-    return P < 1 ? 1 : P;
+    const int nb = K / 1024;
+    int best = 1, bestc = 1 << 30, bestw = 1 << 30;
+    for (int P = 1; P <= nb && P <= kBalWaves; ++P) {
+        const int units = tiles * P;
+        const int w = units < kBalWaves ? units : kBalWaves;
+        int crit = 0;
+        for (int v = 0; v < w; ++v) {
+            int load = 0;
+            for (int u = v; u < units; u += kBalWaves) {
+                const int p = u % P;
+                load += ((p + 1) * nb) / P - (p * nb) / P;
+            }
+            crit = load > crit ? load : crit;
+        }
+        if (crit < bestc || (crit == bestc && w < bestw)) {
+            best = P;
+            bestc = crit;
+            bestw = w;
+        }
+    }
+    return best;
 }
 
-// Workgroups and K parts of the plain product, from (K, N) and the CU count
-// only.  Shapes (N a multiple of 16) whose columns would leave each
-// workgroup partial tiles (6144 -> 5120 and 17408 -> 5120: two 10-column
-// tiles per CU) instead get whole 16-column tiles on fewer workgroups and
-// parts as short as one 8-group block (6144 -> 5120: 160 workgroups of two
-// tiles in 6 parts, 7.95 vs 8.78 us; 17408 -> 5120: 160 workgroups of two
-// tiles in 6 parts, one launch of the LDS-fed kernel with its weights
-// requested before x, 13.4 us, against 14.7-15.3 us for the plain cut in 5
-// parts and 13.1 us for 6 K splits and a reduce, one box).
 struct BalGrid {
     int gx;
     int P;
@@ -144,11 +168,11 @@ BalGrid plain_grid(int K, int N, int ncu)
         const int gw = (n16 + per - 1) / per;
         if (gw < g.gx) {
             g.gx = gw;
-            g.P = bal_parts(K, N, gw, 8);
+            g.P = bal_parts(K, N, gw);
             return g;
         }
     }
-    g.P = bal_parts(K, N, g.gx, kBalMinPart);
+    g.P = bal_parts(K, N, g.gx);
     return g;
 }
 
@@ -202,9 +226,10 @@ BalChoice plan_bal(int M, int K, int N, const void *scale, const void *min, bool
 // register-ring kernel 19.7-20.6 us.  K-part shapes take it in burst form
 // too (17408 -> 5120 in 6 parts: 13.4 against 14.7 us; 6144 -> 5120: even),
 // with SwiGLU x first.  Deeper rings (4 pairs) were slower on every shape.
-// Few whole tiles per CU without parts (5120 -> 12288) stay on the
-// register-ring kernel (10.3 against 10.6-13.1 us).  A shape whose LDS does
-// not fit the burst form takes x first, then the register-ring kernel.
+// Few whole tiles per CU without parts (7 tiles per CU, or K = 1024, which
+// has no block to cut at) stay on the register-ring kernel.  A shape whose
+// LDS does not fit the burst form takes x first, then the register-ring
+// kernel.
 #ifndef Q4G128_LDS_MODE
 #define Q4G128_LDS_MODE -1
 #endif

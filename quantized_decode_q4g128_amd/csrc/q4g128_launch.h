@@ -136,10 +136,6 @@ constexpr int kBalStage = 8;                // x pieces per thread: M * ng * 16 
 constexpr int kBalSmRounds = 2;             // scale/min pieces per lane: 16 * nblk <= 128, nblk <= 8
 constexpr size_t kBalOwnCu = 80 * 1024 + 1024;   // LDS request that keeps two workgroups off one CU
 constexpr int kBalMinTiles = 8;             // fewer tiles per workgroup: cut each tile's K into parts
-#ifndef Q4G128_BAL_MINPART
-#define Q4G128_BAL_MINPART 24
-#endif
-constexpr int kBalMinPart = Q4G128_BAL_MINPART;   // groups per K part, at least
 constexpr size_t kBalMaxLds = 160 * 1024;
 
 // Launch geometry of the balanced kernel for M rows, S K splits, gx

@@ -263,16 +263,20 @@ def test_rows_bit_identical_across_kernel_choice(K, N):
 # rows of every M up to 16 equal the 16-row call's.  At K = 5120, N = 34816
 # the LDS-fed kernel takes M <= 8 with x staged whole and M >= 9 with x in
 # chunks (loaded by the waves without a tile); at K =
-# 8192, N = 777 the balanced kernel cuts K into 2 parts and holds 6 rows per
-# launch; 17408 -> 5120 (5 parts, 2 rows per launch) runs with its default
-# splits (one launch for M <= 2, 5 K splits beyond); 6144 -> 5120 (2 parts,
-# 8 rows per launch) without splits.  5120 -> 12288 (3 tiles per CU: the
-# balanced kernel loads one group per load) and 5120 -> 20480 (5 tiles per
-# CU: two groups per load) tie both load patterns of the register-ring kernel
-# (M <= 8, 9) to the chunked form (M >= 10), and M = 3, 4, 5, 12, 13 cross the
-# 1-, 2-, 3- and 4-row accumulation of the balanced kernels.
+# 8192, N = 777 the balanced kernel cuts K into 8 parts and holds 6 rows per
+# launch; 17408 -> 5120 (6 parts, 2 rows per launch) runs with its default
+# splits (one launch for M <= 2, 6 K splits beyond); 6144 -> 5120 (6 parts,
+# 8 rows per launch) without splits; 5120 -> 12288 (3 parts) and 5120 ->
+# 20480 (2 parts) in row blocks of 9.  1024 -> 12288 (3 tiles per CU, no
+# block to cut: the register-ring kernel loads one group per load, all 16
+# rows in one launch) and 5120 -> 28672 (7 tiles per CU: two groups per load,
+# M <= 9; the chunked form for M >= 10) cover both load patterns of the
+# register-ring kernel, and M = 3,
+# 4, 5, 12, 13 cross the 1-, 2-, 3- and 4-row accumulation of the balanced
+# kernels.
 @pytest.mark.parametrize("K,N,split", [(5120, 34816, False), (8192, 777, False), (17408, 5120, True),
-                                       (6144, 5120, False), (5120, 12288, False), (5120, 20480, False)])
+                                       (6144, 5120, False), (5120, 12288, False), (5120, 20480, False),
+                                       (1024, 12288, False), (5120, 28672, False)])
 def test_rows_bit_identical_up_to_16_rows(K, N, split):
     case = synth.make_random(16, K, N, 60 + K // 1024 + N % 1000, outlier_frac=0.01)
     W, s, m = dev_weights(case.weights)
