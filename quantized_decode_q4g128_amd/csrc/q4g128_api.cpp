@@ -239,19 +239,34 @@ int balanced_mode(int N, bool act, int gx, int P)
     return P > 1 ? (act ? 1 : 2) : tiles >= q4g128::kBalMinTiles ? 2 : 0;
 }
 
-hipError_t launch_balanced(const q4g128::GemvArgs &a, int gx, int P, hipStream_t stream)
+// The LDS-fed form a balanced launch of M rows takes: rd > 0 the ring depth
+// (burst: the first tile requested before x), rd == 0 the register-ring
+// kernel.
+struct LdsForm {
+    int rd;
+    bool burst;
+};
+
+LdsForm lds_form(int M, int K, int N, int gx, int P, bool act)
 {
     using namespace q4g128;
     int mode = Q4G128_LDS_MODE;                 // 0: register ring; 1-4: LDS-fed (rd 2/2/4/4, burst on 2 and 4)
-    if (mode < 0) mode = balanced_mode(a.N, a.act != nullptr, gx, P);
+    if (mode < 0) mode = balanced_mode(N, act, gx, P);
     if (mode > 0) {
         const int rd = mode >= 3 ? 4 : 2;
         const bool burst = mode == 2 || mode == 4;
-        if (lds_plan(a.M, a.K, a.N, gx, P, a.act != nullptr, rd, burst).fits)
-            return launch_gemv_lds(a, gx, P, rd, burst, stream);
-        if (burst && lds_plan(a.M, a.K, a.N, gx, P, a.act != nullptr, 2, false).fits)
-            return launch_gemv_lds(a, gx, P, 2, false, stream);
+        if (lds_plan(M, K, N, gx, P, act, rd, burst).fits) return LdsForm{rd, burst};
+        if (burst && lds_plan(M, K, N, gx, P, act, 2, false).fits) return LdsForm{2, false};
     }
+    return LdsForm{0, false};
+}
+
+hipError_t launch_balanced(const q4g128::GemvArgs &a, int gx, int P, hipStream_t stream)
+{
+    using namespace q4g128;
+    const LdsForm f = lds_form(a.M, a.K, a.N, gx, P, a.act != nullptr);
+    if (f.rd > 0) return launch_gemv_lds(a, gx, P, f.rd, f.burst, stream);
+    const int mode = Q4G128_LDS_MODE < 0 ? balanced_mode(a.N, a.act != nullptr, gx, P) : Q4G128_LDS_MODE;
     // More rows than fit x whole (verify M = 9..16): chunked x, where the
     // LDS-fed kernel is the faster one or the register-ring kernel cannot
     // stage the rows.
@@ -306,10 +321,15 @@ q4g128_status run_gemv(const void *x, int M, int K, const uint32_t *W, const voi
 }
 
 // The product with K cut into S ranges of whole 8-group blocks.  When S is
-// the shape's K-part count and one balanced launch holds all M rows, that
-// launch writes the summed result to `dst` as a single slice; otherwise the
-// per-tile kernel writes S partial slices to `ws`.  *slices tells which (1:
-// in dst; S: in ws).  Both give the same bits after the split-order sum.
+// the shape's K-part count and one LDS-fed balanced launch holds all M rows,
+// that launch writes the summed result to `dst` as a single slice; otherwise
+// the per-tile kernel writes S partial slices to `ws`.  *slices tells which
+// (1: in dst; S: in ws).  Both give the same bits after the split-order sum.
+// Where the rows fit only the register-ring kernel (17408 -> 5120 at M = 2)
+// the partial slices and their sum are the faster way: 13.71 against 14.39
+// us; where the LDS-fed kernel holds them the one launch is (5120 -> 12288 at
+// M = 2, 4, 8: 9.75 / 10.01 / 11.61 against 11.28 / 11.74 / 13.44 us; 8192
+// -> 777 at M = 2: 7.01 against 8.13).
 q4g128_status run_split(const void *x, int M, int K, const uint32_t *W, const void *scale, const void *min,
                         int N, int S, float *ws, float *dst, int *slices, hipStream_t stream)
 {
@@ -319,7 +339,7 @@ q4g128_status run_split(const void *x, int M, int K, const uint32_t *W, const vo
         return run_gemv(x, M, K, W, scale, min, N, dst, 1, stream);
     }
     const BalChoice bc = plan_bal(M, K, N, scale, min);
-    if (bc.gx > 0 && bc.P == S && M <= bc.rb) {
+    if (bc.gx > 0 && bc.P == S && M <= bc.rb && lds_form(M, K, N, bc.gx, bc.P, false).rd > 0) {
         *slices = 1;
         q4g128::GemvArgs a = gemv_args(x, M, K, W, scale, min, N, dst, 1);
         hipError_t e = launch_balanced(a, bc.gx, bc.P, stream);
@@ -433,11 +453,10 @@ int q4g128_splitk_default_splits(int K, int N)
     // Where the balanced kernels take the shape in one launch for one row:
     // no splits when it does not cut K (wider M falls back to the per-tile
     // kernel, which then has enough tiles); when it cuts K into parts, that
-    // many splits, so that the split-K call runs the one launch for the rows
-    // it holds (the 17408 -> 5120 down projection: 6 parts, one row at a time
-    // in the LDS-fed kernel, two in the register-ring one) and the per-tile
-    // kernel with the same splits and a reduce beyond, which streams the
-    // weights once for any M (same bits either way).
+    // many splits, so that the split-K call runs the one LDS-fed launch for
+    // the rows it holds (the 17408 -> 5120 down projection: 6 parts, one row)
+    // and the per-tile kernel with the same splits and a reduce beyond, which
+    // streams the weights once for any M (same bits either way).
     const int ncu = device_cus();
     if (K % 1024 == 0 && ncu > 0) {
         const BalGrid g = plain_grid(K, N, ncu);

@@ -264,8 +264,8 @@ def test_rows_bit_identical_across_kernel_choice(K, N):
 # the LDS-fed kernel takes M <= 8 with x staged whole and M >= 9 with x in
 # chunks (loaded by the waves without a tile); at K =
 # 8192, N = 777 the balanced kernel cuts K into 8 parts and holds 6 rows per
-# launch; 17408 -> 5120 (6 parts, 2 rows per launch) runs with its default
-# splits (one launch for M <= 2, 6 K splits beyond); 6144 -> 5120 (6 parts,
+# launch; 17408 -> 5120 (6 parts) runs with its default splits (one LDS-fed
+# launch for M = 1, 6 K splits and their sum beyond); 6144 -> 5120 (6 parts,
 # 8 rows per launch) without splits; 5120 -> 12288 (3 parts) and 5120 ->
 # 20480 (2 parts) in row blocks of 9.  1024 -> 12288 (3 tiles per CU, no
 # block to cut: the register-ring kernel loads one group per load, all 16
