@@ -240,11 +240,13 @@ int balanced_mode(int N, bool act, int gx, int P)
 }
 
 // The LDS-fed form a balanced launch of M rows takes: rd > 0 the ring depth
-// (burst: the first tile requested before x), rd == 0 the register-ring
-// kernel.
+// (burst: the first tile requested before x; nr: ring slots and burst areas
+// for the tile waves only, plus one spare the waves without a tile share),
+// rd == 0 the register-ring kernel.
 struct LdsForm {
     int rd;
     bool burst;
+    bool nr;
 };
 
 LdsForm lds_form(int M, int K, int N, int gx, int P, bool act)
@@ -255,17 +257,23 @@ LdsForm lds_form(int M, int K, int N, int gx, int P, bool act)
     if (mode > 0) {
         const int rd = mode >= 3 ? 4 : 2;
         const bool burst = mode == 2 || mode == 4;
-        if (lds_plan(M, K, N, gx, P, act, rd, burst).fits) return LdsForm{rd, burst};
-        if (burst && lds_plan(M, K, N, gx, P, act, 2, false).fits) return LdsForm{2, false};
+        if (lds_plan(M, K, N, gx, P, act, rd, burst).fits) return LdsForm{rd, burst, false};
+        // Rows whose x leaves the burst form too little LDS with a slot and an
+        // area for every wave (gate/up at M = 8, 9): the burst form with the
+        // spare slot, 21.38 -> 20.46 us at M = 8 against x first, M = 9 21.77
+        // -> 21.01 us against x in chunks (one box, interleaved).
+        if (burst && P == 1 && M >= 5 && lds_plan(M, K, N, gx, P, act, 2, true, true).fits)
+            return LdsForm{2, true, true};
+        if (burst && lds_plan(M, K, N, gx, P, act, 2, false).fits) return LdsForm{2, false, false};
     }
-    return LdsForm{0, false};
+    return LdsForm{0, false, false};
 }
 
 hipError_t launch_balanced(const q4g128::GemvArgs &a, int gx, int P, hipStream_t stream)
 {
     using namespace q4g128;
     const LdsForm f = lds_form(a.M, a.K, a.N, gx, P, a.act != nullptr);
-    if (f.rd > 0) return launch_gemv_lds(a, gx, P, f.rd, f.burst, stream);
+    if (f.rd > 0) return launch_gemv_lds(a, gx, P, f.rd, f.burst, f.nr, stream);
     const int mode = Q4G128_LDS_MODE < 0 ? balanced_mode(a.N, a.act != nullptr, gx, P) : Q4G128_LDS_MODE;
     // More rows than fit x whole (verify M = 9..16): chunked x, where the
     // LDS-fed kernel is the faster one or the register-ring kernel cannot

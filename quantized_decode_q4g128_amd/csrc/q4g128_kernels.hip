@@ -740,7 +740,11 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
 // between the kernels never changes a bit.
 
 constexpr int kLdsSlotU4 = 128;            // u32x4 per wave and ring slot: one group pair of a 16-column tile
-constexpr int kLdsBurstBlocks = 5;         // BURST: blocks of 8 groups per unit, at most (whole K = 5120 too)
+constexpr int kLdsBurstBlocks = 5;
+// NR launches: tile waves with a ring slot and a burst area of their own; the
+// waves without a tile share one more (their empty loads write only zeros,
+// which nothing reads).
+constexpr int kNarrowRingWaves = 9;         // BURST: blocks of 8 groups per unit, at most (whole K = 5120 too)
 constexpr int kDeepRing = 8;                // pairs in flight for the youngest tile wave (its slots + 3 idle waves')
 // Cache-policy bits of a buffer access: system coherence (sc0 | sc1): loads
 // miss every cache, stores write through to memory.
@@ -839,8 +843,11 @@ __device__ __forceinline__ void group_fma(const u32x4 (&a)[4], const f32x4 &xsum
 // one wave without a tile): x is staged in chunks of xcg groups into two
 // buffers.  The waves without a tile load chunk c + 1 while the others run
 // chunk c; one workgroup barrier per chunk boundary hands the buffers over.
-// Every tile's sums run in the same order as with x staged whole.
-template <int RD, bool PARTS, bool ACT, int RL, bool BURST, int EPI, bool XN, bool XCH = false>
+// Every tile's sums run in the same order as with x staged whole.  NR (whole
+// K, at most kNarrowRingWaves tiles): ring slots and burst areas for the tile
+// waves plus one the others share, 13 KB less static LDS, which leaves x room
+// for M = 8 and 9 at K = 5120 in the burst form.
+template <int RD, bool PARTS, bool ACT, int RL, bool BURST, int EPI, bool XN, bool XCH = false, bool NR = false>
 __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     const uint16_t *__restrict__ x, int M, int K, const uint32_t *__restrict__ W,
     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ mn, int N,
@@ -851,18 +858,20 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     static_assert(!XCH || (!PARTS && !BURST && !XN && EPI == 0), "chunked x: whole-K tiles, x loaded as is");
     constexpr bool burst = BURST;
     constexpr bool NORM = EPI == 2;
-    constexpr bool DEEP = RD == 2 && BURST && !PARTS && !XCH && RL == 1;
+    static_assert(!NR || (RD == 2 && !PARTS && !XCH), "shared spare slot: whole-K tiles, x staged whole");
+    constexpr bool DEEP = RD == 2 && BURST && !PARTS && !XCH && RL == 1 && !NR;
+    constexpr int RW = NR ? kNarrowRingWaves + 1 : kBalWaves;    // ring slots and burst areas
     __shared__ uint32_t last_wg;
     __shared__ uint32_t xflag[XCH ? 2 : 1];               // XCH: chunks staged, chunk completions
-    __shared__ __attribute__((aligned(16))) u32x4 ring0[kBalWaves * kLdsSlotU4];
-    __shared__ __attribute__((aligned(16))) u32x4 ring1[kBalWaves * kLdsSlotU4];
+    __shared__ __attribute__((aligned(16))) u32x4 ring0[RW * kLdsSlotU4];
+    __shared__ __attribute__((aligned(16))) u32x4 ring1[RW * kLdsSlotU4];
     __shared__ __attribute__((aligned(16))) u32x4 ring2[RD > 2 ? kBalWaves * kLdsSlotU4 : 1];
     __shared__ __attribute__((aligned(16))) u32x4 ring3[RD > 2 ? kBalWaves * kLdsSlotU4 : 1];
     // BURST: the scale/minimum areas in an array of their own (units of at
     // most kLdsBurstBlocks blocks), so that x, staged while every load of the
     // burst is in flight, provably shares no LDS with them and its staging
     // waits for the x loads alone.
-    __shared__ __attribute__((aligned(16))) uint8_t smst[BURST ? kBalWaves * 512 * kLdsBurstBlocks : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t smst[BURST ? RW * 512 * kLdsBurstBlocks : 16];
     extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
     u32x4 *const rings[4] = {ring0, ring1, ring2, ring3};
     if (BURST) nblm = kLdsBurstBlocks;
@@ -905,8 +914,10 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     const int xg = XCH ? xcg : G;                          // groups of x staged at once
     const int xstride = M * xg * 128 + xg * kXsRows * 2;  // one x buffer (bf16 units)
     float *slots = reinterpret_cast<float *>(xs + (XCH ? 2 : 1) * xstride);
-    uint8_t *smarea = BURST ? smst + wave * (512 * kLdsBurstBlocks)
-                            : reinterpret_cast<uint8_t *>(slots + nps * 256) + (size_t)wave * (512 * nblm);
+    // Ring slot and burst area index: the wave's own, or NR's shared spare.
+    const int slotw = NR && !active ? kNarrowRingWaves : wave;
+    uint8_t *smarea = BURST ? smst + slotw * (512 * kLdsBurstBlocks)
+                            : reinterpret_cast<uint8_t *>(slots + nps * 256) + (size_t)slotw * (512 * nblm);
 
     const int i = lane & 15, h = lane >> 4;
     const int cq = lane >> 3, jq = lane & 7;
@@ -940,7 +951,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
         __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void *)(dst + 64), 16, voffB,
                                                  so, 0, kPairCpol);
     };
-    auto fill = [&](int r, int p, bool live = true) { fill_at(rings[r] + wave * kLdsSlotU4, p, live); };
+    auto fill = [&](int r, int p, bool live = true) { fill_at(rings[r] + slotw * kLdsSlotU4, p, live); };
     // Unit u: descriptors and its scale/minimum pieces into the wave's area.
     // live == false (a wave without a unit, burst only): unit 0's geometry
     // with empty descriptors, so its loads read nothing and only fill its own
@@ -1130,7 +1141,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
                         // Requested after pair p: RD - 1 pairs (refills past the
                         // last pair included).
                         wait_ring(RD - 1);
-                        pair(p, rings[r] + wave * kLdsSlotU4, RD);
+                        pair(p, rings[r] + slotw * kLdsSlotU4, RD);
                     }
                 }
             }
@@ -1613,7 +1624,7 @@ static hipError_t launch_bal_xn(const GemvArgs &a, int gx, int P, const NormArgs
                     : launch_bal_rl<PARTS, ACT, 2, true>(a, gx, P, na, stream);
 }
 
-LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd, bool burst)
+LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd, bool burst, bool nr)
 {
     LdsPlan lp;
     const int G = K / 128, nb = G / 8;
@@ -1632,9 +1643,13 @@ LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd, bool burs
     // Static LDS: the rings, the burst area, and 256 bytes for the kernel's
     // small arrays (counters, the 1/rms table); the launcher checks the
     // kernel's actual static size too.
-    const size_t stat = (size_t)(rd > 2 ? 4 : 2) * kBalWaves * kLdsSlotU4 * 16 + (rd > 2 ? 0 : 32) +
-                        (burst ? (size_t)kBalWaves * 512 * kLdsBurstBlocks : 16) + 256;
+    const size_t rw = nr ? kNarrowRingWaves + 1 : kBalWaves;
+    const size_t stat = (size_t)(rd > 2 ? 4 : 2) * rw * kLdsSlotU4 * 16 + (rd > 2 ? 0 : 32) +
+                        (burst ? rw * 512 * kLdsBurstBlocks : 16) + 256;
     lp.fits = !burst || lp.nblm <= kLdsBurstBlocks;
+    // x staged whole passes through kBalStage registers per thread.
+    lp.fits = lp.fits && (long)M * G * 16 <= (long)kBalThreads * kBalStage;
+    if (nr) lp.fits = lp.fits && P == 1 && rd == 2 && tiles <= kNarrowRingWaves;
     lp.lds = (size_t)M * G * 256 + (size_t)G * kXsRows * 4 + (size_t)lp.nps * 1024 +
              (burst ? 0 : (size_t)nact * 512 * lp.nblm);
     if (lp.lds + stat < kBalOwnCu) lp.lds = kBalOwnCu - stat;
@@ -1643,15 +1658,16 @@ LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd, bool burs
     return lp;
 }
 
-template <int RD, bool PARTS, bool ACT, int RL, bool BURST, int EPI = 0, bool XN = false, bool XCH = false>
+template <int RD, bool PARTS, bool ACT, int RL, bool BURST, int EPI = 0, bool XN = false, bool XCH = false,
+          bool NR = false>
 static hipError_t launch_lds_v(const GemvArgs &a, int gx, int P, const LdsPlan &lp, const NormArgs &na,
                                hipStream_t stream)
 {
     static LdsRoom room;
-    const void *k = reinterpret_cast<const void *>(&gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST, EPI, XN, XCH>);
+    const void *k = reinterpret_cast<const void *>(&gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST, EPI, XN, XCH, NR>);
     const hipError_t attr = lds_launch_ok(k, lp.lds, room);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST, EPI, XN, XCH>), dim3((unsigned)gx, 1, 1),
+    hipLaunchKernelGGL((gemv_q4g128_lds<RD, PARTS, ACT, RL, BURST, EPI, XN, XCH, NR>), dim3((unsigned)gx, 1, 1),
                        dim3(kBalThreads, 1, 1), lp.lds, stream, a.x, a.M, a.K, a.W, a.scale, a.mn, a.N, a.out, a.act,
                        P, lp.nps, lp.nblm, na, lp.xcg);
     return hipGetLastError();
@@ -1773,9 +1789,24 @@ bool xn_fits(int M, int K, int N, int gx, int P, bool act, bool lds)
     return P == 1;
 }
 
-hipError_t launch_gemv_lds(const GemvArgs &a, int gx, int P, int rd, bool burst, hipStream_t stream)
+// NR: burst form, ring 2, whole K, M = 5-12 (2 or 3 accumulated rows).
+template <bool ACT>
+static hipError_t launch_lds_nr(const GemvArgs &a, int gx, hipStream_t stream)
+{
+    const LdsPlan lp = lds_plan(a.M, a.K, a.N, gx, 1, ACT, 2, true, true);
+    if (!lp.fits || a.M < 5 || a.M > 12) return hipErrorInvalidValue;
+    const NormArgs na{};
+    if (a.M <= 8) return launch_lds_v<2, false, ACT, 2, true, 0, false, false, true>(a, gx, 1, lp, na, stream);
+    return launch_lds_v<2, false, ACT, 3, true, 0, false, false, true>(a, gx, 1, lp, na, stream);
+}
+
+hipError_t launch_gemv_lds(const GemvArgs &a, int gx, int P, int rd, bool burst, bool nr, hipStream_t stream)
 {
     if (a.S != 1) return hipErrorInvalidValue;
+    if (nr) {
+        if (rd != 2 || !burst || P != 1) return hipErrorInvalidValue;
+        return a.act ? launch_lds_nr<true>(a, gx, stream) : launch_lds_nr<false>(a, gx, stream);
+    }
     if (a.act) {
         if (rd != 2 || (burst && P > 1)) return hipErrorInvalidValue;
         if (burst) return launch_lds_rl<2, false, true, true>(a, gx, 1, stream);

@@ -158,6 +158,8 @@ hipError_t launch_gemv_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)
 // 4) group pairs per wave; `burst` requests the first unit's weights before x.
 // Needs S == 1, K % 1024 == 0, 16-byte aligned scale/min, and lds_plan().fits;
 // built variants: rd 2 (plain or fused SwiGLU), burst with rd 2 or 4 (plain).
+// nr (burst, rd 2, K not cut, at most 9 tiles, M = 5-12): ring slots and
+// burst areas for the tile waves only, plus one spare the others share.
 struct LdsPlan {
     size_t lds;     // dynamic LDS bytes
     size_t total;   // dynamic + the static LDS (rings; burst: scale/minimum areas)
@@ -166,8 +168,8 @@ struct LdsPlan {
     bool fits;      // total <= 160 KiB, and (burst) units of at most 4 blocks
     int xcg = 0;    // chunked x (lds_plan_xch): groups per chunk
 };
-LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd, bool burst);
-hipError_t launch_gemv_lds(const GemvArgs &a, int gx, int P, int rd, bool burst, hipStream_t stream);
+LdsPlan lds_plan(int M, int K, int N, int gx, int P, bool act, int rd, bool burst, bool nr = false);
+hipError_t launch_gemv_lds(const GemvArgs &a, int gx, int P, int rd, bool burst, bool nr, hipStream_t stream);
 
 // Chunked x on the LDS-fed kernel (ring 2, no burst, K not cut): for rows
 // whose x does not fit the LDS whole, when every tile is one wave's and at

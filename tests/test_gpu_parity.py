@@ -261,8 +261,9 @@ def test_rows_bit_identical_across_kernel_choice(K, N):
 
 # Verify wider than 8 rows (a draft of up to 15 tokens plus the next one):
 # rows of every M up to 16 equal the 16-row call's.  At K = 5120, N = 34816
-# the LDS-fed kernel takes M <= 8 with x staged whole and M >= 9 with x in
-# chunks (loaded by the waves without a tile); at K =
+# the LDS-fed kernel takes M <= 9 with x staged whole (M = 8, 9 with ring
+# slots for the tile waves only and one spare) and M >= 10 with x in chunks
+# (loaded by the waves without a tile); at K =
 # 8192, N = 777 the balanced kernel cuts K into 8 parts and holds 6 rows per
 # launch; 17408 -> 5120 (6 parts) runs with its default splits (one LDS-fed
 # launch for M = 1, 6 K splits and their sum beyond); 6144 -> 5120 (6 parts,
