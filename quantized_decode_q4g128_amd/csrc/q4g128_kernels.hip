@@ -740,11 +740,11 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_bal(
 // between the kernels never changes a bit.
 
 constexpr int kLdsSlotU4 = 128;            // u32x4 per wave and ring slot: one group pair of a 16-column tile
-constexpr int kLdsBurstBlocks = 5;
+constexpr int kLdsBurstBlocks = 5;         // BURST: blocks of 8 groups per unit, at most (whole K = 5120 too)
 // NR launches: tile waves with a ring slot and a burst area of their own; the
 // waves without a tile share one more (their empty loads write only zeros,
 // which nothing reads).
-constexpr int kNarrowRingWaves = 9;         // BURST: blocks of 8 groups per unit, at most (whole K = 5120 too)
+constexpr int kNarrowRingWaves = 9;
 constexpr int kDeepRing = 8;                // pairs in flight for the youngest tile wave (its slots + 3 idle waves')
 // Cache-policy bits of a buffer access: system coherence (sc0 | sc1): loads
 // miss every cache, stores write through to memory.
@@ -763,18 +763,22 @@ __device__ __forceinline__ uint32_t lds_counter(const uint32_t *f)
     return v;
 }
 
-__device__ __forceinline__ void lds_count_up(uint32_t *f)
+// Sets the LDS counter *f (one writer per counter) to v.
+__device__ __forceinline__ void lds_put(uint32_t *f, uint32_t v)
 {
     const uint32_t a = (uint32_t)(size_t)(__attribute__((address_space(3))) uint32_t *)f;
-    asm volatile("ds_add_u32 %0, %1" : : "v"(a), "v"(1u) : "memory");
+    asm volatile("ds_write_b32 %0, %1" : : "v"(a), "v"(v) : "memory");
 }
 
-// Wait until the LDS counter *f reaches v.  Bounded (about a millisecond):
-// every wave leaves the kernel even if a count never arrives.
-__device__ __forceinline__ void lds_wait_geq(uint32_t *f, uint32_t v)
+// Wait until every one of the n (1..64) LDS counters f[0..n) has reached v;
+// lane j reads f[j].  Each counter has one writer and only grows, so once
+// all have been seen at v or above they stay there.  Bounded (about a
+// millisecond): every wave leaves the kernel even if a count never arrives.
+__device__ __forceinline__ void lds_wait_all_geq(const uint32_t *f, int n, uint32_t v)
 {
+    const uint32_t *g = f + min((int)(threadIdx.x & 63), n - 1);
     for (int it = 0; it < (1 << 14); ++it) {
-        if (lds_counter(f) >= v) break;
+        if (__builtin_amdgcn_ballot_w64(lds_counter(g) < v) == 0) break;
         __builtin_amdgcn_s_sleep(2);
     }
 }
@@ -842,7 +846,7 @@ __device__ __forceinline__ void group_fma(const u32x4 (&a)[4], const f32x4 &xsum
 // XCH (rows that do not fit the LDS whole, every tile one wave's, at least
 // one wave without a tile): x is staged in chunks of xcg groups into two
 // buffers.  The waves without a tile load chunk c + 1 while the others run
-// chunk c; one workgroup barrier per chunk boundary hands the buffers over.
+// chunk c; per-wave progress counters in LDS hand the buffers over.
 // Every tile's sums run in the same order as with x staged whole.  NR (whole
 // K, at most kNarrowRingWaves tiles): ring slots and burst areas for the tile
 // waves plus one the others share, 13 KB less static LDS, which leaves x room
@@ -862,7 +866,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     constexpr bool DEEP = RD == 2 && BURST && !PARTS && !XCH && RL == 1 && !NR;
     constexpr int RW = NR ? kNarrowRingWaves + 1 : kBalWaves;    // ring slots and burst areas
     __shared__ uint32_t last_wg;
-    __shared__ uint32_t xflag[XCH ? 2 : 1];               // XCH: chunks staged, chunk completions
+    __shared__ uint32_t xprog[XCH ? kBalWaves : 1];       // XCH, per wave: chunks run (tile) or last staged (loader)
     __shared__ __attribute__((aligned(16))) u32x4 ring0[RW * kLdsSlotU4];
     __shared__ __attribute__((aligned(16))) u32x4 ring1[RW * kLdsSlotU4];
     __shared__ __attribute__((aligned(16))) u32x4 ring2[RD > 2 ? kBalWaves * kLdsSlotU4 : 1];
@@ -1012,7 +1016,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
     if (burst) prime();                           // after x: x's loads stay older than the ring's
     if constexpr (XN) xst.norm(xs, M, K, na.eps);
     xst.store(xs, M, 0, xg);
-    if (XCH && tid == 0) xflag[0] = xflag[1] = 0u;
+    if (XCH && tid < kBalWaves) xprog[tid] = 0u;
     // Deep ring (whole-K burst form, one accumulated row): where at least
     // three waves have no tile, the youngest tile wave (the last to end its
     // loop) also takes the ring slots of the three after it and keeps
@@ -1031,15 +1035,17 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
         for (int k = 2; k < kDeepRing; ++k) fill_at(dslot(k), k, true);
     }
     if (XCH && !active) {
-        // Loader: chunk c (>= 1) into buffer c % 2 once every tile wave is
-        // done with chunk c - 2 (xflag[1] counts (wave, chunk) completions),
-        // then counted in xflag[0] (one count per loader wave and chunk).
-        // The tile waves do not wait for one another, only for the chunk
-        // they need next: a workgroup barrier at each chunk end would hold
-        // every wave to the slowest one while its ring runs dry.
+        // Loader: its share of chunk c (>= 1) into buffer c % 2 once every
+        // tile wave's counter says it has run chunk c - 2, then c into its
+        // own counter.  The tile waves do not wait for one another, only for
+        // every loader's counter to reach the chunk they need next: a
+        // workgroup barrier at each chunk end would hold every wave to the
+        // slowest one while its ring runs dry.  (One counter per wave: a sum
+        // of counts cannot tell a wave that is ahead from one that is
+        // behind.)
         const int nchk = (G + xg - 1) / xg;
         for (int c = 1; c < nchk; ++c) {
-            if (c >= 2) lds_wait_geq(&xflag[1], (uint32_t)(nunit * (c - 1)));
+            if (c >= 2) lds_wait_all_geq(xprog, nunit, (uint32_t)(c - 1));
             // Rounds of 8 pieces per thread where a chunk is more than 12
             // per loader thread (M = 16 at 5120 -> 34816: 24.2 against
             // 25.2 us), else of 4 (M = 9, 13: 0.3-0.6 us faster than 8).
@@ -1049,7 +1055,7 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
             else
                 stage_rounds<4, kRowPerm>(xs + (c & 1) * xstride, x, M, K, cs, ce, lt, nlt);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");      // this wave's writes have landed
-            if (lane == 0) lds_count_up(&xflag[0]);
+            if (lane == 0) lds_put(&xprog[wave], (uint32_t)c);
         }
         return;
     }
@@ -1127,11 +1133,11 @@ __global__ __launch_bounds__(kBalThreads) void gemv_q4g128_lds(
                         const int p = p0 + r;
                         if (XCH && ucs + 2 * p == cce) {
                             // Chunk end: this wave is done with the buffer; wait
-                            // until the loaders have filled the next chunk.
+                            // until every loader has staged its share of the next.
                             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                            if (lane == 0) lds_count_up(&xflag[1]);
                             ++chk;
-                            lds_wait_geq(&xflag[0], (uint32_t)((kBalWaves - nunit) * chk));
+                            if (lane == 0) lds_put(&xprog[wave], (uint32_t)chk);
+                            lds_wait_all_geq(xprog + nunit, kBalWaves - nunit, (uint32_t)chk);
                             ccs = cce;
                             cce = min(ccs + xg, G);
                             const int bo = (chk & 1) * xstride;
