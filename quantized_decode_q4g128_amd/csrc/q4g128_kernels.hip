@@ -1795,15 +1795,18 @@ bool xn_fits(int M, int K, int N, int gx, int P, bool act, bool lds)
     return P == 1;
 }
 
-// NR: burst form, ring 2, whole K, M = 5-12 (2 or 3 accumulated rows).
+// NR: burst form, ring 2, whole K, M = 5-16 (2 to 4 accumulated rows; the
+// plan admits it where x leaves the 12-wave burst form too little LDS: M = 8,
+// 9 at K = 5120, 10, 11 at 4096, 14, 15 at 3072).
 template <bool ACT>
 static hipError_t launch_lds_nr(const GemvArgs &a, int gx, hipStream_t stream)
 {
     const LdsPlan lp = lds_plan(a.M, a.K, a.N, gx, 1, ACT, 2, true, true);
-    if (!lp.fits || a.M < 5 || a.M > 12) return hipErrorInvalidValue;
+    if (!lp.fits || a.M < 5 || a.M > 16) return hipErrorInvalidValue;
     const NormArgs na{};
     if (a.M <= 8) return launch_lds_v<2, false, ACT, 2, true, 0, false, false, true>(a, gx, 1, lp, na, stream);
-    return launch_lds_v<2, false, ACT, 3, true, 0, false, false, true>(a, gx, 1, lp, na, stream);
+    if (a.M <= 12) return launch_lds_v<2, false, ACT, 3, true, 0, false, false, true>(a, gx, 1, lp, na, stream);
+    return launch_lds_v<2, false, ACT, 4, true, 0, false, false, true>(a, gx, 1, lp, na, stream);
 }
 
 hipError_t launch_gemv_lds(const GemvArgs &a, int gx, int P, int rd, bool burst, bool nr, hipStream_t stream)

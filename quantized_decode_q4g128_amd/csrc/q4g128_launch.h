@@ -158,7 +158,7 @@ hipError_t launch_gemv_bal(const GemvArgs &a, int gx, int P, hipStream_t stream)
 // 4) group pairs per wave; `burst` requests the first unit's weights before x.
 // Needs S == 1, K % 1024 == 0, 16-byte aligned scale/min, and lds_plan().fits;
 // built variants: rd 2 (plain or fused SwiGLU), burst with rd 2 or 4 (plain).
-// nr (burst, rd 2, K not cut, at most 9 tiles, M = 5-12): ring slots and
+// nr (burst, rd 2, K not cut, at most 9 tiles, M = 5-16): ring slots and
 // burst areas for the tile waves only, plus one spare the others share.
 struct LdsPlan {
     size_t lds;     // dynamic LDS bytes

@@ -108,16 +108,17 @@ def test_swiglu_paths_agree(name, M, K, N, seed):
     assert np.array_equal(fused, again)
 
 
-@pytest.mark.parametrize("K,N,seed", [(5120, 34816, 93), (4096, 33000, 94)])
+@pytest.mark.parametrize("K,N,seed", [(5120, 34816, 93), (4096, 33000, 94), (3072, 33000, 95)])
 def test_swiglu_rows_identical_up_to_16_rows(K, N, seed):
     """Verify drafts of up to 15 tokens: gate/up + SwiGLU with x staged in
     chunks against x staged whole (5120: M <= 9, M = 8, 9 with ring slots
-    for the tile waves only and one spare; 4096: that form at M = 10, 11)."""
+    for the tile waves only and one spare; 4096: that form at M = 10, 11;
+    3072: at M = 14, 15)."""
     case = synth.make_random(16, K, N, seed)
     x16 = dev_x(case.x)
     W, s, m = dev_weights(case.weights)
     full = host_bf16(q.q4g128_gemm_swiglu(x16, W, s, m))
-    for M in (1, 4, 8, 9, 10, 11, 12, 13, 15):
+    for M in (1, 4, 8, 9, 10, 11, 12, 13, 14, 15):
         part = host_bf16(q.q4g128_gemm_swiglu(x16[:M].contiguous(), W, s, m))
         assert np.array_equal(part, full[:M]), M
 

@@ -277,25 +277,27 @@ def test_rows_bit_identical_across_kernel_choice(K, N):
 # kernels.  4096 -> 33000 (9 tiles per CU) takes the burst form with every
 # wave's slots for M <= 9, the one with the tile waves' slots and a shared
 # spare for M = 10, 11 (3 accumulated rows), and x in chunks from M = 12.
-# 6144 -> 33001 (9 tiles, the last workgroup's ragged) stages x in chunks
-# from M = 9 (its x no longer fits the staging registers whole).
+# 3072 -> 33000 takes that form at M = 14, 15 (4 accumulated rows).  6144 ->
+# 33001 (9 tiles, the last workgroup's ragged) stages x in chunks from M = 9
+# (its x no longer fits the staging registers whole).
 @pytest.mark.parametrize("K,N,split", [(5120, 34816, False), (8192, 777, False), (17408, 5120, True),
                                        (6144, 5120, False), (5120, 12288, False), (5120, 20480, False),
                                        (1024, 12288, False), (5120, 28672, False), (4096, 33000, False),
-                                       (6144, 33001, False)])
+                                       (6144, 33001, False), (3072, 33000, False)])
 def test_rows_bit_identical_up_to_16_rows(K, N, split):
     case = synth.make_random(16, K, N, 60 + K // 1024 + N % 1000, outlier_frac=0.01)
     W, s, m = dev_weights(case.weights)
     x16 = dev_x(case.x)
     f = q.q4g128_gemm_splitk if split else q.q4g128_gemm
     y16 = host_f32(f(x16, W, s, m))
-    for M in (1, 2, 3, 4, 5, 8, 9, 10, 11, 12, 13, 15):
+    for M in (1, 2, 3, 4, 5, 8, 9, 10, 11, 12, 13, 14, 15):
         yM = host_f32(f(x16[:M].contiguous(), W, s, m))
         assert np.array_equal(bits(yM), bits(y16[:M])), M
 
 
 @pytest.mark.parametrize("M,K,N", [(9, 5120, 34816), (16, 5120, 34816), (9, 17408, 5120), (16, 2048, 1001),
-                                   (13, 1024, 17), (16, 640, 100), (11, 4096, 33000), (12, 6144, 33001)])
+                                   (13, 1024, 17), (16, 640, 100), (11, 4096, 33000), (12, 6144, 33001),
+                                   (14, 3072, 33000)])
 def test_wide_verify_within_tolerance(orc, M, K, N):
     case = synth.make_random(M, K, N, 70 + M, outlier_frac=0.01)
     wt = case.weights
