@@ -59,3 +59,35 @@ def test_every_row_count_runs_and_keeps_rows(K, N):
             part = f(x[:M].contiguous())
             assert same_bits(part, full[:M]), f"{name} K={K} N={N} M={M}"
     torch.cuda.synchronize(DEV)
+
+
+@pytest.mark.parametrize("K,N", SHAPES)
+def test_fused_norm_entries_keep_rows(K, N):
+    """The same for the entries with a norm: the product of RMSNorm(h) made
+    inside the launch (plain and SwiGLU; M <= 8 in one launch, the
+    normalised x through the workspace beyond) and h = r + y with and
+    without x_out = RMSNorm(h) (K-part shapes in one launch where the rows
+    fit, partial sums and one norm launch otherwise): each row depends on its
+    own inputs only, so every output must equal the 16-row call's rows."""
+    _, W, s, m = device_case(K, N, 2000 + K // 128 + N % 997)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3000 + K // 128 + N % 997)
+    hin = torch.randn((16, K), device=DEV, generator=g) * 3.0
+    gk = (1.0 + 0.1 * torch.randn((K,), device=DEV, generator=g)).to(torch.bfloat16)
+    xr = torch.randn((16, K), device=DEV, generator=g).to(torch.bfloat16)
+    res = torch.randn((16, N), device=DEV, generator=g)
+    gn = (1.0 + 0.1 * torch.randn((N,), device=DEV, generator=g)).to(torch.bfloat16)
+    calls = [("prenorm", lambda M: (q.q4g128_gemm_prenorm(hin[:M].contiguous(), gk, W, s, m),)),
+             ("rmsnorm", lambda M: q.q4g128_gemm_rmsnorm(xr[:M].contiguous(), W, s, m, res[:M].contiguous(), gn)),
+             ("residual", lambda M: q.q4g128_gemm_rmsnorm(xr[:M].contiguous(), W, s, m, res[:M].contiguous(), gn,
+                                                         norm=False)[:1])]
+    if N % 2 == 0:
+        calls.append(("swiglu_prenorm", lambda M: (q.q4g128_gemm_swiglu_prenorm(hin[:M].contiguous(), gk, W, s, m),)))
+    for name, f in calls:
+        full = f(16)
+        torch.cuda.synchronize(DEV)
+        for M in range(1, 16):
+            part = f(M)
+            for j, (a, b) in enumerate(zip(part, full)):
+                assert same_bits(a, b[:M]), f"{name} output {j} K={K} N={N} M={M}"
+    torch.cuda.synchronize(DEV)
