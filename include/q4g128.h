@@ -74,7 +74,12 @@ typedef enum {
 } q4g128_status;
 
 /* The product without splitting K: one kernel launch, y written directly.
- * Best for wide N (N/16 well above the compute-unit count).
+ * Best for wide N (N/16 well above the compute-unit count).  Short-N shapes
+ * whose one-launch form cuts K into parts (q4g128_gemm_parts > 1) hold only
+ * a few rows per launch and run wider M as launches over row blocks, each
+ * streaming the weights again (17408 -> 5120: 2 rows per launch); for those
+ * at M > 1, q4g128_gemm_splitk with the default split count gives the same
+ * bits and streams the weights once.
  * Passages: Token Rush README, bandwidth and weight format paragraphs
  * (decode as one pass over the streamed weights; the format), steps table row
  * 3 (an int4 GEMV with projections fused side by side along N). */
