@@ -270,9 +270,9 @@ size_t q4g128_prenorm_workspace_bytes(int M, int K, int N, int swiglu);
  * (the q/k/v projection, the gate/up projection, the output head) instead of
  * in a launch of its own (Token Rush README, steps table: norm, then the
  * projections).  One launch when the shape's one-launch plan takes it (M <=
- * 8; h and gamma 16-byte aligned, scale and min too): every workgroup reads
+ * 6; h and gamma 16-byte aligned, scale and min too): every workgroup reads
  * the whole rows of h and gamma while it stages x.  Otherwise x goes to the
- * workspace first.  h fp32 [M][K] (4-byte aligned), gamma bf16 [K] (2-byte
+ * workspace first (from 7 rows that pair of launches is the faster).  h fp32 [M][K] (4-byte aligned), gamma bf16 [K] (2-byte
  * aligned), eps >= 0, y fp32 [M][N]; workspace: at least
  * q4g128_prenorm_workspace_bytes(M, K, N, 0) bytes, 256-byte aligned, not
  * shared by calls in flight.  Other requirements as q4g128_gemm. */

@@ -698,10 +698,18 @@ size_t q4g128_prenorm_workspace_bytes(int M, int K, int N, int swiglu)
     return xb + (swiglu ? q4g128_swiglu_workspace_bytes(M, K, N) : 0);
 }
 
+// Rows up to which the product of a normalised input runs in one launch: from
+// 7 rows a norm launch and the product on its x are the faster pair (gate/up
+// + SwiGLU at M = 5 / 7 / 8: 23.23 / 24.28 / 25.14 us in one launch, 23.64 /
+// 24.10 / 24.37 in two; plain gate/up M = 8 25.10 against 24.11, q/k/v M = 7
+// 15.11 against 14.94; one box, interleaved): every workgroup of the one
+// launch reads all M rows of fp32 h, twice x's bytes, before its norm.
+constexpr int kXnMaxRows = 6;
+
 // The product of x = RMSNorm(h) * gamma: in one launch when the shape's
-// balanced plan takes the normalising staging (whole rows, M <= 8, operands
-// 16-byte aligned), else x into the workspace and the product on it.  The
-// same bits either way, and those of the product called on that x.
+// balanced plan takes the normalising staging (whole rows, M <= kXnMaxRows,
+// operands 16-byte aligned), else x into the workspace and the product on
+// it.  The same bits either way, and those of the product called on that x.
 q4g128_status run_prenorm(const float *h, const void *gamma, float eps, int M, int K, const uint32_t *W,
                           const void *scale, const void *min, int N, float *y, uint16_t *act, float *workspace,
                           hipStream_t st)
@@ -709,7 +717,7 @@ q4g128_status run_prenorm(const float *h, const void *gamma, float eps, int M, i
     clear_pending_error();
     const bool sw = act != nullptr;
     const BalChoice bc = plan_bal(M, K, N, scale, min, sw);
-    if (bc.gx > 0 && M <= 8 && (bc.P == 1 || M <= bc.rb) && aligned(h, 16) && aligned(gamma, 16)) {
+    if (bc.gx > 0 && M <= kXnMaxRows && (bc.P == 1 || M <= bc.rb) && aligned(h, 16) && aligned(gamma, 16)) {
         const int mode = balanced_mode(N, sw, bc.gx, bc.P);
         bool lds = mode > 0;
         if (!q4g128::xn_fits(M, K, N, bc.gx, bc.P, sw, lds)) lds = !lds;

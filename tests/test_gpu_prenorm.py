@@ -68,8 +68,9 @@ def run_prenorm(ht, gt, W, s, m, swiglu, eps=1e-6):
 # (M, K, N, swiglu, one launch expected: True / False / None = either)
 CASES = [(1, 5120, 12288, False, True),      # q/k/v: register-ring kernel
          (1, 5120, 34816, True, True),       # gate/up + SwiGLU: LDS-fed kernel
-         (7, 5120, 34816, True, True),       # verify rows
-         (8, 5120, 34816, True, None),
+         (6, 5120, 34816, True, True),       # verify rows: one launch up to 6
+         (7, 5120, 34816, True, False),      # from 7 rows: a norm launch, then the product
+         (8, 5120, 34816, True, False),
          (1, 5120, 32768, False, True),      # many tiles, plain
          (1, 6144, 5120, False, True),       # K parts
          (3, 6144, 5120, False, True),
