@@ -145,7 +145,23 @@ class RawCalls:
                 args = (x.data_ptr(), M, K, Wi.data_ptr(), si.data_ptr(), mi.data_ptr(), N, y.data_ptr())
                 calls.append(lambda st, a=args: L.q4g128_gemm(*a, st))
         self.ys.append((calls, y))
+        self.sets_of = getattr(self, "sets_of", [])
+        self.sets_of.append((calls, sets, case.K, case.N))
         return calls, splits
+
+    def rows_on(self, calls, x_bits):
+        """Launch closures for the product of other rows x (bf16 bits [M][K])
+        on the weight copies of an existing launch list (q4g128_gemm, K not
+        split): only x and M differ."""
+        torch, L = self.torch, self.L
+        dev = torch.device("cuda:0")
+        sets, K, N = next((st, k, n) for c, st, k, n in self.sets_of if c is calls)
+        M = x_bits.shape[0]
+        x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).to(dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        self.keep += [x, y]
+        return [lambda st, a=(x.data_ptr(), M, K, Wi.data_ptr(), si.data_ptr(), mi.data_ptr(), N, y.data_ptr()):
+                L.q4g128_gemm(*a, st) for Wi, si, mi in sets]
 
     def y_of(self, calls):
         """The output tensor the launch list writes."""
@@ -265,7 +281,8 @@ def trace_reading(kernel_prefix):
 def measure_verify_ratios(torch, raw, dec_calls, ver_calls, ver_bytes, steps, warmup, passes=3):
     """Verify steps against the decode step on the gate/up shape: M = 7 (the
     verify workload), M = 9 (a draft of 8 tokens plus the next) and M = 16
-    (the MFMA tile's rows), each `steps` launches on rotating weight copies,
+    (the MFMA tile's rows), and the rest of the sweep M = 2..8 (on the decode
+    step's weight copies), each `steps` launches on rotating weight copies,
     timed in `passes` interleaved passes together with M = 1; each ratio is
     of medians taken in the same passes, so box-to-box and drift effects
     cancel."""
@@ -276,6 +293,9 @@ def measure_verify_ratios(torch, raw, dec_calls, ver_calls, ver_bytes, steps, wa
         case = synth.make_random(M, 5120, 34816, 80 + M)
         B = synth.algorithmic_bytes(M, case.K, case.N)
         sets[M] = (raw.prepare(case, max(2, math.ceil(ROTATE_BYTES / B)), splits=1)[0], B)
+    rows = synth.make_random(8, 5120, 1, 90).x
+    for M in (2, 3, 4, 5, 6, 8):
+        sets[M] = (raw.rows_on(dec_calls, rows[:M]), synth.algorithmic_bytes(M, 5120, 34816))
     t = {M: [] for M in sets}
     for _ in range(passes):
         for M, (calls, _) in sets.items():
@@ -1075,11 +1095,12 @@ def main():
     gbps = B_dec * n_dec / (wall_d * 1e-3) / 1e9
     achieved = B_dec / t_dec / 1e9
     dist = per_call_distribution(torch, dec_calls, max(DIST_CALLS, args.steps))
-    verify, wider = None, None
+    verify, wider, sweep = None, None, None
     if ver_calls:
         vr = measure_verify_ratios(torch, raw, dec_calls, ver_calls, B_ver, args.steps, args.warmup)
         verify = vr.pop(7)
-        wider = {f"M{M}": v for M, v in vr.items()}
+        wider = {f"M{M}": vr.pop(M) for M in (9, 16)}
+        sweep = {f"M{M}": vr[M] for M in sorted(vr)}
     traffic = traffic_from_summary()
     ceiling = None if args.no_read_ceiling else measure_read_ceiling(torch, dec_case)
     if ceiling is not None:
@@ -1127,6 +1148,7 @@ def main():
                    "verify_M7": None if ok_ver is None else ("pass" if ok_ver else "FAIL")},
         "verify_M7": verify,
         "verify_wider": wider,
+        "verify_sweep": sweep,
         "down_M1": down,
         "decode_step_stream": stream_step,
         "epilogues": epilogues,
