@@ -312,6 +312,20 @@ def measure_verify_ratios(torch, raw, dec_calls, ver_calls, ver_bytes, steps, wa
     return out
 
 
+def measure_tiny(torch, q, steps, warmup):
+    """The tiny workload (M=1, K=1024, N=1024; 563,200 bytes per call): a
+    launch-bound product.  64 weight copies rotate (36 MB, so they sit in the
+    last-level cache, as a product this small would)."""
+    case = synth.make_case("tiny")
+    B = synth.algorithmic_bytes(case.M, case.K, case.N)
+    rc = RawCalls(torch, q)
+    calls, splits = rc.prepare(case, 64)
+    n = max(steps, len(calls))
+    t = timed_launches(torch, calls, n, warmup) * 1e-3 / n
+    return {"us_per_call": round(t * 1e6, 3), "GBps": round(B / t / 1e9, 1), "splits": splits,
+            "bytes_per_call": B, "note": "launch-bound; weight copies resident in the last-level cache"}
+
+
 def measure_down(torch, q, steps, warmup):
     """Decode down projection (M=1, K=17408, N=5120; split-K with the default
     split count, partial sums reduced in split order)."""
@@ -1106,6 +1120,7 @@ def main():
     if ceiling is not None:
         ceiling["product_vs_probe"] = measure_product_vs_probe(torch, q)
     down = None if args.no_down else measure_down(torch, q, args.steps, args.warmup)
+    tiny = measure_tiny(torch, q, args.steps, args.warmup)
     stream_step = measure_stream(torch, q) if not args.no_stream else None
     epilogues = None if args.no_epilogues else measure_epilogues(torch, q, args.steps, args.warmup)
     chain = measure_chain(torch, q) if not (args.no_stream or args.no_epilogues) else None
@@ -1149,6 +1164,7 @@ def main():
         "verify_M7": verify,
         "verify_wider": wider,
         "verify_sweep": sweep,
+        "tiny_M1": tiny,
         "down_M1": down,
         "decode_step_stream": stream_step,
         "epilogues": epilogues,
