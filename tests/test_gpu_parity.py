@@ -295,7 +295,8 @@ def test_rows_bit_identical_up_to_16_rows(K, N, split):
         assert np.array_equal(bits(yM), bits(y16[:M])), M
 
 
-@pytest.mark.parametrize("M,K,N", [(9, 5120, 34816), (16, 5120, 34816), (9, 17408, 5120), (16, 2048, 1001),
+@pytest.mark.parametrize("M,K,N", [(8, 5120, 34816), (9, 5120, 34816), (16, 5120, 34816), (9, 17408, 5120),
+                                   (16, 2048, 1001),
                                    (13, 1024, 17), (16, 640, 100), (11, 4096, 33000), (12, 6144, 33001),
                                    (14, 3072, 33000)])
 def test_wide_verify_within_tolerance(orc, M, K, N):
