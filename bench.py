@@ -88,6 +88,9 @@ def parse():
                    help="run the counter workload (a known-size copy, then decode launches) and exit")
     p.add_argument("--pmc-summarize", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                    help="turn two rocprofv3 counter runs of --pmc-workload into a traffic summary")
+    p.add_argument("--pmc-shape", nargs=2, type=int, metavar=("K", "N"), default=None,
+                   help="the counter workload's product shape at M=1 (default: the decode gate/up projection, "
+                        "K=5120 N=34816; another shape draws seeded random weights)")
     p.add_argument("--trace-summarize", nargs=2, metavar=("TRACE_DIR", "OUT"),
                    help="per-launch-shape durations from a rocprofv3 --kernel-trace run of bench.py")
     p.add_argument("--trace-command", default="rocprofv3 --kernel-trace --stats -d OUT -o run --output-format csv "
@@ -927,10 +930,19 @@ def env_info(torch):
 
 # ---- HBM traffic from counters ------------------------------------------------
 
-def pmc_workload():
+def pmc_case(shape):
+    """The counter workload's case: the decode gate/up projection, or seeded
+    random weights of another (K, N) at M=1."""
+    if shape is None or tuple(shape) == (5120, 34816):
+        return synth.make_case("gateup")
+    K, N = shape
+    return synth.make_random(1, K, N, 700 + K // 128 + N % 997)
+
+
+def pmc_workload(shape=None):
     """One elementwise copy of COPY_BYTES (the calibration: it reads and
-    writes exactly that many bytes), then PMC_LAUNCHES decode launches over
-    rotating weight copies."""
+    writes exactly that many bytes), then PMC_LAUNCHES launches of the
+    product (M=1, default split count) over rotating weight copies."""
     import torch
     import quantized_decode_q4g128_amd as q
     dev = torch.device("cuda:0")
@@ -939,10 +951,10 @@ def pmc_workload():
     torch.cuda.synchronize()
     torch.mul(src, 1, out=dst)              # an elementwise kernel: reads and writes COPY_BYTES
     torch.cuda.synchronize()
-    case = synth.make_case("gateup")
+    case = pmc_case(shape)
     raw = RawCalls(torch, q)
     calls, _ = raw.prepare(case, max(2, math.ceil(ROTATE_BYTES / synth.algorithmic_bytes(case.M, case.K, case.N))),
-                           splits=1)
+                           splits=None if shape else 1)
     st = torch.cuda.current_stream().cuda_stream
     for i in range(PMC_LAUNCHES):
         calls[i % len(calls)](st)
@@ -962,7 +974,7 @@ def _counter_per_dispatch(d, name_filter):
     return [per[k] for k in sorted(per)]
 
 
-def pmc_summarize(fetch_dir, write_dir, out):
+def pmc_summarize(fetch_dir, write_dir, out, shape=None):
     is_kernel = lambda n: KERNEL in n and "streamk" not in n and "splitk" not in n
     is_copy = lambda n: "MulFunctor" in n
     lines = {}
@@ -975,18 +987,21 @@ def pmc_summarize(fetch_dir, write_dir, out):
         factor = (COPY_BYTES / 1024.0) / copy_kib
         steady = k[len(k) // 4:]            # skip the first launches
         lines[label] = (float(np.mean(steady)), copy_kib, factor, len(steady))
-    case = synth.make_case("gateup")
+    case = pmc_case(shape)
     B = synth.algorithmic_bytes(case.M, case.K, case.N)
+    sh = f" --pmc-shape {case.K} {case.N}" if shape else ""
+    what = ("the decode gate/up projection (M=1 K=5120 N=34816)" if not shape else
+            f"the product M=1 K={case.K} N={case.N} (default split count: one launch)")
     fetch_b = lines["FETCH_SIZE"][0] * 1024 * lines["FETCH_SIZE"][2]
     write_b = lines["WRITE_SIZE"][0] * 1024 * lines["WRITE_SIZE"][2]
     with open(out, "w") as f:
-        f.write(f"# HBM traffic of {KERNEL} on the decode gate/up projection (M=1 K=5120 N=34816)\n")
+        f.write(f"# HBM traffic of {KERNEL} on {what}\n")
         f.write("# commands (from the repository root; rocprofv3 run from /tmp with TMPDIR=/tmp):\n")
         f.write("#   rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run --output-format csv -- "
-                "python3 bench.py --pmc-workload\n")
+                f"python3 bench.py --pmc-workload{sh}\n")
         f.write("#   rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run --output-format csv -- "
-                "python3 bench.py --pmc-workload\n")
-        f.write("#   python3 bench.py --pmc-summarize OUT/fetch OUT/write " + os.path.relpath(out, ROOT) + "\n")
+                f"python3 bench.py --pmc-workload{sh}\n")
+        f.write(f"#   python3 bench.py --pmc-summarize OUT/fetch OUT/write {os.path.relpath(out, ROOT)}{sh}\n")
         f.write("# calibration: one device copy of copy_bytes; factor = copy_bytes / counter reading\n")
         f.write(f"kernel_source_hash: {kernel_source_hash()}\n")
         f.write(f"copy_bytes: {COPY_BYTES}\n")
@@ -1054,7 +1069,7 @@ def traffic_from_summary():
 def main():
     args = parse()
     if args.pmc_summarize:
-        pmc_summarize(*args.pmc_summarize)
+        pmc_summarize(*args.pmc_summarize, shape=args.pmc_shape)
         return
     if args.trace_summarize:
         trace_summarize(*args.trace_summarize, args.trace_command)
@@ -1069,7 +1084,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     if args.pmc_workload:
-        pmc_workload()
+        pmc_workload(args.pmc_shape)
         return
     if args.stream_only:
         print(json.dumps({"decode_step_stream": measure_stream(torch, q)}))
